@@ -1,0 +1,304 @@
+"""Plain, slow, obviously correct CPU oracle for weight-only quantized linear layers.
+
+TEST INFRASTRUCTURE.  This module is the yardstick the HIP library is checked
+against; it shares no code with that library and must never be imported by
+it.  Only the tests, the smoke check and the CPU-baseline leg of the benchmark
+use it.
+
+What it computes, and where each step comes from:
+
+* Round-to-nearest (RTN) group quantization of fp16 weights to b-bit codes
+  with one fp16 scale and one integer zero-point per (group of input
+  channels, output column).  Round-to-nearest as the baseline quantizer:
+  "GPTQ, AWQ and the rules of post-training quantization", section "The
+  problem both methods solve".  Per-group scales and zero-points, group size
+  typically 128, bit widths 2/3/4/8 and the optional desc_act (act-order)
+  group map: "AutoGPTQ vs The Stack v2", first capability paragraph (GPTQ
+  quantization).  The `w_bit` / `q_group_size` parameter pair: "When to Use
+  AWQ vs GPTQ", section "Practical Usage".
+* AWQ equivalence rescaling: scale input channel k of the weights by s_k and
+  divide the matching activation by s_k, with s_k the channel's mean
+  activation magnitude raised to alpha; the layer output is unchanged in exact
+  arithmetic.  "GPTQ, AWQ and the rules of post-training quantization",
+  section "AWQ: find the one percent that matters".
+* Packing of codes into 32-bit words, dequantization (q - z) * s and the
+  product y = x . dequant(Wq)^T.  Weights stay packed and are dequantized on
+  the fly inside the product: "AutoAWQ vs The Stack v2", paragraph on the
+  WQLinear_* GEMM/GEMV modules, and "AutoAWQ vs Unsloth", the matching
+  paragraph.  The product is defined exactly, so the oracle writes that
+  definition out in float64.
+
+The pages fix none of the following; the reading taken for each is stated
+where it is used:
+  scale = (max - min) / (2^b - 1) in fp32, rounded to fp16, and the codes are
+  derived from the stored fp16 scale; zero = clip(rint(-min / s), 0, 2^b - 1);
+  symmetric mode uses scale = 2 * max|w| / (2^b - 1) and zero = 2^(b-1);
+  rounding is IEEE round-half-to-even; a zero scale becomes 2^-14;
+  little-endian LSB-first bitstream packing; act-order packs columns in the
+  stable-sorted order of the group map; AWQ statistics in float64 over the
+  rows of the activation batch, s rounded once to fp16.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F16 = np.float16
+F32 = np.float32
+F64 = np.float64
+
+#: Bit widths the GPTQ capability lists (2/3/4/8-bit integer weights).
+SUPPORTED_BITS = (2, 3, 4, 8)
+
+#: Smallest normal fp16, used in place of a scale that rounds to zero.
+_SCALE_FLOOR = F16(2.0 ** -14)
+
+
+def _check_bits(bits: int) -> int:
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"bits must be one of {SUPPORTED_BITS}, got {bits}")
+    return (1 << bits) - 1
+
+
+def group_of_channel(K: int, group_size: int, g_idx=None) -> np.ndarray:
+    """Group index of every input channel k (int64 [K]).
+
+    Without act-order, channels are grouped contiguously: g(k) = k // group_size.
+    group_size == -1 means one group spanning all K channels (per-channel, i.e.
+    one scale per output column).  With act-order the caller's g_idx map gives
+    the group of each channel directly (GPTQ desc_act, "AutoGPTQ vs The Stack
+    v2", first capability).
+    """
+    if g_idx is not None:
+        g = np.asarray(g_idx, dtype=np.int64)
+        if g.shape != (K,):
+            raise ValueError("g_idx must have shape [K]")
+        return g
+    gs = K if group_size == -1 else group_size
+    if gs <= 0 or K % gs:
+        raise ValueError("group_size must divide K")
+    return np.arange(K, dtype=np.int64) // gs
+
+
+def act_order_perm(g_idx) -> np.ndarray:
+    """Packed column order for act-order: the stable sort of k by g_idx[k].
+
+    Column k' of the packed matrix holds original channel perm[k'], so the
+    members of each group sit next to each other and the group of packed
+    column k' is k' // group_size when all groups have equal size.
+    """
+    return np.argsort(np.asarray(g_idx, dtype=np.int64), kind="stable")
+
+
+def rtn_quantize(w, bits: int, group_size: int, g_idx=None, symmetric: bool = False):
+    """Round-to-nearest group quantization of fp16 weights w[N][K].
+
+    Returns (codes uint8 [N][K] in original channel order,
+             scales fp16 [N][G], zeros uint8 [N][G] or None when symmetric).
+
+    Per (output column n, group j), over the member channels of group j:
+      asymmetric: s32 = (max - min) / qmax          (fp32 subtract, fp32 divide)
+      symmetric:  s32 = (2 * max|w|) / qmax         (fp32)
+      s = fp16(s32), replaced by 2^-14 if it rounds to zero
+      asymmetric: z = clip(rint(-min / s), 0, qmax) (fp32 divide)
+      symmetric:  z = 2^(b-1)
+      q = clip(rint(w / s) + z, 0, qmax)            (fp32 divide, half-even)
+    """
+    qmax = _check_bits(bits)
+    w = np.asarray(w)
+    if w.dtype != F16 or w.ndim != 2:
+        raise ValueError("w must be a 2-D float16 array [N][K]")
+    N, K = w.shape
+    gk = group_of_channel(K, group_size, g_idx)
+    G = int(gk.max()) + 1 if K else 0
+    w32 = w.astype(F32)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, G), dtype=F16)
+    zeros = None if symmetric else np.zeros((N, G), dtype=np.uint8)
+    for j in range(G):
+        members = np.nonzero(gk == j)[0]
+        if members.size == 0:
+            raise ValueError(f"group {j} has no members")
+        wg = w32[:, members]                                   # [N][|group|]
+        if symmetric:
+            amax = np.max(np.abs(wg), axis=1)
+            s32 = (F32(2.0) * amax) / F32(qmax)
+        else:
+            mn = np.min(wg, axis=1)
+            mx = np.max(wg, axis=1)
+            s32 = (mx - mn) / F32(qmax)
+        s_h = s32.astype(F16)
+        s_h[s_h == 0] = _SCALE_FLOOR
+        s_f = s_h.astype(F32)
+        if symmetric:
+            z = np.full(N, F32(1 << (bits - 1)), dtype=F32)
+        else:
+            z = np.clip(np.rint((-mn) / s_f), F32(0), F32(qmax))
+            zeros[:, j] = z.astype(np.uint8)
+        q = np.clip(np.rint(wg / s_f[:, None]) + z[:, None], F32(0), F32(qmax))
+        codes[:, members] = q.astype(np.uint8)
+        scales[:, j] = s_h
+    return codes, scales, zeros
+
+
+def pack(codes, bits: int) -> np.ndarray:
+    """Pack b-bit codes[N][K] into uint32 words[N][K*b/32].
+
+    Convention (the pages give no layout): each row is a little-endian
+    bitstream; code k occupies bits [k*b, k*b + b) counted from the least
+    significant bit of word 0, and a field that crosses a word boundary
+    continues in the low bits of the next word.
+    """
+    qmax = _check_bits(bits)
+    c = np.asarray(codes)
+    if c.ndim != 2:
+        raise ValueError("codes must be 2-D [N][K]")
+    N, K = c.shape
+    if (K * bits) % 32:
+        raise ValueError("K * bits must be a multiple of 32")
+    if c.size and int(c.max()) > qmax:
+        raise ValueError("code out of range")
+    c = c.astype(np.uint64)
+    # bit plane i of code k lands on stream bit k*bits + i
+    stream = np.zeros((N, K * bits), dtype=np.uint64)
+    for i in range(bits):
+        stream[:, i::bits] = (c >> np.uint64(i)) & np.uint64(1)
+    stream = stream.reshape(N, K * bits // 32, 32)
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
+    return (stream * weights).sum(axis=2).astype(np.uint32)
+
+
+def unpack(packed, bits: int, K: int) -> np.ndarray:
+    """Exact inverse of `pack`: uint32 words[N][K*b/32] -> uint8 codes[N][K]."""
+    _check_bits(bits)
+    p = np.asarray(packed, dtype=np.uint32)
+    N, W = p.shape
+    if W * 32 != K * bits:
+        raise ValueError("packed width does not match K * bits / 32")
+    shifts = np.arange(32, dtype=np.uint64)
+    stream = (p.astype(np.uint64)[:, :, None] >> shifts) & np.uint64(1)
+    stream = stream.reshape(N, W * 32)
+    codes = np.zeros((N, K), dtype=np.uint64)
+    for i in range(bits):
+        codes |= stream[:, i::bits] << np.uint64(i)
+    return codes.astype(np.uint8)
+
+
+def _zero_matrix(zeros, bits, shape):
+    if zeros is None:
+        return np.full(shape, 1 << (bits - 1), dtype=np.int64)
+    return np.asarray(zeros).astype(np.int64)
+
+
+def dequant(codes, scales, zeros, bits: int, group_size: int, g_idx=None) -> np.ndarray:
+    """w_hat[n][k] = fp16( fp32(q - z) * fp32(s) ) for the group of channel k.
+
+    (q - z) is an exact small integer and the fp32 product of it with an fp16
+    scale is exact, so there is a single round-to-nearest-even, to fp16.
+    zeros=None means the symmetric zero 2^(b-1).
+    """
+    _check_bits(bits)
+    q = np.asarray(codes).astype(np.int64)
+    N, K = q.shape
+    gk = group_of_channel(K, group_size, g_idx)
+    s = np.asarray(scales, dtype=F16)
+    z = _zero_matrix(zeros, bits, s.shape)
+    diff = (q - z[:, gk]).astype(F32)
+    return (diff * s[:, gk].astype(F32)).astype(F16)
+
+
+def dequant_fp64_path(codes, scales, zeros, bits: int, group_size: int, g_idx=None) -> np.ndarray:
+    """Second formulation of `dequant`: exact product in float64, one direct
+    float64 -> fp16 rounding.  Must agree bit for bit with `dequant`."""
+    q = np.asarray(codes).astype(np.int64)
+    N, K = q.shape
+    gk = group_of_channel(K, group_size, g_idx)
+    s = np.asarray(scales, dtype=F16).astype(F64)
+    z = _zero_matrix(zeros, bits, s.shape)
+    return ((q - z[:, gk]).astype(F64) * s[:, gk]).astype(F16)
+
+
+def awq_channel_scales(x, alpha: float = 0.5):
+    """AWQ per-input-channel scale from activation statistics.
+
+    a_k = mean over rows m of |x[m][k]| (float64), s_k = a_k ** alpha, then
+    s_h = fp16(s) by one direct float64 -> fp16 rounding ("GPTQ, AWQ and the
+    rules of post-training quantization", section "AWQ: find the one percent
+    that matters": average activation magnitude raised to a power alpha).
+    A channel whose scale rounds to zero gets 2^-14 (the pages are silent on
+    dead channels).  Returns (s float64 [K], s_h fp16 [K]).
+    """
+    x64 = np.asarray(x, dtype=F16).astype(F64)
+    a = np.mean(np.abs(x64), axis=0)
+    s = np.sqrt(a) if alpha == 0.5 else np.power(a, F64(alpha))
+    s_h = s.astype(F16)
+    s_h[s_h == 0] = _SCALE_FLOOR
+    return s, s_h
+
+
+def awq_fold_weight(w, s_h) -> np.ndarray:
+    """W'[n][k] = fp16( fp32(W[n][k]) * fp32(s_h[k]) ): input channel k of the
+    weights is multiplied by s_k (the product of two fp16 values is exact in
+    fp32, so this is one rounding)."""
+    w = np.asarray(w, dtype=F16)
+    s = np.asarray(s_h, dtype=F16).astype(F32)
+    return (w.astype(F32) * s[None, :]).astype(F16)
+
+
+def awq_scale_act(x, s_h) -> np.ndarray:
+    """x'[m][k] = fp16( fp32(x[m][k]) / fp32(s_h[k]) ): the matching
+    activation is divided by s_k (IEEE fp32 division, then one rounding to
+    fp16)."""
+    x = np.asarray(x, dtype=F16)
+    s = np.asarray(s_h, dtype=F16).astype(F32)
+    return (x.astype(F32) / s[None, :]).astype(F16)
+
+
+def linear_ref(x, w_hat, chunk: int = 8192) -> np.ndarray:
+    """y[m][n] = sum_k x[m][k] * w_hat[n][k] in float64 (exact definition of
+    the layer output from the dequantized weights).  Chunked over n only to
+    bound memory."""
+    x64 = np.asarray(x, dtype=F16).astype(F64)
+    w = np.asarray(w_hat, dtype=F16)
+    N = w.shape[0]
+    y = np.empty((x64.shape[0], N), dtype=F64)
+    for n0 in range(0, N, chunk):
+        y[:, n0:n0 + chunk] = x64 @ w[n0:n0 + chunk].astype(F64).T
+    return y
+
+
+def quantize_linear_layer(w, bits: int, group_size: int, g_idx=None, symmetric: bool = False):
+    """RTN-quantize w[N][K] and pack it the way the packed format stores it.
+
+    Returns a dict with codes (original order), scales, zeros, perm (None
+    without act-order), packed words (packed column order) and w_hat (the
+    dequantized fp16 weights in original channel order).
+    """
+    N, K = np.asarray(w).shape
+    codes, scales, zeros = rtn_quantize(w, bits, group_size, g_idx, symmetric)
+    perm = None
+    packed_codes = codes
+    if g_idx is not None:
+        perm = act_order_perm(g_idx)
+        packed_codes = codes[:, perm]
+    return dict(
+        codes=codes, scales=scales, zeros=zeros, perm=perm,
+        packed=pack(packed_codes, bits),
+        w_hat=dequant(codes, scales, zeros, bits, group_size, g_idx),
+    )
+
+
+def f64_to_f16_nearest(v: float) -> np.float16:
+    """Nearest fp16 to a float64 value by exhaustive search over all finite
+    fp16 values (ties to the even bit pattern).  Only used to pin numpy's
+    float64 -> fp16 conversion; far too slow for anything else."""
+    allh = np.arange(0, 0x7C00, dtype=np.uint16).view(F16).astype(F64)
+    a = abs(float(v))
+    d = np.abs(allh - a)
+    best = np.nonzero(d == d.min())[0]
+    if best.size > 1:
+        best = best[best % 2 == 0]
+    h = np.uint16(best[0])
+    if v < 0:
+        h = np.uint16(h | 0x8000)
+    return np.array([h], dtype=np.uint16).view(F16)[0]

@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle against things fixed outside the oracle itself:
+hand-worked fixtures, closed forms, invariants, brute force and textbook
+special cases.  CPU only."""
+
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import wq_inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ----------------------------------------------------------------- packing
+
+def test_pack_golden_words():
+    rows = _read_fixture("pack_words.txt")
+    assert len(rows) == 5
+    for row in rows:
+        bits, K, pattern = int(row[0]), int(row[1]), row[2]
+        want = np.array([int(v, 16) for v in row[3:]], dtype=np.uint32)
+        k = np.arange(K)
+        codes = (k % (1 << bits)) if pattern == "mod" else np.full(K, (1 << bits) - 1)
+        codes = codes.astype(np.uint8)[None, :]
+        got = O.pack(codes, bits)
+        assert got.shape == (1, len(want))
+        assert np.array_equal(got[0], want), (bits, [hex(v) for v in got[0]])
+        assert np.array_equal(O.unpack(got, bits, K), codes)
+
+
+def _bits_of_stream(words, start, nbits):
+    # Brute-force read of a bit field from a little-endian word stream using
+    # Python integers.
+    value = 0
+    for i in range(nbits):
+        pos = start + i
+        bit = (int(words[pos // 32]) >> (pos % 32)) & 1
+        value |= bit << i
+    return value
+
+
+@pytest.mark.parametrize("bits", O.SUPPORTED_BITS)
+def test_pack_bruteforce_bit_reads(bits):
+    K = 96 if bits == 3 else 64
+    codes = I.random_codes((11, bits), 3, K, bits)
+    packed = O.pack(codes, bits)
+    assert packed.shape == (3, K * bits // 32)
+    for n in range(3):
+        for k in range(K):
+            assert _bits_of_stream(packed[n], k * bits, bits) == codes[n, k]
+
+
+@pytest.mark.parametrize("bits", O.SUPPORTED_BITS)
+def test_pack_roundtrip(bits):
+    for K in (32, 128, 4096 // bits * bits if bits != 3 else 384):
+        codes = I.random_codes((12, bits, K), 7, K, bits)
+        assert np.array_equal(O.unpack(O.pack(codes, bits), bits, K), codes)
+
+
+def test_pack_rejects_bad_input():
+    with pytest.raises(ValueError):
+        O.pack(np.zeros((1, 8), np.uint8), 3)          # 24 bits: not whole words
+    with pytest.raises(ValueError):
+        O.pack(np.full((1, 32), 16, np.uint8), 4)      # code out of range
+    with pytest.raises(ValueError):
+        O.pack(np.zeros((1, 32), np.uint8), 5)         # unsupported width
+
+
+# ------------------------------------------------------------- quantizer
+
+def _on_grid_group():
+    fx = {r[0]: r[1:] for r in _read_fixture("rtn_on_grid.txt") if r[0] != "tie"}
+    ties = [r[1:] for r in _read_fixture("rtn_on_grid.txt") if r[0] == "tie"]
+    base, step = float(fx["base"][0]), float(fx["step"][0])
+    j = np.arange(int(fx["group"][0]))
+    w = (base + step * (j % 16)).astype(np.float16)[None, :]
+    return fx, ties, w
+
+
+def test_rtn_on_grid_is_exact():
+    fx, _, w = _on_grid_group()
+    bits = int(fx["bits"][0])
+    codes, scales, zeros = O.rtn_quantize(w, bits, 128)
+    assert scales[0, 0] == np.float16(float(fx["scale"][0]))
+    assert zeros[0, 0] == int(fx["zero"][0])
+    assert np.array_equal(codes[0], (np.arange(128) % 16).astype(np.uint8))
+    w_hat = O.dequant(codes, scales, zeros, bits, 128)
+    assert np.array_equal(w_hat.view(np.uint16), w.view(np.uint16))
+
+
+def test_rtn_tie_break_half_even():
+    fx, ties, w = _on_grid_group()
+    bits = int(fx["bits"][0])
+    for value, code, deq in ties:
+        w2 = w.copy()
+        w2[0, 7] = np.float16(float(value))   # j=7 holds 0.375: not an extreme
+        codes, scales, zeros = O.rtn_quantize(w2, bits, 128)
+        assert scales[0, 0] == np.float16(0.125) and zeros[0, 0] == 4
+        assert codes[0, 7] == int(code), value
+        w_hat = O.dequant(codes, scales, zeros, bits, 128)
+        assert w_hat[0, 7] == np.float16(float(deq))
+
+
+def test_rtn_tie_with_odd_zero():
+    fx = {r[0]: r[1:] for r in _read_fixture("rtn_on_grid.txt")}
+    base, step = float(fx["odd_base"][0]), float(fx["step"][0])
+    w = (base + step * (np.arange(128) % 16)).astype(np.float16)[None, :]
+    value, code, deq = fx["odd_tie"]
+    w[0, 7] = np.float16(float(value))
+    codes, scales, zeros = O.rtn_quantize(w, 4, 128)
+    assert zeros[0, 0] == int(fx["odd_zero"][0]) and scales[0, 0] == np.float16(step)
+    assert codes[0, 7] == int(code)
+    assert O.dequant(codes, scales, zeros, 4, 128)[0, 7] == np.float16(float(deq))
+
+
+def test_rtn_codes_use_stored_fp16_scale():
+    rows = _read_fixture("rtn_scale_rounding.txt")
+    fx = {r[0]: r[1] for r in rows if len(r) == 2}
+    cases = [r for r in rows if len(r) == 3]
+    w = np.zeros((1, 32), np.float16)
+    for i, (v, _, _) in enumerate(cases):
+        w[0, i] = np.float16(float(v))
+    codes, scales, zeros = O.rtn_quantize(w, 4, 32)
+    assert scales[0, 0] == np.float16(float(fx["scale"])) and zeros[0, 0] == int(fx["zero"])
+    w_hat = O.dequant(codes, scales, zeros, 4, 32)
+    for i, (v, c, d) in enumerate(cases):
+        assert codes[0, i] == int(c), v
+        assert float(w_hat[0, i]) == float(d), v
+
+
+def test_rtn_groups_are_indexed_per_group():
+    # Two groups of 32 with very different ranges: a wrong group index (or
+    # swapped axis) gives the wrong scale for one of them.
+    K = 64
+    w = np.zeros((2, K), np.float16)
+    w[0, :32] = np.linspace(-1, 1, 32)     # range 2
+    w[0, 32:] = np.linspace(-4, 4, 32)     # range 8
+    w[1, :32] = np.linspace(0, 0.5, 32) - 0.25
+    w[1, 32:] = np.linspace(-2, 2, 32)
+    codes, scales, zeros = O.rtn_quantize(w, 4, 32)
+    want = np.array([[2 / 15, 8 / 15], [0.5 / 15, 4 / 15]])
+    assert np.allclose(scales.astype(np.float64), want, rtol=1e-3)
+    # Per-channel (group_size = -1) is one group over all of K.
+    c2, s2, z2 = O.rtn_quantize(w, 4, -1)
+    assert s2.shape == (2, 1)
+    assert np.isclose(float(s2[0, 0]), 8 / 15, rtol=1e-3)
+
+
+@pytest.mark.parametrize("bits,gs,sym", [(4, 128, False), (2, 32, True), (3, 128, True),
+                                         (8, -1, True), (3, 32, False), (8, 128, False)])
+def test_rtn_code_range_and_error_bound(bits, gs, sym):
+    N, K = 64, 512
+    w = I.weights((21, bits, gs % 1000), N, K, 0.02)
+    codes, scales, zeros = O.rtn_quantize(w, bits, gs, symmetric=sym)
+    qmax = (1 << bits) - 1
+    assert codes.max() <= qmax
+    if sym:
+        assert zeros is None
+    else:
+        assert zeros.max() <= qmax
+    w_hat = O.dequant(codes, scales, zeros, bits, gs)
+    gk = O.group_of_channel(K, gs)
+    s_h = scales.astype(np.float64)[:, gk]
+    # recompute the unrounded fp32 scale to bound the edge clipping
+    w64 = w.astype(np.float64)
+    G = scales.shape[1]
+    s32 = np.zeros((N, G))
+    for j in range(G):
+        wg = w64[:, gk == j]
+        s32[:, j] = (2 * np.abs(wg).max(1) if sym else wg.max(1) - wg.min(1)) / qmax
+    clip = qmax * np.abs(s32 - scales.astype(np.float64))[:, gk]
+    bound = 0.5 * s_h + clip + 2.0 ** -11 * np.abs(w_hat.astype(np.float64)) + 1e-7
+    if sym:
+        bound = bound + 0.5 * s_h  # the positive end of the symmetric grid is one step short
+    err = np.abs(w64 - w_hat.astype(np.float64))
+    assert np.all(err <= bound)
+
+
+def test_rtn_symmetric_closed_form():
+    # amax = 1.5, 4-bit: scale = 3/15 = 0.2 -> fp16(0.2); zero = 8.
+    w = np.array([[-1.5, -0.2, 0.0, 0.2, 1.5] + [0.0] * 27], np.float16)
+    codes, scales, zeros = O.rtn_quantize(w, 4, 32, symmetric=True)
+    s = np.float16(0.2)
+    assert zeros is None and scales[0, 0] == s
+    s32 = np.float32(s)
+    want = np.clip(np.rint(w.astype(np.float32) / s32) + 8, 0, 15)
+    assert np.array_equal(codes[0], want[0].astype(np.uint8))
+    assert codes[0, 0] == 0 and codes[0, 2] == 8 and codes[0, 4] == 15
+
+
+def test_rtn_degenerate_group_scale_floor():
+    w = np.full((1, 32), 0.25, np.float16)      # max == min
+    codes, scales, zeros = O.rtn_quantize(w, 4, 32)
+    assert scales[0, 0] == np.float16(2.0 ** -14)
+    assert zeros[0, 0] == 0                     # -0.25/s < 0 clips to 0
+    assert np.all(codes == 15)                  # 0.25/s is far above the top code
+
+
+# ----------------------------------------------------------------- dequant
+
+@pytest.mark.parametrize("bits,sym", [(2, True), (3, False), (4, False), (8, True)])
+def test_dequant_formulations_agree(bits, sym):
+    w = I.weights((31, bits), 16, 256, 0.05)
+    codes, scales, zeros = O.rtn_quantize(w, bits, 64, symmetric=sym)
+    a = O.dequant(codes, scales, zeros, bits, 64)
+    b = O.dequant_fp64_path(codes, scales, zeros, bits, 64)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_numpy_f64_to_f16_is_correctly_rounded():
+    # The AWQ scale is rounded float64 -> fp16 in one step; pin numpy's
+    # conversion against an exhaustive nearest-value search, including
+    # values just either side of rounding midpoints.
+    g = np.random.default_rng(5)
+    vals = list(g.uniform(0.01, 30.0, 40))
+    for h in g.integers(0x1000, 0x7000, 20):
+        lo = float(np.array([h], np.uint16).view(np.float16)[0])
+        hi = float(np.array([h + 1], np.uint16).view(np.float16)[0])
+        mid = 0.5 * (lo + hi)
+        vals += [mid, np.nextafter(mid, 0), np.nextafter(mid, 100)]
+    for v in vals:
+        got = np.float64(v).astype(np.float16)
+        want = O.f64_to_f16_nearest(v)
+        assert got.view(np.uint16) == want.view(np.uint16), v
+
+
+# --------------------------------------------------------------------- AWQ
+
+def test_awq_scale_closed_form():
+    # Column k alternates +a_k and -b_k: mean |x| = c_k = (a_k + b_k) / 2 (the
+    # mean, not the max, of the magnitudes), so s = c_k ** alpha.
+    a = np.array([0.25, 1.0, 2.0, 1.0] * 8, dtype=np.float64)
+    b = np.array([0.25, 7.0, 6.0, 17.0] * 8, dtype=np.float64)
+    c = (a + b) / 2                                    # 0.25, 4, 4, 9
+    rows = np.arange(6)[:, None] % 2 == 0
+    x = np.where(rows, a[None, :], -b[None, :]).astype(np.float16)
+    s, s_h = O.awq_channel_scales(x, 0.5)
+    assert np.allclose(s, np.sqrt(c), rtol=0, atol=1e-15)
+    assert np.array_equal(s_h, np.sqrt(c).astype(np.float16))
+    s0, _ = O.awq_channel_scales(x, 0.0)
+    assert np.all(s0 == 1.0)
+    s1, _ = O.awq_channel_scales(x, 1.0)
+    assert np.allclose(s1, c)
+
+
+def test_awq_scale_rounds_once_to_fp16():
+    # mean |x| = 0.5 + 2^-12 + 2^-26 lies just above the midpoint between
+    # fp16 0.5 and 0.5 + 2^-11; one direct rounding gives the upper value
+    # (rounding through fp32 first would land on the midpoint and tie down).
+    x = np.array([[1.0], [1.0 + 2.0 ** -10], [2.0 ** -24], [0.0]], dtype=np.float16)
+    s, s_h = O.awq_channel_scales(x, 1.0)
+    assert s[0] == 0.5 + 2.0 ** -12 + 2.0 ** -26
+    assert float(s_h[0]) == 0.5 + 2.0 ** -11
+
+
+def test_awq_invariance_exact_with_power_of_two_scales():
+    # With s_k a power of two, folding and dividing are exact, so the layer
+    # computes the same function bit for bit (the equivalence the rescaling
+    # rests on).
+    K, M, N = 64, 4, 5
+    mags = 4.0 ** (np.arange(K) % 5 - 2)              # mean|x| = 4^j -> s = 2^j
+    signs = np.where((np.arange(M)[:, None] + np.arange(K)[None, :]) % 2, 1.0, -1.0)
+    x = (signs * mags[None, :]).astype(np.float16)
+    w = I.weights((41,), N, K, 0.5)
+    s, s_h = O.awq_channel_scales(x, 0.5)
+    assert np.all(s_h.astype(np.float64) == 2.0 ** (np.arange(K) % 5 - 2))
+    xs, ws = O.awq_scale_act(x, s_h), O.awq_fold_weight(w, s_h)
+    assert np.array_equal(O.linear_ref(xs, ws), O.linear_ref(x, w))
+
+
+def test_awq_invariance_with_rounding():
+    # Generic scales: only the fp16 roundings of x' and W' separate the two
+    # products.  Scaling the wrong axis would break this by O(1).
+    K, M, N = 256, 64, 96
+    x = I.with_outliers(I.activations((42,), M, K), I.outlier_channels((42,), K, 0.05))
+    w = I.weights((42,), N, K, 0.02)
+    _, s_h = O.awq_channel_scales(x, 0.5)
+    y0 = O.linear_ref(x, w)
+    y1 = O.linear_ref(O.awq_scale_act(x, s_h), O.awq_fold_weight(w, s_h))
+    rel = np.linalg.norm(y1 - y0) / np.linalg.norm(y0)
+    assert rel < 2e-3
+    # a fold along the wrong axis is far off
+    bad = (w.astype(np.float32) * s_h.astype(np.float32)[:N, None]).astype(np.float16)
+    relbad = np.linalg.norm(O.linear_ref(O.awq_scale_act(x, s_h), bad) - y0) / np.linalg.norm(y0)
+    assert relbad > 0.1
+
+
+def test_awq_reduces_error_on_outlier_channels():
+    # Activation-aware rescaling protects the weights on high-magnitude input
+    # channels, so the quantized layer's output error drops relative to plain
+    # RTN on the same weights ("AWQ: find the one percent that matters").
+    K, M, N = 1024, 256, 256
+    seed = (43,)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    y_true = O.linear_ref(x, w)
+    plain = O.quantize_linear_layer(w, 4, 128)
+    e_plain = np.linalg.norm(O.linear_ref(x, plain["w_hat"]) - y_true)
+    _, s_h = O.awq_channel_scales(x, 0.5)
+    awq = O.quantize_linear_layer(O.awq_fold_weight(w, s_h), 4, 128)
+    e_awq = np.linalg.norm(O.linear_ref(O.awq_scale_act(x, s_h), awq["w_hat"]) - y_true)
+    assert e_awq < 0.8 * e_plain
+
+
+# ------------------------------------------------------------------ matmul
+
+def test_linear_matches_bruteforce_triple_loop():
+    M, K, N = 3, 64, 5
+    seed = (51,)
+    x = I.activations(seed, M, K)
+    q = O.quantize_linear_layer(I.weights(seed, N, K, 0.02), 4, 32)
+    y = O.linear_ref(x, q["w_hat"])
+    assert y.shape == (M, N)
+    for m, n in itertools.product(range(M), range(N)):
+        acc = 0.0
+        for k in range(K):
+            zq = 8 if q["zeros"] is None else int(q["zeros"][n, k // 32])
+            w_nk = (int(q["codes"][n, k]) - zq) * float(q["scales"][n, k // 32])
+            acc += float(x[m, k]) * float(np.float16(w_nk))
+        assert abs(y[m, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def test_linear_integer_special_case_is_exact():
+    # Scale 1, zero 0 and integer activations: the layer is an integer
+    # matrix product, which numpy's int64 matmul computes exactly.
+    M, K, N, bits = 4, 128, 6, 4
+    g = np.random.default_rng(52)
+    codes = g.integers(0, 16, (N, K), dtype=np.uint8)
+    xi = g.integers(-8, 9, (M, K))
+    scales = np.ones((N, K // 32), np.float16)
+    zeros = np.zeros((N, K // 32), np.uint8)
+    w_hat = O.dequant(codes, scales, zeros, bits, 32)
+    y = O.linear_ref(xi.astype(np.float16), w_hat)
+    assert np.array_equal(y, (xi @ codes.astype(np.int64).T).astype(np.float64))
+
+
+# --------------------------------------------------------------- act-order
+
+def test_act_order_perm_hand_example():
+    g_idx = np.array([1, 0, 0, 1, 2, 2, 0, 1, 2], np.int32)
+    perm = O.act_order_perm(g_idx)
+    assert list(perm) == [1, 2, 6, 0, 3, 7, 4, 5, 8]
+    assert list(g_idx[perm]) == [0, 0, 0, 1, 1, 1, 2, 2, 2]
+
+
+def test_act_order_group_scales_follow_gidx():
+    # Group 0 = the channels g_idx maps to 0 (wherever they are).
+    K = 64
+    g_idx = np.array([k % 2 for k in range(K)], np.int32)   # even -> 0, odd -> 1
+    w = np.zeros((1, K), np.float16)
+    w[0, 0::2] = np.linspace(-1, 1, 32)
+    w[0, 1::2] = np.linspace(-3, 3, 32)
+    _, scales, _ = O.rtn_quantize(w, 4, 32, g_idx=g_idx)
+    assert np.allclose(scales[0].astype(np.float64), [2 / 15, 6 / 15], rtol=1e-3)
+
+
+def test_act_order_permutation_invariance():
+    # Relabelling input channels consistently in x, W and g_idx leaves the
+    # output unchanged, and the packed words only depend on the packed order.
+    M, N, K, gs, bits = 3, 8, 256, 32, 3
+    seed = (61,)
+    x = I.activations(seed, M, K)
+    w = I.weights(seed, N, K, 0.02)
+    g_idx = I.act_order_gidx(seed, K, gs)
+    q = O.quantize_linear_layer(w, bits, gs, g_idx=g_idx, symmetric=True)
+    y = O.linear_ref(x, q["w_hat"])
+    sigma = np.random.default_rng(62).permutation(K)
+    q2 = O.quantize_linear_layer(w[:, sigma], bits, gs, g_idx=g_idx[sigma], symmetric=True)
+    y2 = O.linear_ref(x[:, sigma], q2["w_hat"])
+    assert np.max(np.abs(y - y2)) <= 1e-12 * np.max(np.abs(y))
+    # unpacking the packed words and undoing perm gives the original codes
+    unp = O.unpack(q["packed"], bits, K)
+    back = np.empty_like(unp)
+    back[:, q["perm"]] = unp
+    assert np.array_equal(back, q["codes"])
+    # groups are contiguous in packed order
+    assert np.array_equal(g_idx[q["perm"]], np.arange(K) // gs)
