@@ -190,15 +190,17 @@ def test_rtn_code_range_and_error_bound(bits, gs, sym):
 
 
 def test_rtn_symmetric_closed_form():
-    # amax = 1.5, 4-bit: scale = 3/15 = 0.2 -> fp16(0.2); zero = 8.
-    w = np.array([[-1.5, -0.2, 0.0, 0.2, 1.5] + [0.0] * 27], np.float16)
+    # max|w| = 1.5 (taken by the negative end), 4-bit: scale = 3/15 = 0.2 ->
+    # fp16(0.2) = 0.199951171875; zero = 8.  -1.5/s = -7.5018 -> -8 -> code 0;
+    # 1.0/s = 5.0012 -> 5 -> code 13.
+    w = np.array([[-1.5, -0.2, 0.0, 0.2, 1.0] + [0.0] * 27], np.float16)
     codes, scales, zeros = O.rtn_quantize(w, 4, 32, symmetric=True)
     s = np.float16(0.2)
     assert zeros is None and scales[0, 0] == s
     s32 = np.float32(s)
     want = np.clip(np.rint(w.astype(np.float32) / s32) + 8, 0, 15)
     assert np.array_equal(codes[0], want[0].astype(np.uint8))
-    assert codes[0, 0] == 0 and codes[0, 2] == 8 and codes[0, 4] == 15
+    assert codes[0, 0] == 0 and codes[0, 2] == 8 and codes[0, 4] == 13
 
 
 def test_rtn_degenerate_group_scale_floor():
