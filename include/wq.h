@@ -1,0 +1,184 @@
+/*
+ * wq.h - C ABI of libwq: weight-only quantized linear layers on gfx950.
+ *
+ * The layer computes y = x . dequant(Wq)^T with fp16 activations x [M][K],
+ * b-bit weight codes (b in {2,3,4,8}) packed into 32-bit words, and one fp16
+ * scale s and one integer zero-point z per (group of input channels, output
+ * column); a code q dequantizes to (q - z) * s.  Sources: 2/3/4/8-bit codes,
+ * per-group scales and zero-points with group size typically 128, optional
+ * desc_act ("AutoGPTQ vs The Stack v2", first capability paragraph); weights
+ * stay packed and are dequantized on the fly inside fused GEMM (batch) and
+ * GEMV (single token) kernels chosen by batch size ("AutoAWQ vs The Stack
+ * v2" and "AutoAWQ vs Unsloth", the WQLinear_* paragraphs).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - fp16 values travel as uint16_t bit patterns (IEEE binary16).
+ *  - Every array argument is a DEVICE pointer to caller-owned, contiguous,
+ *    row-major memory (last index fastest).  Inputs and outputs must not
+ *    overlap unless an entry point says so.  The library allocates no device
+ *    memory and keeps no state between calls; it is thread-safe.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    All work is enqueued asynchronously on it, except where stated.
+ *  - Shapes: K = input channels (a multiple of 32), N = output columns,
+ *    M = activation rows.  In wq_scale_act, wq_gemv, wq_gemm and wq_linear
+ *    M = 0 or N = 0 is an empty problem: the call succeeds and does nothing.
+ *    group_size is a multiple of 32 dividing K, or -1 for one group spanning
+ *    all of K (one scale per output column).
+ *    G = K / group_size groups (G = 1 for -1).
+ *  - Packed weights: uint32 [N][K*bits/32].  Row n is a little-endian
+ *    bitstream: packed column k' occupies bits [k'*bits, k'*bits + bits)
+ *    counted from the least significant bit of the row's first word; a field
+ *    that crosses a word boundary continues in the low bits of the next word.
+ *  - Act-order (desc_act): g_idx[k] (int32 [K]) names the group of original
+ *    input channel k.  Groups must all hold exactly group_size channels.
+ *    Packing stores channels in the order perm = stable sort of k by
+ *    g_idx[k]: packed column k' holds original channel perm[k'] and belongs
+ *    to group k' / group_size.  Kernels take perm (int32 [K]) and read
+ *    x[m][perm[k']]; perm = NULL means the identity (contiguous groups).
+ *  - scales: fp16 [N][G]; zeros: uint8 [N][G], or NULL for the symmetric
+ *    zero-point 2^(bits-1).
+ *  - Errors: every argument is checked on the host before any device work;
+ *    a failed check returns a status and enqueues nothing.  No entry point
+ *    throws or aborts.  WQ_ERR_HIP reports a failed HIP call (launch or
+ *    copy); the stream's earlier work is unaffected.
+ *  - Alignment: x, y, packed and workspace pointers must be 16-byte aligned.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WQ_OK = 0,
+    WQ_ERR_ARG = 1,          /* null/misaligned pointer, bad shape or group map */
+    WQ_ERR_UNSUPPORTED = 2,  /* bit width or M outside what the kernel handles  */
+    WQ_ERR_HIP = 3           /* a HIP runtime call failed                        */
+} wq_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char* wq_status_str(wq_status s);
+
+/* Library version as "major.minor.patch". */
+const char* wq_version(void);
+
+/* ---------------------------------------------------------------- set-up --
+ * Round-to-nearest group quantization of fp16 weights w [N][K] (the
+ * baseline quantizer of "GPTQ, AWQ and the rules of post-training
+ * quantization", section "The problem both methods solve"; group scales and
+ * zero-points as in "AutoGPTQ vs The Stack v2").  For every output column n
+ * and group j, over the group's member channels:
+ *   asymmetric (symmetric = 0): s32 = (max - min) / (2^bits - 1) in fp32;
+ *   symmetric  (symmetric = 1): s32 = 2 * max|w| / (2^bits - 1) in fp32;
+ *   s = fp16(s32) (round to nearest even), 2^-14 if that is zero;
+ *   z = clip(rint(-min / s), 0, 2^bits - 1) (asymmetric) or 2^(bits-1);
+ *   q = clip(rint(w / s) + z, 0, 2^bits - 1), IEEE fp32 division,
+ *   ties to even.
+ * perm (nullable, int32 [K]): group j is channels perm[j*gs .. j*gs+gs-1];
+ * NULL means channels j*gs .. j*gs+gs-1.
+ * Outputs: codes uint8 [N][K] in original channel order, scales fp16 [N][G],
+ * zeros uint8 [N][G] (must be NULL when symmetric, non-NULL otherwise).
+ */
+wq_status wq_quantize_rtn(const uint16_t* w, const int32_t* perm, int32_t N, int32_t K,
+                          int32_t bits, int32_t group_size, int32_t symmetric,
+                          uint8_t* codes, uint16_t* scales, uint8_t* zeros, void* stream);
+
+/* AWQ per-input-channel scale ("GPTQ, AWQ and the rules of post-training
+ * quantization", section "AWQ: find the one percent that matters"):
+ * a_k = mean over the M rows of |x[m][k]| in float64, s_k = a_k^alpha
+ * (alpha = 0.5 is an exact square root), s_out[k] = fp16(s_k) with one
+ * float64 -> fp16 round-to-nearest-even; 2^-14 if that is zero.
+ * x fp16 [M][K] -> s_out fp16 [K].  alpha must lie in [0, 1]. */
+wq_status wq_awq_scales(const uint16_t* x, int32_t M, int32_t K, double alpha,
+                        uint16_t* s_out, void* stream);
+
+/* AWQ fold: w_out[n][k] = fp16(fp32(w[n][k]) * fp32(s[k])) - input channel
+ * k of the weights multiplied by s_k.  w_out may equal w (in place). */
+wq_status wq_awq_fold(const uint16_t* w, const uint16_t* s, int32_t N, int32_t K,
+                      uint16_t* w_out, void* stream);
+
+/* Act-order packing order: perm = stable sort of k by g_idx[k].  Checks that
+ * every g_idx lies in [0, K/group_size) and every group holds exactly
+ * group_size channels; returns WQ_ERR_ARG otherwise.  This call SYNCHRONIZES
+ * `stream`: it copies g_idx and the computed perm back to the host to check
+ * them. */
+wq_status wq_act_order_perm(const int32_t* g_idx, int32_t K, int32_t group_size,
+                            int32_t* perm, void* stream);
+
+/* Pack codes uint8 [N][K] (original channel order, each < 2^bits; higher bits
+ * are ignored) into packed uint32 [N][K*bits/32].  With g_idx (nullable) the
+ * packing order is first computed into perm (int32 [K], caller-allocated,
+ * required when g_idx is given) as by wq_act_order_perm, and this call then
+ * synchronizes `stream`; without g_idx, perm is ignored and the call is
+ * asynchronous. */
+wq_status wq_pack(const uint8_t* codes, const int32_t* g_idx, int32_t K, int32_t N,
+                  int32_t bits, int32_t group_size, uint32_t* packed, int32_t* perm,
+                  void* stream);
+
+/* Inverse of wq_pack: codes uint8 [N][K] in original channel order. */
+wq_status wq_unpack(const uint32_t* packed, const int32_t* perm, int32_t K, int32_t N,
+                    int32_t bits, uint8_t* codes, void* stream);
+
+/* Materialize the dequantized weights w fp16 [N][K] (original channel
+ * order): w[n][perm[k']] = fp16((q - z) * s), q the code at packed column k',
+ * with one round-to-nearest-even.  Same dequantization arithmetic as the
+ * GEMV/GEMM kernels; used to check it bit for bit. */
+wq_status wq_dequant(const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                     const int32_t* perm, int32_t K, int32_t N, int32_t bits,
+                     int32_t group_size, uint16_t* w, void* stream);
+
+/* ------------------------------------------------------------- hot path --
+ * AWQ input scaling: x_out[m][k] = fp16(fp32(x[m][k]) / fp32(s[k])), IEEE
+ * fp32 division then one round-to-nearest-even (the activation side of the
+ * AWQ rescaling).  x_out may equal x. */
+wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t K,
+                       uint16_t* x_out, void* stream);
+
+/* Bytes of device workspace wq_gemv / wq_gemm / wq_linear need for these
+ * arguments (0 when none is needed; currently only wq_gemm with act-order
+ * uses it, for the gathered activations). */
+size_t wq_workspace_size(int32_t M, int32_t K, int32_t has_perm);
+
+/* y fp16 [M][N] = x fp16 [M][K] . dequant(packed)^T with fp32 accumulation
+ * and one rounding of the sum to fp16.
+ *
+ * wq_gemv: the decode kernel for M <= 16 (returns WQ_ERR_UNSUPPORTED
+ *   above): streams the packed words with 128-bit loads, unpacks and
+ *   dequantizes in registers, accumulates with fp16-pair dot products into
+ *   fp32, and reduces the split-K partial sums across the wavefront.
+ * wq_gemm: the prefill kernel for any M: dequantizes weight tiles to
+ *   fp16 and feeds fp16 matrix-core (MFMA) instructions with fp32
+ *   accumulators.
+ * wq_linear: picks wq_gemv for M <= wq_gemv_max_m() and wq_gemm otherwise
+ *   (the batch-size dispatch).
+ *
+ * workspace: device memory of at least wq_workspace_size(M, K, perm != NULL)
+ * bytes, or NULL when that size is 0.  y must not overlap any input. */
+wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                  const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                  int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+wq_status wq_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                  const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                  int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                    const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                    int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Largest M that wq_linear sends to wq_gemv. */
+int32_t wq_gemv_max_m(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -158,14 +158,13 @@ def pack(codes, bits: int) -> np.ndarray:
         raise ValueError("K * bits must be a multiple of 32")
     if c.size and int(c.max()) > qmax:
         raise ValueError("code out of range")
-    c = c.astype(np.uint64)
     # bit plane i of code k lands on stream bit k*bits + i
-    stream = np.zeros((N, K * bits), dtype=np.uint64)
+    stream = np.zeros((N, K * bits), dtype=np.uint8)
     for i in range(bits):
-        stream[:, i::bits] = (c >> np.uint64(i)) & np.uint64(1)
-    stream = stream.reshape(N, K * bits // 32, 32)
-    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
-    return (stream * weights).sum(axis=2).astype(np.uint32)
+        stream[:, i::bits] = (c >> i) & 1
+    # numpy packs stream bit 8j + t into bit t of byte j (bitorder="little"),
+    # and four consecutive bytes read as a little-endian uint32 form one word
+    return np.packbits(stream, axis=1, bitorder="little").view("<u4").astype(np.uint32)
 
 
 def unpack(packed, bits: int, K: int) -> np.ndarray:
@@ -175,13 +174,11 @@ def unpack(packed, bits: int, K: int) -> np.ndarray:
     N, W = p.shape
     if W * 32 != K * bits:
         raise ValueError("packed width does not match K * bits / 32")
-    shifts = np.arange(32, dtype=np.uint64)
-    stream = (p.astype(np.uint64)[:, :, None] >> shifts) & np.uint64(1)
-    stream = stream.reshape(N, W * 32)
-    codes = np.zeros((N, K), dtype=np.uint64)
+    stream = np.unpackbits(p.astype("<u4").view(np.uint8), axis=1, bitorder="little")
+    codes = np.zeros((N, K), dtype=np.uint8)
     for i in range(bits):
-        codes |= stream[:, i::bits] << np.uint64(i)
-    return codes.astype(np.uint8)
+        codes |= stream[:, i::bits] << i
+    return codes
 
 
 def _zero_matrix(zeros, bits, shape):

@@ -1,0 +1,100 @@
+"""The C-ABI library loads on the CPU, exports every declared symbol and
+rejects bad arguments on the host before any device work.  No kernel is
+launched here: every call below fails argument validation."""
+
+import ctypes
+
+import pytest
+
+import weight_only_int4_wq_amd as wq
+
+WQ_OK, WQ_ERR_ARG, WQ_ERR_UNSUPPORTED, WQ_ERR_HIP = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p(0x10008)   # misaligned
+
+
+def test_library_exports_every_declared_symbol():
+    names = wq.exported_names()
+    expected = {"wq_status_str", "wq_version", "wq_quantize_rtn", "wq_awq_scales", "wq_awq_fold",
+                "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
+                "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m"}
+    assert set(names) == expected
+    handle = wq.lib()
+    for name in names:
+        assert hasattr(handle, name), name
+
+
+def test_status_strings_and_version():
+    assert wq.status_str(WQ_OK) == "ok"
+    for code in (WQ_ERR_ARG, WQ_ERR_UNSUPPORTED, WQ_ERR_HIP):
+        assert len(wq.status_str(code)) > 5
+    assert wq.status_str(99) == "unknown status"
+    assert wq.version().count(".") == 2
+    assert 1 <= wq.gemv_max_m() <= 16
+
+
+def test_workspace_size():
+    assert wq.workspace_size(2048, 4096, False) == 0
+    assert wq.workspace_size(256, 4096, True) == 256 * 4096 * 2
+
+
+def _mm(name, x=FAKE, packed=FAKE, scales=FAKE, zeros=None, perm=None, y=FAKE, M=1, N=64, K=128, bits=4,
+        gs=128, ws=None, wsb=0):
+    fn = getattr(wq.lib(), name)
+    return fn(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name", ["wq_gemv", "wq_gemm", "wq_linear"])
+def test_matmul_argument_checks(name):
+    assert _mm(name, x=None) == WQ_ERR_ARG
+    assert _mm(name, scales=None) == WQ_ERR_ARG
+    assert _mm(name, y=None) == WQ_ERR_ARG
+    assert _mm(name, K=100) == WQ_ERR_ARG            # K not a multiple of 32
+    assert _mm(name, K=0) == WQ_ERR_ARG
+    assert _mm(name, M=-1) == WQ_ERR_ARG
+    assert _mm(name, gs=100) == WQ_ERR_ARG           # not a multiple of 32
+    assert _mm(name, gs=96, K=128) == WQ_ERR_ARG     # does not divide K
+    assert _mm(name, gs=0) == WQ_ERR_ARG
+    assert _mm(name, bits=5) == WQ_ERR_UNSUPPORTED
+    assert _mm(name, bits=16) == WQ_ERR_UNSUPPORTED
+    assert _mm(name, x=FAKE_MIS) == WQ_ERR_ARG
+    assert _mm(name, y=FAKE_MIS) == WQ_ERR_ARG
+    assert _mm(name, packed=FAKE_MIS) == WQ_ERR_ARG
+    # empty problems are valid and enqueue nothing
+    assert _mm(name, M=0) == WQ_OK
+    assert _mm(name, N=0) == WQ_OK
+
+
+def test_gemv_rejects_large_m():
+    assert _mm("wq_gemv", M=17) == WQ_ERR_UNSUPPORTED
+
+
+def test_gemm_act_order_needs_workspace():
+    assert _mm("wq_gemm", M=64, perm=FAKE) == WQ_ERR_ARG
+    assert _mm("wq_gemm", M=64, perm=FAKE, ws=FAKE, wsb=64 * 128 * 2 - 1) == WQ_ERR_ARG
+
+
+def test_setup_entry_points_check_arguments():
+    L = wq.lib()
+    assert L.wq_quantize_rtn(None, None, 4, 128, 4, 128, 0, FAKE, FAKE, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_quantize_rtn(FAKE, None, 4, 128, 4, 128, 0, FAKE, FAKE, None, None) == WQ_ERR_ARG  # zeros needed
+    assert L.wq_quantize_rtn(FAKE, None, 4, 128, 4, 128, 1, FAKE, FAKE, FAKE, None) == WQ_ERR_ARG  # no zeros if sym
+    assert L.wq_quantize_rtn(FAKE, None, 4, 128, 6, 128, 0, FAKE, FAKE, FAKE, None) == WQ_ERR_UNSUPPORTED
+    assert L.wq_awq_scales(FAKE, 4, 128, 1.5, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_awq_scales(FAKE, 4, 128, -0.1, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_awq_fold(None, FAKE, 4, 128, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_act_order_perm(FAKE, 128, 96, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_act_order_perm(FAKE, 100, 32, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_pack(FAKE, None, 100, 4, 4, 128, FAKE, None, None) == WQ_ERR_ARG
+    assert L.wq_pack(FAKE, FAKE, 128, 4, 4, 128, FAKE, None, None) == WQ_ERR_ARG   # perm required
+    assert L.wq_pack(FAKE, None, 128, 4, 7, 128, FAKE, None, None) == WQ_ERR_UNSUPPORTED
+    assert L.wq_unpack(FAKE_MIS, None, 128, 4, 4, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_dequant(FAKE, None, None, None, 128, 4, 4, 128, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_scale_act(FAKE, FAKE, 4, 100, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_scale_act(FAKE, FAKE_MIS, 4, 128, FAKE, None) == WQ_ERR_ARG
+    assert L.wq_scale_act(FAKE, FAKE, 0, 128, FAKE, None) == WQ_OK
+
+
+def test_binding_raises_on_status():
+    with pytest.raises(wq.WQError):
+        wq._check(WQ_ERR_ARG, "wq_gemv")

@@ -1,0 +1,295 @@
+"""Parity of the HIP path against the CPU oracle, through the C ABI.
+
+Integer and byte results (codes, packed words, perm) and the dequantized fp16
+weights must match bit for bit; layer outputs must satisfy relative L2 error
+<= 1e-3 and max abs error <= 5e-2 against the float64 oracle.  Small shapes
+are checked in full (several tiles plus ragged tails); full-size layer shapes
+are checked on sampled output columns, which the oracle quantizes and
+multiplies one row of W at a time."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import wq_inputs as I
+
+torch = pytest.importorskip("torch")
+import weight_only_int4_wq_amd as wq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAX_ABS = 5e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wq.lib()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def check_y(y_gpu, y_ref, tag=""):
+    y = host(y_gpu).astype(np.float64)
+    assert y.shape == y_ref.shape, tag
+    assert np.all(np.isfinite(y)), tag
+    err = y - y_ref
+    denom = np.linalg.norm(y_ref)
+    rel = np.linalg.norm(err) / denom if denom > 0 else np.linalg.norm(err)
+    mx = np.max(np.abs(err)) if err.size else 0.0
+    assert rel <= REL_L2 and mx <= MAX_ABS, f"{tag}: rel_l2={rel:.3e} max_abs={mx:.3e}"
+    return rel, mx
+
+
+def gpu_layer(w, bits, gs, g_idx=None, sym=False):
+    """Quantize and pack fp16 w on the GPU."""
+    wd = dev(w)
+    perm = None
+    if g_idx is not None:
+        perm = wq.act_order_perm(dev(g_idx), gs)
+    codes, scales, zeros = wq.quantize_rtn(wd, bits, gs, perm=perm, symmetric=sym)
+    packed, perm2 = wq.pack(codes, bits, gs, g_idx=None if g_idx is None else dev(g_idx))
+    return dict(codes=codes, scales=scales, zeros=zeros, packed=packed, perm=perm2)
+
+
+def run(kernel, x, L, bits, gs):
+    fn = {"gemv": wq.gemv, "gemm": wq.gemm, "linear": wq.linear}[kernel]
+    return fn(dev(x), L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"])
+
+
+# ------------------------------------------------ quantizer and format ----
+
+FORMAT_CASES = [
+    # bits, gs, sym, act_order, N, K
+    (4, 128, False, False, 96, 512),
+    (4, 128, False, True, 96, 512),
+    (4, -1, False, False, 40, 256),
+    (2, 32, True, False, 64, 256),
+    (2, 32, True, True, 64, 256),
+    (3, 128, True, False, 50, 384),
+    (3, 32, True, True, 50, 384),
+    (3, -1, True, False, 50, 384),
+    (8, 128, True, True, 33, 512),
+    (8, 32, False, False, 33, 512),
+    (4, 64, True, False, 17, 4096),
+]
+
+
+@pytest.mark.parametrize("bits,gs,sym,act,N,K", FORMAT_CASES)
+def test_quantize_pack_unpack_dequant_bit_exact(bits, gs, sym, act, N, K):
+    seed = (101, bits, gs % 997, int(sym), int(act))
+    w = I.weights(seed, N, K, 0.02)
+    g_idx = I.act_order_gidx(seed, K, gs) if act else None
+    ref = O.quantize_linear_layer(w, bits, gs, g_idx=g_idx, symmetric=sym)
+    L = gpu_layer(w, bits, gs, g_idx, sym)
+    assert np.array_equal(host(L["codes"]), ref["codes"])
+    assert np.array_equal(host(L["scales"]).view(np.uint16), ref["scales"].view(np.uint16))
+    if sym:
+        assert L["zeros"] is None
+    else:
+        assert np.array_equal(host(L["zeros"]), ref["zeros"])
+    if act:
+        assert np.array_equal(host(L["perm"]), ref["perm"])
+    assert np.array_equal(host(L["packed"]).view(np.uint32), ref["packed"])
+    # unpack and dequant of the oracle's own packed words
+    pk = dev(ref["packed"].view(np.int32))
+    pm = None if ref["perm"] is None else dev(ref["perm"].astype(np.int32))
+    assert np.array_equal(host(wq.unpack(pk, bits, K, perm=pm)), ref["codes"])
+    zd = None if ref["zeros"] is None else dev(ref["zeros"])
+    w_hat = wq.dequant(pk, dev(ref["scales"]), zd, bits, gs, K, perm=pm)
+    assert np.array_equal(host(w_hat).view(np.uint16), ref["w_hat"].view(np.uint16))
+
+
+def test_pack_of_random_codes_matches_oracle():
+    for bits in O.SUPPORTED_BITS:
+        codes = I.random_codes((102, bits), 37, 640, bits)
+        packed, _ = wq.pack(dev(codes), bits)
+        assert np.array_equal(host(packed).view(np.uint32), O.pack(codes, bits)), bits
+        assert np.array_equal(host(wq.unpack(packed, bits, 640)), codes), bits
+
+
+def test_act_order_perm_rejects_bad_maps():
+    K, gs = 256, 32
+    good = I.act_order_gidx((103,), K, gs)
+    assert np.array_equal(host(wq.act_order_perm(dev(good), gs)), O.act_order_perm(good))
+    bad = good.copy()
+    bad[0] = K // gs                     # out of range
+    with pytest.raises(wq.WQError):
+        wq.act_order_perm(dev(bad), gs)
+    bad = good.copy()
+    bad[np.nonzero(good == 1)[0][0]] = 2  # group 1 short, group 2 long
+    with pytest.raises(wq.WQError):
+        wq.act_order_perm(dev(bad), gs)
+
+
+def test_quantize_full_square_layer_bit_exact():
+    # 4096 x 4096, 4-bit, g=128, asymmetric: the single-GEMV layer in full.
+    seed = (1, 0)
+    w = I.weights(seed, 4096, 4096, 0.02)
+    ref = O.quantize_linear_layer(w, 4, 128)
+    L = gpu_layer(w, 4, 128)
+    assert np.array_equal(host(L["packed"]).view(np.uint32), ref["packed"])
+    assert np.array_equal(host(L["scales"]).view(np.uint16), ref["scales"].view(np.uint16))
+    assert np.array_equal(host(L["zeros"]), ref["zeros"])
+    w_hat = wq.dequant(L["packed"], L["scales"], L["zeros"], 4, 128, 4096)
+    assert np.array_equal(host(w_hat).view(np.uint16), ref["w_hat"].view(np.uint16))
+    x = I.activations(seed, 1, 4096)
+    y_ref = O.linear_ref(x, ref["w_hat"])
+    for kernel in ("gemv", "gemm", "linear"):
+        check_y(run(kernel, x, L, 4, 128), y_ref, kernel)
+
+
+# ----------------------------------------------------------------- AWQ ----
+
+def test_awq_scale_fold_and_act_division_bit_exact():
+    # Prefill activations with 1% outlier channels (x20), 2048 x 4096.
+    seed = (3, 0)
+    M, K, N = 2048, 4096, 512
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    _, s_ref = O.awq_channel_scales(x, 0.5)
+    s = wq.awq_scales(dev(x), 0.5)
+    assert np.array_equal(host(s).view(np.uint16), s_ref.view(np.uint16))
+    for alpha in (0.0, 0.25, 1.0):
+        _, s_a = O.awq_channel_scales(x[:64], alpha)
+        assert np.array_equal(host(wq.awq_scales(dev(x[:64]), alpha)).view(np.uint16), s_a.view(np.uint16))
+    wf = wq.awq_fold(dev(w), s)
+    assert np.array_equal(host(wf).view(np.uint16), O.awq_fold_weight(w, s_ref).view(np.uint16))
+    xs = wq.scale_act(dev(x), s)
+    assert np.array_equal(host(xs).view(np.uint16), O.awq_scale_act(x, s_ref).view(np.uint16))
+
+
+# --------------------------------------------------- layer outputs -------
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 16])
+@pytest.mark.parametrize("N,K", [(100, 4096), (4104, 1024), (64, 4128), (7, 32)])
+def test_gemv_ragged_shapes(M, N, K):
+    seed = (104, M, N, K)
+    w = I.weights(seed, N, K, 0.02)
+    gs = 128 if K % 128 == 0 else 32
+    ref = O.quantize_linear_layer(w, 4, gs)
+    L = gpu_layer(w, 4, gs)
+    x = I.activations(seed, M, K)
+    check_y(run("gemv", x, L, 4, gs), O.linear_ref(x, ref["w_hat"]), f"gemv M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 33, 100, 130, 300])
+@pytest.mark.parametrize("N,K", [(1000, 512), (4104, 256), (72, 4128)])
+def test_gemm_ragged_shapes(M, N, K):
+    seed = (105, M, N, K)
+    w = I.weights(seed, N, K, 0.02)
+    gs = 128 if K % 128 == 0 else 32
+    ref = O.quantize_linear_layer(w, 4, gs)
+    L = gpu_layer(w, 4, gs)
+    x = I.activations(seed, M, K)
+    check_y(run("gemm", x, L, 4, gs), O.linear_ref(x, ref["w_hat"]), f"gemm M={M} N={N} K={K}")
+
+
+VARIANTS = [(b, g, a) for b in (2, 3, 8) for g in (32, 128, -1) for a in (False, True) if not (a and g == -1)]
+
+
+@pytest.mark.parametrize("bits,gs,act", VARIANTS)
+def test_gptq_variants(bits, gs, act):
+    # K = N = 4096, symmetric zero 2^(b-1), M in {1, 256}; act-order from a
+    # seeded random permutation of K.
+    seed = (5, bits, gs % 997, int(act))
+    K = N = 4096
+    w = I.weights(seed, N, K, 0.02)
+    g_idx = I.act_order_gidx(seed, K, gs) if act else None
+    ref = O.quantize_linear_layer(w, bits, gs, g_idx=g_idx, symmetric=True)
+    L = gpu_layer(w, bits, gs, g_idx, sym=True)
+    assert np.array_equal(host(L["packed"]).view(np.uint32), ref["packed"])
+    for M in (1, 256):
+        x = I.activations(seed, M, K)
+        y_ref = O.linear_ref(x, ref["w_hat"])
+        check_y(run("linear", x, L, bits, gs), y_ref, f"linear b={bits} g={gs} act={act} M={M}")
+        if M == 1:
+            check_y(run("gemm", x, L, bits, gs), y_ref, f"gemm b={bits} g={gs} act={act} M=1")
+
+
+def test_dispatch_follows_batch_size():
+    seed = (106,)
+    K, N = 1024, 512
+    w = I.weights(seed, N, K, 0.02)
+    L = gpu_layer(w, 4, 128)
+    mmax = wq.gemv_max_m()
+    for M, kernel in ((1, "gemv"), (mmax, "gemv"), (mmax + 1, "gemm"), (64, "gemm")):
+        x = I.activations(seed, M, K)
+        a = host(run("linear", x, L, 4, 128))
+        b = host(run(kernel, x, L, 4, 128))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (M, kernel)
+
+
+def test_empty_problems():
+    L = gpu_layer(I.weights((107,), 64, 256, 0.02), 4, 128)
+    x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    for fn in (wq.gemv, wq.gemm, wq.linear):
+        y = fn(x, L["packed"], L["scales"], L["zeros"], 4, 128)
+        assert y.shape == (0, 64)
+
+
+# --------------------------------------- full-size layers, sampled -------
+
+def sampled_check(seed, K, N, sigma, Ms, kernels, awq=False, n_rows=48):
+    """Quantize the full layer on the GPU; the oracle quantizes n_rows sampled
+    output columns (plus the first and last) and computes their outputs."""
+    w = I.weights(seed, N, K, sigma)
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(list(seed) + [9]).choice(N, n_rows)]))
+    xs = {M: I.activations(seed, M, K) for M in Ms}
+    s_h = None
+    if awq:
+        (M,) = Ms
+        xs[M] = I.with_outliers(xs[M], I.outlier_channels(seed, K))
+        _, s_h = O.awq_channel_scales(xs[M], 0.5)
+    w_src = dev(w)
+    if awq:
+        s_d = wq.awq_scales(dev(xs[Ms[0]]), 0.5)
+        assert np.array_equal(host(s_d).view(np.uint16), s_h.view(np.uint16))
+        w_src = wq.awq_fold(w_src, s_d)
+    codes, scales, zeros = wq.quantize_rtn(w_src, 4, 128)
+    packed, _ = wq.pack(codes, 4)
+    del codes, w_src
+    w_rows = O.awq_fold_weight(w[rows], s_h) if awq else w[rows]
+    ref = O.quantize_linear_layer(w_rows, 4, 128)
+    r_d = torch.from_numpy(rows).cuda()
+    assert np.array_equal(host(packed[r_d]).view(np.uint32), ref["packed"])
+    assert np.array_equal(host(scales[r_d]).view(np.uint16), ref["scales"].view(np.uint16))
+    assert np.array_equal(host(zeros[r_d]), ref["zeros"])
+    for M in Ms:
+        x = xs[M]
+        x_in = dev(x)
+        if awq:
+            x_in = wq.scale_act(x_in, s_d)
+            x = O.awq_scale_act(x, s_h)
+        y_ref = O.linear_ref(x, ref["w_hat"])
+        for kernel in kernels(M):
+            fn = {"gemv": wq.gemv, "gemm": wq.gemm, "linear": wq.linear}[kernel]
+            y = fn(x_in, packed, scales, zeros, 4, 128)
+            check_y(y[:, r_d], y_ref, f"{kernel} K={K} N={N} M={M}")
+
+
+DECODE_SHAPES = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)]
+
+
+@pytest.mark.parametrize("K,N", DECODE_SHAPES)
+def test_llama7b_decode_shapes_sampled(K, N):
+    sampled_check((2, K, N), K, N, 0.02, (1, 4, 16),
+                  lambda M: ("linear", "gemv", "gemm"))
+
+
+def test_prefill_awq_gemm_sampled():
+    sampled_check((3, 1), 4096, 11008, 0.02, (2048,), lambda M: ("linear", "gemm"), awq=True)
+
+
+@pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192), (8192, 10240)])
+def test_70b_layer_shapes_sampled(K, N):
+    sampled_check((4, K, N), K, N, 0.015, (1, 8, 32, 512),
+                  lambda M: ("linear", "gemv", "gemm") if M <= 16 else ("linear", "gemm"))

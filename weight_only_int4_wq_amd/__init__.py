@@ -1,0 +1,332 @@
+"""Weight-only quantized linear layers on AMD gfx950 (MI355X).
+
+Thin Python binding over libwq.so, the HIP library whose C ABI is declared in
+include/wq.h.  Every function here only checks and marshals arguments (torch
+tensors for device memory, torch's current HIP stream) and calls the entry
+point of the same name; all computation runs in the library's kernels.
+There is no fallback: if libwq.so is missing or cannot be loaded, every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "lib", "lib_path", "header_path", "exported_names", "WQError",
+    "quantize_rtn", "awq_scales", "awq_fold", "act_order_perm", "pack", "unpack",
+    "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_max_m",
+    "status_str", "version", "QuantizedLinear",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG_DIR, "libwq.so")
+header_path = os.path.join(os.path.dirname(_PKG_DIR), "include", "wq.h")
+
+_lib = None
+
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SIG = {
+    "wq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "wq_version": (ctypes.c_char_p, []),
+    "wq_quantize_rtn": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "wq_awq_scales": (ctypes.c_int, [_VP, _I32, _I32, ctypes.c_double, _VP, _VP]),
+    "wq_awq_fold": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _VP]),
+    "wq_act_order_perm": (ctypes.c_int, [_VP, _I32, _I32, _VP, _VP]),
+    "wq_pack": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP]),
+    "wq_unpack": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP]),
+    "wq_dequant": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP]),
+    "wq_scale_act": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _VP]),
+    "wq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "wq_gemv_max_m": (_I32, []),
+}
+for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
+    _SIG[_name] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                                  _VP, ctypes.c_size_t, _VP])
+
+
+class WQError(RuntimeError):
+    """A libwq entry point returned a non-zero status."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(
+                f"{lib_path} is missing: build it with `python -m weight_only_int4_wq_amd.build` "
+                "(there is no non-HIP fallback)")
+        handle = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIG.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_names() -> list:
+    """Function names declared in include/wq.h."""
+    with open(header_path) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)) - {"wq_status"})
+
+
+def status_str(code: int) -> str:
+    return lib().wq_status_str(code).decode()
+
+
+def version() -> str:
+    return lib().wq_version().decode()
+
+
+def gemv_max_m() -> int:
+    return int(lib().wq_gemv_max_m())
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise WQError(f"{what}: {status_str(code)} (status {code})")
+
+
+# ----------------------------------------------------------- marshalling --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name, ndim=None, allow_none=False):
+    torch = _torch()
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _groups(K: int, group_size: int) -> int:
+    return 1 if group_size == -1 else K // group_size
+
+
+# ------------------------------------------------------------ set-up ops --
+
+def quantize_rtn(w, bits: int, group_size: int, perm=None, symmetric: bool = False):
+    """RTN group quantization of fp16 w [N][K] -> (codes u8 [N][K], scales fp16
+    [N][G], zeros u8 [N][G] or None)."""
+    torch = _torch()
+    w = _dev(w, torch.float16, "w", 2)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    N, K = w.shape
+    G = _groups(K, group_size)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    zeros = None if symmetric else torch.empty((N, G), dtype=torch.uint8, device=w.device)
+    _check(lib().wq_quantize_rtn(_ptr(w), _ptr(perm), N, K, bits, group_size, int(symmetric),
+                                 _ptr(codes), _ptr(scales), _ptr(zeros), _stream(w.device)),
+           "wq_quantize_rtn")
+    return codes, scales, zeros
+
+
+def awq_scales(x, alpha: float = 0.5):
+    """AWQ per-input-channel scale fp16 [K] from activations x fp16 [M][K]."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    M, K = x.shape
+    s = torch.empty((K,), dtype=torch.float16, device=x.device)
+    _check(lib().wq_awq_scales(_ptr(x), M, K, float(alpha), _ptr(s), _stream(x.device)), "wq_awq_scales")
+    return s
+
+
+def awq_fold(w, s, out=None):
+    """fp16(W[n][k] * s[k])."""
+    torch = _torch()
+    w = _dev(w, torch.float16, "w", 2)
+    s = _dev(s, torch.float16, "s", 1)
+    N, K = w.shape
+    out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2)
+    _check(lib().wq_awq_fold(_ptr(w), _ptr(s), N, K, _ptr(out), _stream(w.device)), "wq_awq_fold")
+    return out
+
+
+def act_order_perm(g_idx, group_size: int):
+    """Stable packing order of the act-order group map (synchronizes)."""
+    torch = _torch()
+    g_idx = _dev(g_idx, torch.int32, "g_idx", 1)
+    K = g_idx.shape[0]
+    perm = torch.empty((K,), dtype=torch.int32, device=g_idx.device)
+    _check(lib().wq_act_order_perm(_ptr(g_idx), K, group_size, _ptr(perm), _stream(g_idx.device)),
+           "wq_act_order_perm")
+    return perm
+
+
+def pack(codes, bits: int, group_size: int = -1, g_idx=None):
+    """Pack codes u8 [N][K] -> (packed int32 [N][K*bits/32] holding uint32
+    words, perm int32 [K] or None)."""
+    torch = _torch()
+    codes = _dev(codes, torch.uint8, "codes", 2)
+    g_idx = _dev(g_idx, torch.int32, "g_idx", 1, allow_none=True)
+    N, K = codes.shape
+    if (K * bits) % 32:
+        raise ValueError("K * bits must be a multiple of 32")
+    packed = torch.empty((N, K * bits // 32), dtype=torch.int32, device=codes.device)
+    perm = None if g_idx is None else torch.empty((K,), dtype=torch.int32, device=codes.device)
+    _check(lib().wq_pack(_ptr(codes), _ptr(g_idx), K, N, bits, group_size, _ptr(packed), _ptr(perm),
+                         _stream(codes.device)), "wq_pack")
+    return packed, perm
+
+
+def unpack(packed, bits: int, K: int, perm=None):
+    torch = _torch()
+    packed = _dev(packed, torch.int32, "packed", 2)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    N = packed.shape[0]
+    if packed.shape[1] * 32 != K * bits:
+        raise ValueError("packed width does not match K * bits / 32")
+    codes = torch.empty((N, K), dtype=torch.uint8, device=packed.device)
+    _check(lib().wq_unpack(_ptr(packed), _ptr(perm), K, N, bits, _ptr(codes), _stream(packed.device)),
+           "wq_unpack")
+    return codes
+
+
+def dequant(packed, scales, zeros, bits: int, group_size: int, K: int, perm=None):
+    """fp16 dequantized weights [N][K] in original channel order."""
+    torch = _torch()
+    packed = _dev(packed, torch.int32, "packed", 2)
+    scales = _dev(scales, torch.float16, "scales", 2)
+    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    N = packed.shape[0]
+    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
+    w = torch.empty((N, K), dtype=torch.float16, device=packed.device)
+    _check(lib().wq_dequant(_ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), K, N, bits, group_size,
+                            _ptr(w), _stream(packed.device)), "wq_dequant")
+    return w
+
+
+def _check_meta(N, K, bits, group_size, packed, scales, zeros, perm):
+    G = _groups(K, group_size) if group_size == -1 or (group_size > 0 and K % group_size == 0) else None
+    if packed.shape != (N, K * bits // 32):
+        raise ValueError("packed must be [N][K*bits/32]")
+    if G is not None and tuple(scales.shape) != (N, G):
+        raise ValueError("scales must be [N][G]")
+    if zeros is not None and G is not None and tuple(zeros.shape) != (N, G):
+        raise ValueError("zeros must be [N][G]")
+    if perm is not None and tuple(perm.shape) != (K,):
+        raise ValueError("perm must be [K]")
+
+
+# ----------------------------------------------------------- hot path ----
+
+def scale_act(x, s, out=None):
+    """fp16(x / s) per input channel (AWQ activation side)."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    s = _dev(s, torch.float16, "s", 1)
+    M, K = x.shape
+    out = torch.empty_like(x) if out is None else _dev(out, torch.float16, "out", 2)
+    _check(lib().wq_scale_act(_ptr(x), _ptr(s), M, K, _ptr(out), _stream(x.device)), "wq_scale_act")
+    return out
+
+
+def workspace_size(M: int, K: int, has_perm: bool) -> int:
+    return int(lib().wq_workspace_size(M, K, int(bool(has_perm))))
+
+
+def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, out=None, workspace=None):
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    packed = _dev(packed, torch.int32, "packed", 2)
+    scales = _dev(scales, torch.float16, "scales", 2)
+    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    M, K = x.shape
+    N = packed.shape[0]
+    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
+        _dev(out, torch.float16, "out", 2)
+    need = workspace_size(M, K, perm is not None)
+    ws_bytes = 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+        workspace = _dev(workspace, torch.uint8, "workspace", 1)
+        ws_bytes = workspace.numel()
+    else:
+        workspace = None
+    fn = getattr(lib(), entry)
+    _check(fn(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(y), M, N, K, bits,
+              group_size, _ptr(workspace), ws_bytes, _stream(x.device)), entry)
+    return y
+
+
+def gemv(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
+    """Decode kernel, 1 <= M <= 16."""
+    return _matmul("wq_gemv", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
+
+
+def gemm(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
+    """Matrix-core kernel, any M."""
+    return _matmul("wq_gemm", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
+
+
+def linear(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
+    """Batch-size dispatch between gemv and gemm."""
+    return _matmul("wq_linear", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
+
+
+class QuantizedLinear:
+    """A quantized linear layer held in device memory: packed weights, group
+    scales and zero-points, optional act-order perm and AWQ input scale.
+
+    `from_float` quantizes fp16 weights on the GPU (optionally folding an AWQ
+    scale first); calling the object runs y = x . dequant(Wq)^T.
+    """
+
+    def __init__(self, packed, scales, zeros, bits, group_size, K, perm=None, act_scale=None):
+        self.packed, self.scales, self.zeros = packed, scales, zeros
+        self.bits, self.group_size, self.K = bits, group_size, K
+        self.N = packed.shape[0]
+        self.perm, self.act_scale = perm, act_scale
+
+    @classmethod
+    def from_float(cls, w, bits: int = 4, group_size: int = 128, g_idx=None, symmetric: bool = False,
+                   act_scale=None):
+        if act_scale is not None:
+            w = awq_fold(w, act_scale)
+        N, K = w.shape
+        perm = None
+        if g_idx is not None:
+            perm = act_order_perm(g_idx, group_size)
+        codes, scales, zeros = quantize_rtn(w, bits, group_size, perm=perm, symmetric=symmetric)
+        packed, perm2 = pack(codes, bits, group_size, g_idx=g_idx)
+        return cls(packed, scales, zeros, bits, group_size, K, perm2, act_scale)
+
+    def __call__(self, x, out=None, workspace=None, kernel: str = "linear"):
+        if self.act_scale is not None:
+            x = scale_act(x, self.act_scale)
+        fn = {"linear": linear, "gemv": gemv, "gemm": gemm}[kernel]
+        return fn(x, self.packed, self.scales, self.zeros, self.bits, self.group_size, self.perm, out, workspace)

@@ -1,0 +1,51 @@
+// Status strings, shared argument checks and the batch-size dispatch.
+//
+// Dispatch by batch size: a GEMV kernel for single-token decode and a GEMM
+// kernel for batches, picked automatically ("AutoAWQ vs Unsloth", WQLinear_*
+// paragraph; "AutoAWQ vs The Stack v2", WQLinear_* paragraph).
+#include "wq_common.h"
+
+namespace {
+// Largest activation row count sent to the GEMV kernel by wq_linear.
+constexpr int kGemvMaxM = 16;
+}  // namespace
+
+namespace wqh {
+
+wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* y,
+                            int M, int N, int K, int bits, int group_size, int* gs_out) {
+    if (!x || !packed || !scales || !y) return WQ_ERR_ARG;
+    if (M < 0 || N < 0 || K <= 0 || K % 32) return WQ_ERR_ARG;
+    if (!wqh::bits_ok(bits)) return WQ_ERR_UNSUPPORTED;
+    const int gs = resolve_group(K, group_size);
+    if (!gs) return WQ_ERR_ARG;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return WQ_ERR_ARG;
+    *gs_out = gs;
+    return WQ_OK;
+}
+
+}  // namespace wqh
+
+extern "C" const char* wq_status_str(wq_status s) {
+    switch (s) {
+        case WQ_OK: return "ok";
+        case WQ_ERR_ARG: return "invalid argument (null or misaligned pointer, bad shape, group size or group map)";
+        case WQ_ERR_UNSUPPORTED: return "unsupported configuration (bit width or row count)";
+        case WQ_ERR_HIP: return "HIP runtime call failed";
+    }
+    return "unknown status";
+}
+
+extern "C" const char* wq_version(void) { return "0.1.0"; }
+
+extern "C" int32_t wq_gemv_max_m(void) { return kGemvMaxM; }
+
+extern "C" wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                               const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
+                               int32_t K, int32_t bits, int32_t group_size, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (M <= kGemvMaxM)
+        return wq_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, workspace, workspace_bytes,
+                       stream);
+    return wq_gemm(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream);
+}

@@ -1,0 +1,204 @@
+// Quantization-side kernels: round-to-nearest group quantization, the AWQ
+// per-channel scale, the AWQ weight fold and the activation division.
+//
+// Round-to-nearest as the baseline quantizer: "GPTQ, AWQ and the rules of
+// post-training quantization", section "The problem both methods solve".
+// AWQ rescaling (multiply input channel k of W by s_k, divide the matching
+// activation by s_k, s_k = mean activation magnitude to the power alpha):
+// same page, section "AWQ: find the one percent that matters".
+#include <math.h>
+
+#include "wq_common.h"
+
+namespace {
+
+using namespace wq;
+
+__device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// float64 -> fp16 with a single round-to-nearest-even (no detour through
+// fp32, which could round twice).  Finite, non-negative inputs are all the
+// AWQ scale produces; signs, infinities and NaN are handled for completeness.
+__device__ uint16_t f64_to_f16_rne(double d) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, d);
+    const uint16_t sign = uint16_t((b >> 48) & 0x8000u);
+    const int exp = int((b >> 52) & 0x7FF);
+    const uint64_t man = b & ((1ull << 52) - 1);
+    if (exp == 0x7FF) return sign | 0x7C00u | (man ? 0x200u : 0u);
+    if (exp == 0) return sign;  // float64 subnormal: far below the fp16 range
+    const int e = exp - 1023;
+    if (e > 15) return sign | 0x7C00u;
+    const uint64_t sig = man | (1ull << 52);
+    // fp16 normal numbers keep 10 fraction bits; subnormals are multiples of 2^-24
+    const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+    if (shift > 63) return sign;
+    uint64_t q = sig >> shift;
+    const uint64_t rem = sig & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (q & 1))) ++q;
+    uint32_t h;
+    if (e >= -14)
+        h = (uint32_t(e + 14) << 10) + uint32_t(q);  // q carries the implicit bit (1024)
+    else
+        h = uint32_t(q);  // subnormal; q == 1024 is the smallest normal
+    if (h >= 0x7C00u) h = 0x7C00u;
+    return sign | uint16_t(h);
+}
+
+// --------------------------------------------------------------- RTN ----
+// One thread per (output column n, group j).  Two passes over the group's
+// members: min/max (or max |w|), then the codes.
+template <int BITS, bool SYM>
+__global__ void __launch_bounds__(256) rtn_kernel(const uint16_t* __restrict__ w, const int32_t* __restrict__ perm,
+                                                  int N, int K, int gs, uint8_t* __restrict__ codes,
+                                                  uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+    constexpr int qmax = (1 << BITS) - 1;
+    const int G = K / gs;
+    const long long total = (long long)N * G;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (long long)gridDim.x * blockDim.x) {
+        const int n = int(t / G), j = int(t % G);
+        const uint16_t* row = w + (size_t)n * K;
+        float mn = INFINITY, mx = -INFINITY, amax = 0.f;
+        for (int i = 0; i < gs; ++i) {
+            const int k = perm ? perm[j * gs + i] : j * gs + i;
+            const float v = h2f(row[k]);
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+            amax = fmaxf(amax, fabsf(v));
+        }
+        const float s32 = SYM ? __fdiv_rn(2.0f * amax, float(qmax)) : __fdiv_rn(mx - mn, float(qmax));
+        uint16_t sh = f2h(s32);
+        if ((sh & 0x7FFFu) == 0) sh = 0x0400u;  // 2^-14
+        const float s = h2f(sh);
+        float z;
+        if (SYM) {
+            z = float(1 << (BITS - 1));
+        } else {
+            z = fminf(fmaxf(rintf(__fdiv_rn(-mn, s)), 0.f), float(qmax));
+            zeros[(size_t)n * G + j] = uint8_t(z);
+        }
+        scales[(size_t)n * G + j] = sh;
+        uint8_t* crow = codes + (size_t)n * K;
+        for (int i = 0; i < gs; ++i) {
+            const int k = perm ? perm[j * gs + i] : j * gs + i;
+            const float q = fminf(fmaxf(rintf(__fdiv_rn(h2f(row[k]), s)) + z, 0.f), float(qmax));
+            crow[k] = uint8_t(q);
+        }
+    }
+}
+
+// --------------------------------------------------------------- AWQ ----
+// One thread per input channel k: float64 sum of |x| down the column.
+__global__ void __launch_bounds__(256) awq_scales_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                         double alpha, uint16_t* __restrict__ s_out) {
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= K) return;
+    double acc = 0.0;
+    for (int m = 0; m < M; ++m) acc += fabs(double(h2f(x[(size_t)m * K + k])));
+    const double a = acc / double(M);
+    const double s = (alpha == 0.5) ? sqrt(a) : pow(a, alpha);
+    uint16_t h = f64_to_f16_rne(s);
+    if ((h & 0x7FFFu) == 0) h = 0x0400u;
+    s_out[k] = h;
+}
+
+__global__ void __launch_bounds__(256) awq_fold_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ s,
+                                                       long long total, int K, uint16_t* __restrict__ w_out) {
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (long long)gridDim.x * blockDim.x) {
+        const int k = int(t % K);
+        w_out[t] = f2h(h2f(w[t]) * h2f(s[k]));  // exact fp32 product, one rounding
+    }
+}
+
+// x_out = fp16(x / s), 8 elements per thread (K is a multiple of 32, so rows
+// split into whole 8-element groups).
+__global__ void __launch_bounds__(256) scale_act_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s,
+                                                        long long total8, int K, uint16_t* __restrict__ x_out) {
+    const int K8 = K / 8;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total8;
+         t += (long long)gridDim.x * blockDim.x) {
+        const int k0 = int(t % K8) * 8;
+        const u4 v = reinterpret_cast<const u4*>(x)[t];
+        const u4 sv = *reinterpret_cast<const u4*>(s + k0);
+        u4 o;
+        uint32_t in[4] = {v.x, v.y, v.z, v.w}, sc[4] = {sv.x, sv.y, sv.z, sv.w}, out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __fdiv_rn(h2f(uint16_t(in[i])), h2f(uint16_t(sc[i])));
+            const float hi = __fdiv_rn(h2f(uint16_t(in[i] >> 16)), h2f(uint16_t(sc[i] >> 16)));
+            out[i] = uint32_t(f2h(lo)) | (uint32_t(f2h(hi)) << 16);
+        }
+        o.x = out[0]; o.y = out[1]; o.z = out[2]; o.w = out[3];
+        reinterpret_cast<u4*>(x_out)[t] = o;
+    }
+}
+
+int grid_for(long long work, int block, long long cap = 65536) {
+    long long g = (work + block - 1) / block;
+    if (g > cap) g = cap;
+    if (g < 1) g = 1;
+    return int(g);
+}
+
+template <int BITS>
+wq_status launch_rtn(const uint16_t* w, const int32_t* perm, int N, int K, int gs, bool sym, uint8_t* codes,
+                     uint16_t* scales, uint8_t* zeros, hipStream_t s) {
+    const long long work = (long long)N * (K / gs);
+    const dim3 grid(grid_for(work, 256)), block(256);
+    if (sym)
+        hipLaunchKernelGGL((rtn_kernel<BITS, true>), grid, block, 0, s, w, perm, N, K, gs, codes, scales, zeros);
+    else
+        hipLaunchKernelGGL((rtn_kernel<BITS, false>), grid, block, 0, s, w, perm, N, K, gs, codes, scales, zeros);
+    return wqh::launch_status();
+}
+
+}  // namespace
+
+extern "C" wq_status wq_quantize_rtn(const uint16_t* w, const int32_t* perm, int32_t N, int32_t K, int32_t bits,
+                                     int32_t group_size, int32_t symmetric, uint8_t* codes, uint16_t* scales,
+                                     uint8_t* zeros, void* stream) {
+    if (!w || !codes || !scales || N <= 0 || K <= 0 || K % 32) return WQ_ERR_ARG;
+    if (!wqh::bits_ok(bits)) return WQ_ERR_UNSUPPORTED;
+    const int gs = wqh::resolve_group(K, group_size);
+    if (!gs) return WQ_ERR_ARG;
+    if (symmetric ? (zeros != nullptr) : (zeros == nullptr)) return WQ_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (bits) {
+        case 2: return launch_rtn<2>(w, perm, N, K, gs, symmetric, codes, scales, zeros, s);
+        case 3: return launch_rtn<3>(w, perm, N, K, gs, symmetric, codes, scales, zeros, s);
+        case 4: return launch_rtn<4>(w, perm, N, K, gs, symmetric, codes, scales, zeros, s);
+        default: return launch_rtn<8>(w, perm, N, K, gs, symmetric, codes, scales, zeros, s);
+    }
+}
+
+extern "C" wq_status wq_awq_scales(const uint16_t* x, int32_t M, int32_t K, double alpha, uint16_t* s_out,
+                                   void* stream) {
+    if (!x || !s_out || M <= 0 || K <= 0) return WQ_ERR_ARG;
+    if (!(alpha >= 0.0 && alpha <= 1.0)) return WQ_ERR_ARG;
+    hipLaunchKernelGGL(awq_scales_kernel, dim3((K + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+                       int(M), int(K), alpha, s_out);
+    return wqh::launch_status();
+}
+
+extern "C" wq_status wq_awq_fold(const uint16_t* w, const uint16_t* s, int32_t N, int32_t K, uint16_t* w_out,
+                                 void* stream) {
+    if (!w || !s || !w_out || N <= 0 || K <= 0) return WQ_ERR_ARG;
+    const long long total = (long long)N * K;
+    hipLaunchKernelGGL(awq_fold_kernel, dim3(grid_for(total, 256)), dim3(256), 0, static_cast<hipStream_t>(stream), w,
+                       s, total, int(K), w_out);
+    return wqh::launch_status();
+}
+
+extern "C" wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t K, uint16_t* x_out,
+                                  void* stream) {
+    if (!x || !s || !x_out || M < 0 || K <= 0 || K % 32) return WQ_ERR_ARG;
+    if (!wqh::aligned16(x) || !wqh::aligned16(x_out) || !wqh::aligned16(s)) return WQ_ERR_ARG;
+    if (M == 0) return WQ_OK;
+    const long long total8 = (long long)M * K / 8;
+    hipLaunchKernelGGL(scale_act_kernel, dim3(grid_for(total8, 256, 8192)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), x, s, total8, int(K), x_out);
+    return wqh::launch_status();
+}
