@@ -1,0 +1,340 @@
+"""Throughput of the weight-only quantized linear layer on one MI355X.
+
+One step = one decode token (M = 1) through the four 4-bit, group-128
+quantized linears of a Llama-7B-shaped layer: fused qkv (4096 -> 12288),
+o_proj (4096 -> 4096), fused gate+up (4096 -> 22016) and down
+(11008 -> 4096), each dispatched by batch size (M = 1 -> the GEMV kernel).
+`value` is packed-weight bytes streamed per second (GB/s).  The same JSON line
+also carries the prefill figure: M = 2048, K = 4096, N = 11008 with AWQ input
+scaling, in TFLOP/s on the matrix-core GEMM.
+
+Weights are random-init (seeded Gaussian) and quantized on the GPU by the
+library itself; activations are seeded Gaussian.  A rotating pool of more
+than 1 GiB of distinct weight copies keeps every step reading from HBM rather
+than from the 256 MB Infinity Cache.  Steps are captured in HIP graphs (one
+per pool entry) and timed with HIP events on the launch stream.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import wq_inputs as I  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+FP16_MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense fp16 matrix cores (2.5 PFLOP/s)
+POOL_BYTES = 1 << 30             # rotate at least 1 GiB of distinct copies
+
+DECODE_SHAPES = [("qkv", 4096, 12288), ("o_proj", 4096, 4096), ("gate_up", 4096, 22016), ("down", 11008, 4096)]
+PREFILL = dict(M=2048, K=4096, N=11008)
+BITS, GROUP = 4, 128
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def layer_bytes(M, K, N, bits=BITS, group=GROUP):
+    G = K // group
+    packed = N * K * bits // 8
+    meta = N * G * 2 + N * G       # fp16 scales + uint8 zeros
+    act = M * K * 2 + M * N * 2    # x in, y out
+    return packed, packed + meta + act
+
+
+def src_sha(name):
+    with open(os.path.join(ROOT, "weight_only_int4_wq_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src, key):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    summary was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        entry = data[key]
+        if entry.get("kernel_source_sha") != src_sha(kernel_src):
+            return None
+        return entry.get("hbm_bytes_per_launch")
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------ GPU legs ----
+
+def build_decode_pool(wq, torch):
+    """One quantized copy of each decode projection, replicated into a pool."""
+    base = []
+    for i, (name, K, N) in enumerate(DECODE_SHAPES):
+        w = torch.from_numpy(I.weights((2, K, N), N, K, 0.02)).cuda()
+        layer = wq.QuantizedLinear.from_float(w, bits=BITS, group_size=GROUP)
+        del w
+        x = torch.from_numpy(I.activations((2, K, N), 1, K)).cuda()
+        y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+        base.append(dict(name=name, K=K, N=N, layer=layer, x=x, y=y))
+    per_copy = sum(b["layer"].packed.numel() * 4 + b["layer"].scales.numel() * 2 + b["layer"].zeros.numel()
+                   for b in base)
+    copies = max(2, -(-POOL_BYTES // per_copy))
+    pool = [base]
+    for _ in range(copies - 1):
+        entry = []
+        for b in base:
+            L = b["layer"]
+            clone = wq.QuantizedLinear(L.packed.clone(), L.scales.clone(), L.zeros.clone(), BITS, GROUP, b["K"])
+            entry.append(dict(b, layer=clone))
+        pool.append(entry)
+    return pool, per_copy
+
+
+def capture(torch, fn, n_graphs):
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n_graphs):       # eager warm-up of every entry
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for i in range(n_graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def timed(torch, graphs, steps, warmup):
+    """Replay graphs round-robin; HIP events on the replay stream bracket
+    exactly `steps` replays after `warmup` untimed ones."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per replay
+
+
+def decode_leg(wq, torch, steps, warmup):
+    pool, per_copy = build_decode_pool(wq, torch)
+
+    def step(i):
+        for b in pool[i]:
+            wq.linear(b["x"], b["layer"].packed, b["layer"].scales, b["layer"].zeros, BITS, GROUP, out=b["y"])
+
+    graphs = capture(torch, step, len(pool))
+    ms = timed(torch, graphs, steps, warmup)
+    packed_b = sum(layer_bytes(1, K, N)[0] for _, K, N in DECODE_SHAPES)
+    all_b = sum(layer_bytes(1, K, N)[1] for _, K, N in DECODE_SHAPES)
+    # Kernel view: every launch in a step is the same GEMV kernel; the event
+    # time of a step spread over its launches is the average launch duration.
+    n_launch = len(DECODE_SHAPES)
+    per_layer = {}
+    for li, (name, K, N) in enumerate(DECODE_SHAPES):
+        def one(i, li=li):
+            b = pool[i][li]
+            wq.linear(b["x"], b["layer"].packed, b["layer"].scales, b["layer"].zeros, BITS, GROUP, out=b["y"])
+        g1 = capture(torch, one, len(pool))
+        ms1 = timed(torch, g1, steps, warmup)
+        pk, al = layer_bytes(1, K, N)
+        per_layer[name] = dict(K=K, N=N, us=round(ms1 * 1e3, 3), packed_GBs=round(pk / (ms1 * 1e6), 1),
+                               all_GBs=round(al / (ms1 * 1e6), 1))
+        del g1
+    del graphs
+    torch.cuda.synchronize()
+    return dict(ms=ms, packed_b=packed_b, all_b=all_b, n_launch=n_launch, copies=len(pool),
+                pool_bytes=per_copy * len(pool), per_layer=per_layer)
+
+
+def prefill_leg(wq, torch, steps, warmup):
+    M, K, N = PREFILL["M"], PREFILL["K"], PREFILL["N"]
+    seed = (3, 1)
+    x_np = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    x = torch.from_numpy(x_np).cuda()
+    s = wq.awq_scales(x, 0.5)
+    w = torch.from_numpy(I.weights(seed, N, K, 0.02)).cuda()
+    layer = wq.QuantizedLinear.from_float(w, bits=BITS, group_size=GROUP, act_scale=s)
+    del w
+    per_copy = layer.packed.numel() * 4 + layer.scales.numel() * 3 + M * K * 2 * 2 + M * N * 2
+    copies = max(2, -(-POOL_BYTES // per_copy))
+    pool = []
+    for c in range(copies):
+        L = layer if c == 0 else wq.QuantizedLinear(layer.packed.clone(), layer.scales.clone(),
+                                                    layer.zeros.clone(), BITS, GROUP, K, act_scale=s)
+        pool.append(dict(L=L, x=x.clone(), xs=torch.empty_like(x),
+                         y=torch.empty((M, N), dtype=torch.float16, device="cuda")))
+
+    def full(i):
+        p = pool[i]
+        wq.scale_act(p["x"], s, out=p["xs"])
+        wq.linear(p["xs"], p["L"].packed, p["L"].scales, p["L"].zeros, BITS, GROUP, out=p["y"])
+
+    def gemm_only(i):
+        p = pool[i]
+        wq.linear(p["xs"], p["L"].packed, p["L"].scales, p["L"].zeros, BITS, GROUP, out=p["y"])
+
+    def act_only(i):
+        p = pool[i]
+        wq.scale_act(p["x"], s, out=p["xs"])
+
+    ms_full = timed(torch, capture(torch, full, copies), steps, warmup)
+    ms_gemm = timed(torch, capture(torch, gemm_only, copies), steps, warmup)
+    ms_act = timed(torch, capture(torch, act_only, copies), steps, warmup)
+    torch.cuda.synchronize()
+    return dict(ms_full=ms_full, ms_gemm=ms_gemm, ms_act=ms_act, copies=copies)
+
+
+# -------------------------------------------------------- CPU baseline ----
+
+def cpu_baseline(target_s):
+    """The CPU oracle (unpack -> dequant -> float64 product) on a bounded
+    sample of output columns of each decode projection, M = 1."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+
+    def run(rows_per_layer):
+        t_total, packed_total = 0.0, 0
+        for name, K, N in DECODE_SHAPES:
+            r = min(rows_per_layer, N)
+            w = I.weights((2, K, N), r, K, 0.02)  # same distribution as the GPU layer
+            q = O.quantize_linear_layer(w, BITS, GROUP)
+            x = I.activations((2, K, N), 1, K)
+            t0 = time.perf_counter()
+            codes = O.unpack(q["packed"], BITS, K)
+            w_hat = O.dequant(codes, q["scales"], q["zeros"], BITS, GROUP)
+            O.linear_ref(x, w_hat)
+            t_total += time.perf_counter() - t0
+            packed_total += r * K * BITS // 8
+        return t_total, packed_total
+
+    t, b = run(64)
+    rows = int(64 * max(1.0, target_s / max(t, 1e-3)))
+    rows = min(rows, max(N for _, _, N in DECODE_SHAPES))
+    t, b = run(rows)
+    return dict(value=round(b / t / 1e9, 4), unit="GB/s (packed weights, M=1)", cores=threads, kind="oracle",
+                sample=f"{rows} output columns (capped at N) of each of the 4 decode projections, M=1; "
+                       f"unpack + dequant + float64 product; {t:.1f} s",
+                seconds=round(t, 2))
+
+
+# ----------------------------------------------------------------- main ----
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not implemented (the layer shards across GPUs but this path runs on one)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import weight_only_int4_wq_amd as wq
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wq.lib()
+    gemm_steps = args.gemm_steps or max(10, args.steps // 5)
+
+    t0 = time.time()
+    dec = decode_leg(wq, torch, args.steps, args.warmup)
+    print(f"[bench] decode leg done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    t0 = time.time()
+    pre = prefill_leg(wq, torch, gemm_steps, max(5, args.warmup // 5))
+    print(f"[bench] prefill leg done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    ms = dec["ms"]
+    value = dec["packed_b"] / (ms * 1e-3) / 1e9
+    launch_us = ms * 1e3 / dec["n_launch"]
+    achieved = dec["all_b"] / dec["n_launch"] / (launch_us * 1e-6) / 1e9
+    tr = traffic_from_profile("wq_gemv.hip", "gemv_decode_step")
+
+    M, K, N = PREFILL["M"], PREFILL["K"], PREFILL["N"]
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (pre["ms_gemm"] * 1e-3) / 1e12
+    step_tflops = flops / (pre["ms_full"] * 1e-3) / 1e12
+    gtr = traffic_from_profile("wq_gemm.hip", "gemm_prefill")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(args.cpu_seconds)
+        print(f"[bench] cpu baseline done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "W4A16 GEMV HBM GB/s (M=1) & GEMM TFLOP/s (M=2048), % of roofline",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama7b-decode-layer-w4g128-M1: qkv 4096x12288, o_proj 4096x4096, "
+                        "gate_up 4096x22016, down 11008x4096; 4-bit asymmetric RTN, group 128, fp16 x",
+            "M": 1, "bits": BITS, "group_size": GROUP,
+            "value_bytes": "packed 4-bit weight bytes per step (%d)" % dec["packed_b"],
+            "rotating_pool_bytes": dec["pool_bytes"], "pool_copies": dec["copies"],
+            "per_layer": dec["per_layer"],
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
+            "kernel": "gemv_kernel<4,1,4>", "avg_launch_us": round(launch_us, 3),
+            "bytes_per_launch": dec["all_b"] / dec["n_launch"],
+        },
+        "gemm": {
+            "workload": "prefill-awq-w4g128: M=2048 K=4096 N=11008, 1% outlier channels x20, "
+                        "s=mean|x|^0.5 folded into W, x/s at input",
+            "value": round(gemm_tflops, 1), "unit": "TFLOP/s",
+            "step_tflops_incl_act_scaling": round(step_tflops, 1),
+            "ms_gemm": round(pre["ms_gemm"], 5), "ms_scale_act": round(pre["ms_act"], 5),
+            "ms_step": round(pre["ms_full"], 5), "pool_copies": pre["copies"],
+            "roofline": {
+                "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": gtr,
+                "kernel": "gemm_kernel<4,128,128,2>", "avg_launch_us": round(pre["ms_gemm"] * 1e3, 3),
+                "flops_per_launch": flops,
+            },
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,6 +63,7 @@ def test_matmul_argument_checks(name):
     # empty problems are valid and enqueue nothing
     assert _mm(name, M=0) == WQ_OK
     assert _mm(name, N=0) == WQ_OK
+    assert _mm(name, M=0, x=None, y=None) == WQ_OK   # an empty tensor may have no storage
 
 
 def test_gemv_rejects_large_m():

@@ -14,11 +14,13 @@ namespace wqh {
 
 wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* y,
                             int M, int N, int K, int bits, int group_size, int* gs_out) {
-    if (!x || !packed || !scales || !y) return WQ_ERR_ARG;
     if (M < 0 || N < 0 || K <= 0 || K % 32) return WQ_ERR_ARG;
     if (!wqh::bits_ok(bits)) return WQ_ERR_UNSUPPORTED;
     const int gs = resolve_group(K, group_size);
     if (!gs) return WQ_ERR_ARG;
+    *gs_out = gs;
+    if (M == 0 || N == 0) return WQ_OK;  // empty problem: no pointer is read
+    if (!x || !packed || !scales || !y) return WQ_ERR_ARG;
     if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return WQ_ERR_ARG;
     *gs_out = gs;
     return WQ_OK;

@@ -194,9 +194,10 @@ extern "C" wq_status wq_awq_fold(const uint16_t* w, const uint16_t* s, int32_t N
 
 extern "C" wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t K, uint16_t* x_out,
                                   void* stream) {
-    if (!x || !s || !x_out || M < 0 || K <= 0 || K % 32) return WQ_ERR_ARG;
+    if (M < 0 || K <= 0 || K % 32) return WQ_ERR_ARG;
+    if (M == 0) return WQ_OK;  // empty problem: no pointer is read
+    if (!x || !s || !x_out) return WQ_ERR_ARG;
     if (!wqh::aligned16(x) || !wqh::aligned16(x_out) || !wqh::aligned16(s)) return WQ_ERR_ARG;
-    if (M == 0) return WQ_OK;
     const long long total8 = (long long)M * K / 8;
     hipLaunchKernelGGL(scale_act_kernel, dim3(grid_for(total8, 256, 8192)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), x, s, total8, int(K), x_out);
