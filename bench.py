@@ -11,8 +11,9 @@ scaling, in TFLOP/s on the matrix-core GEMM.
 Weights are random-init (seeded Gaussian) and quantized on the GPU by the
 library itself; activations are seeded Gaussian.  A rotating pool of more
 than 1 GiB of distinct weight copies keeps every step reading from HBM rather
-than from the 256 MB Infinity Cache.  Steps are captured in HIP graphs (one
-per pool entry) and timed with HIP events on the launch stream.
+than from the 256 MB Infinity Cache.  The steps over the pool are captured
+in one HIP graph (plus one for a remainder, so exactly --steps steps run)
+and timed with HIP events on the stream the graphs replay on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -51,6 +52,8 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--only", choices=["decode", "prefill"], default=None,
+                   help="run one leg only (for profiler runs); prints that leg's figures")
     return p.parse_args()
 
 
@@ -108,38 +111,43 @@ def build_decode_pool(wq, torch):
     return pool, per_copy
 
 
-def capture(torch, fn, n_graphs):
-    graphs = []
+def capture(torch, fn, n):
+    """One HIP graph that runs fn(0), fn(1), ..., fn(n-1) back to back."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in range(n_graphs):       # eager warm-up of every entry
+        for i in range(n):              # eager warm-up of every pool entry
             fn(i)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    for i in range(n_graphs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
             fn(i)
-        graphs.append(g)
     torch.cuda.synchronize()
-    return graphs
+    return g
 
 
-def timed(torch, graphs, steps, warmup):
-    """Replay graphs round-robin; HIP events on the replay stream bracket
-    exactly `steps` replays after `warmup` untimed ones."""
+def timed(torch, fn, n_pool, steps, warmup):
+    """Time exactly `steps` calls fn(i % n_pool) (after `warmup` untimed ones)
+    with HIP events on the stream the graphs replay on.  The calls run as
+    replays of a graph of n_pool calls plus one graph for the remainder."""
+    full = capture(torch, fn, n_pool)
+    rem = steps % n_pool
+    part = capture(torch, fn, rem) if rem else None
     stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+    for _ in range(max(1, -(-warmup // n_pool))):
+        full.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for i in range(steps):
-        graphs[i % len(graphs)].replay()
+    for _ in range(steps // n_pool):
+        full.replay()
+    if part is not None:
+        part.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per replay
+    return start.elapsed_time(end) / steps  # ms per call
 
 
 def decode_leg(wq, torch, steps, warmup):
@@ -149,8 +157,7 @@ def decode_leg(wq, torch, steps, warmup):
         for b in pool[i]:
             wq.linear(b["x"], b["layer"].packed, b["layer"].scales, b["layer"].zeros, BITS, GROUP, out=b["y"])
 
-    graphs = capture(torch, step, len(pool))
-    ms = timed(torch, graphs, steps, warmup)
+    ms = timed(torch, step, len(pool), steps, warmup)
     packed_b = sum(layer_bytes(1, K, N)[0] for _, K, N in DECODE_SHAPES)
     all_b = sum(layer_bytes(1, K, N)[1] for _, K, N in DECODE_SHAPES)
     # Kernel view: every launch in a step is the same GEMV kernel; the event
@@ -161,13 +168,10 @@ def decode_leg(wq, torch, steps, warmup):
         def one(i, li=li):
             b = pool[i][li]
             wq.linear(b["x"], b["layer"].packed, b["layer"].scales, b["layer"].zeros, BITS, GROUP, out=b["y"])
-        g1 = capture(torch, one, len(pool))
-        ms1 = timed(torch, g1, steps, warmup)
+        ms1 = timed(torch, one, len(pool), steps, warmup)
         pk, al = layer_bytes(1, K, N)
         per_layer[name] = dict(K=K, N=N, us=round(ms1 * 1e3, 3), packed_GBs=round(pk / (ms1 * 1e6), 1),
                                all_GBs=round(al / (ms1 * 1e6), 1))
-        del g1
-    del graphs
     torch.cuda.synchronize()
     return dict(ms=ms, packed_b=packed_b, all_b=all_b, n_launch=n_launch, copies=len(pool),
                 pool_bytes=per_copy * len(pool), per_layer=per_layer)
@@ -204,9 +208,9 @@ def prefill_leg(wq, torch, steps, warmup):
         p = pool[i]
         wq.scale_act(p["x"], s, out=p["xs"])
 
-    ms_full = timed(torch, capture(torch, full, copies), steps, warmup)
-    ms_gemm = timed(torch, capture(torch, gemm_only, copies), steps, warmup)
-    ms_act = timed(torch, capture(torch, act_only, copies), steps, warmup)
+    ms_full = timed(torch, full, copies, steps, warmup)
+    ms_gemm = timed(torch, gemm_only, copies, steps, warmup)
+    ms_act = timed(torch, act_only, copies, steps, warmup)
     torch.cuda.synchronize()
     return dict(ms_full=ms_full, ms_gemm=ms_gemm, ms_act=ms_act, copies=copies)
 
@@ -265,6 +269,14 @@ def main():
     wq.lib()
     gemm_steps = args.gemm_steps or max(10, args.steps // 5)
 
+    if args.only == "decode":
+        dec = decode_leg(wq, torch, args.steps, args.warmup)
+        print(json.dumps({"leg": "decode", "ms_per_step": dec["ms"], "per_layer": dec["per_layer"]}), flush=True)
+        return
+    if args.only == "prefill":
+        pre = prefill_leg(wq, torch, gemm_steps, max(5, args.warmup // 5))
+        print(json.dumps({"leg": "prefill", **pre}), flush=True)
+        return
     t0 = time.time()
     dec = decode_leg(wq, torch, args.steps, args.warmup)
     print(f"[bench] decode leg done in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)

@@ -33,6 +33,15 @@ constexpr uint32_t kMagic2 = 0x64006400u;  // fp16 pair (1024, 1024)
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// (a & mask) | magic in one VALU instruction.  The compiler splits this into
+// two (its VOP3 form cannot take two literal constants), so it is written
+// out: mask travels in an SGPR, magic in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+    return r;
+}
+
 // Number of 32-bit words in one 32-code chunk of a `bits`-wide code stream.
 template <int BITS>
 struct Chunk {
@@ -49,10 +58,10 @@ __device__ __forceinline__ void decode_chunk<4>(const uint32_t* w, uint32_t* h) 
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const uint32_t v = w[b];
-        h[4 * b + 0] = (v & 0x000F000Fu) | kMagic2;
-        h[4 * b + 1] = ((v >> 4) & 0x000F000Fu) | kMagic2;
-        h[4 * b + 2] = ((v >> 8) & 0x000F000Fu) | kMagic2;
-        h[4 * b + 3] = ((v >> 12) & 0x000F000Fu) | kMagic2;
+        h[4 * b + 0] = and_or(v, 0x000F000Fu, kMagic2);
+        h[4 * b + 1] = and_or(v >> 4, 0x000F000Fu, kMagic2);
+        h[4 * b + 2] = and_or(v >> 8, 0x000F000Fu, kMagic2);
+        h[4 * b + 3] = and_or(v >> 12, 0x000F000Fu, kMagic2);
     }
 }
 
@@ -80,10 +89,10 @@ __device__ __forceinline__ void decode_chunk<2>(const uint32_t* w, uint32_t* h) 
         const uint32_t base = (b & 1) ? 2u : 0u;
         const uint32_t sel = 0x0C000C00u | ((base + 1u) << 16) | base;
         const uint32_t t = __builtin_amdgcn_perm(0u, v, sel);
-        h[4 * b + 0] = (t & 0x00030003u) | kMagic2;
-        h[4 * b + 1] = ((t >> 2) & 0x00030003u) | kMagic2;
-        h[4 * b + 2] = ((t >> 4) & 0x00030003u) | kMagic2;
-        h[4 * b + 3] = ((t >> 6) & 0x00030003u) | kMagic2;
+        h[4 * b + 0] = and_or(t, 0x00030003u, kMagic2);
+        h[4 * b + 1] = and_or(t >> 2, 0x00030003u, kMagic2);
+        h[4 * b + 2] = and_or(t >> 4, 0x00030003u, kMagic2);
+        h[4 * b + 3] = and_or(t >> 6, 0x00030003u, kMagic2);
     }
 }
 
@@ -99,11 +108,24 @@ __device__ __forceinline__ void decode_chunk<3>(const uint32_t* w, uint32_t* h) 
     for (int b = 0; b < 4; ++b) {
         // codes 0..3 (12 bits) to the low half, codes 4..7 to the high half
         const uint32_t t = (v[b] & 0x00000FFFu) | ((v[b] << 4) & 0x0FFF0000u);
-        h[4 * b + 0] = (t & 0x00070007u) | kMagic2;
-        h[4 * b + 1] = ((t >> 3) & 0x00070007u) | kMagic2;
-        h[4 * b + 2] = ((t >> 6) & 0x00070007u) | kMagic2;
-        h[4 * b + 3] = ((t >> 9) & 0x00070007u) | kMagic2;
+        h[4 * b + 0] = and_or(t, 0x00070007u, kMagic2);
+        h[4 * b + 1] = and_or(t >> 3, 0x00070007u, kMagic2);
+        h[4 * b + 2] = and_or(t >> 6, 0x00070007u, kMagic2);
+        h[4 * b + 3] = and_or(t >> 9, 0x00070007u, kMagic2);
     }
+}
+
+// Group of a 32-code chunk, cg / (group_size / 32), by multiply-shift with a
+// magic number from group_magic() on the host: exact for cg < 2^24 and free
+// of branches (a branch around it would make the compiler drain every load
+// in flight at the join).
+struct GroupDiv {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+__device__ __forceinline__ int chunk_group(int cg, GroupDiv gd) {
+    return int((uint64_t(uint32_t(cg)) * gd.mul) >> gd.shift);
 }
 
 // Group constants as fp16 pairs: zz = (1024 + z, 1024 + z), ss = (s, s).
@@ -152,6 +174,19 @@ inline int resolve_group(int K, int group_size) {
     if (group_size == -1) return K;
     if (group_size <= 0 || group_size % 32 != 0 || K % group_size != 0) return 0;
     return group_size;
+}
+
+// Host side of chunk_group.  For d = group_size / 32 chunks per group, take
+// s = 24 + ceil(log2 d) and mul = ceil(2^s / d).  Then for n < 2^24,
+// n * mul / 2^s = n / d + err with 0 <= err < n / 2^s < 1 / d, which never
+// reaches the next integer, so the floor is exactly n / d.
+inline wq::GroupDiv group_magic(int gs) {
+    const uint64_t d = uint64_t(gs / 32);
+    uint32_t lg = 0;
+    while ((uint64_t(1) << lg) < d) ++lg;
+    const uint32_t sh = 24 + lg;
+    const uint64_t mul = ((uint64_t(1) << sh) + d - 1) / d;
+    return wq::GroupDiv{uint32_t(mul), sh};
 }
 
 inline wq_status hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HIP; }

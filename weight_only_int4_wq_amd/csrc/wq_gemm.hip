@@ -10,7 +10,9 @@
 // WAVES_M x WAVES_N grid of wavefronts; K advances in stages of 128.
 //  - A (activations): each stage's BM x 128 fp16 tile goes through LDS,
 //    written in the decoder's pair order, and is read back as
-//    v_mfma_f32_16x16x32_f16 A fragments (16 rows x 32 k).
+//    v_mfma_f32_16x16x32_f16 A fragments (16 rows x 32 k).  A is double
+//    buffered in LDS (one barrier per stage) and the next stage's global
+//    loads of A and B are issued before this stage's MFMAs.
 //  - B (weights): for v_mfma_f32_16x16x32_f16 a lane holds 8 consecutive k
 //    of one output column, which is exactly one 8-code block of the packed
 //    row.  Each lane therefore loads its own packed chunk (32 codes: 4
@@ -44,12 +46,63 @@ __device__ __forceinline__ void load_chunk_b(const uint32_t* p, uint32_t* w) {
     }
 }
 
-template <int BITS, int BM, int BN, int WAVES_M>
+// B operand of one stage for this lane: the raw packed chunk of each of its
+// TN columns plus the group's zero byte and scale bits.  Loads are
+// unconditional (out-of-range columns and chunks read row 0, chunk 0) and
+// are converted only at use, so the compiler never waits on them early.
+template <int BITS, int TN>
+struct BStage {
+    uint32_t w[TN][BITS];
+    uint32_t z[TN], s[TN];
+    bool ok[TN];
+};
+
+template <int BITS, int TN, bool HAS_Z>
+__device__ __forceinline__ void load_b_stage(BStage<BITS, TN>& b, const uint32_t* __restrict__ packed,
+                                             const uint16_t* __restrict__ scales,
+                                             const uint8_t* __restrict__ zeros, int n_lane0, int N,
+                                             size_t row_words, int G, GroupDiv gd, int cg, bool kval) {
+    const int cgc = kval ? cg : 0;
+    const int g = chunk_group(cgc, gd);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = n_lane0 + j * 16;
+        const bool ok = kval && n < N;
+        const size_t nn = ok ? size_t(n) : 0;
+        b.ok[j] = ok;
+        load_chunk_b<BITS>(packed + nn * row_words + (size_t)cgc * BITS, b.w[j]);
+        b.s[j] = scales[nn * G + g];
+        if constexpr (HAS_Z)
+            b.z[j] = zeros[nn * G + g];
+        else
+            b.z[j] = 1u << (BITS - 1);
+    }
+}
+
+// Activation tile of one stage: A_ITERS 16-byte pieces per thread, loaded
+// from clamped addresses; pieces outside the matrix are zeroed when written.
+template <int BM, int BK, int A_ITERS>
+__device__ __forceinline__ void load_a_stage(u4 (&av)[A_ITERS], uint32_t& amask, const uint16_t* __restrict__ x,
+                                             int tid, int m0, int k0, int M, int K) {
+    amask = 0;
+#pragma unroll
+    for (int i = 0; i < A_ITERS; ++i) {
+        const int t = tid + 256 * i;
+        const int row = t / (BK / 8), blk = t % (BK / 8);
+        const int gm = m0 + row, gk = k0 + 8 * blk;
+        const bool ok = gm < M && gk < K;
+        amask |= ok ? (1u << i) : 0u;
+        const size_t off = ok ? (size_t)gm * K + gk : 0;
+        av[i] = *reinterpret_cast<const u4*>(x + off);
+    }
+}
+
+template <int BITS, int BM, int BN, int WAVES_M, bool HAS_Z>
 __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ x,
                                                    const uint32_t* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, uint16_t* __restrict__ y,
-                                                   int M, int N, int K, int gs) {
+                                                   int M, int N, int K, int gs, GroupDiv gd) {
     constexpr int WAVES_N = 4 / WAVES_M;
     constexpr int BK = 128;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -58,7 +111,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     constexpr int A_ITERS = BM * (BK / 8) / 256;
     static_assert(TM >= 1 && TN >= 1 && A_ITERS >= 1, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDA];
+    // Two A buffers: stage s is written to buffer s & 1 while the other one
+    // may still be read by slower wavefronts of stage s - 1.
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -67,6 +122,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     const int G = K / gs;
     const int chunks = K / 32;
     const size_t row_words = (size_t)chunks * BITS;
+    const int n_lane0 = n0 + wn * WN + li;
+    const int stages = (K + BK - 1) / BK;
 
     f4 acc[TM][TN];
 #pragma unroll
@@ -74,74 +131,59 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        // ---- B: this lane's packed chunk of each of its TN columns
-        const int cg = k0 / 32 + lg;
-        const bool kval = cg < chunks;
-        uint32_t bw[TN][BITS];
-        uint32_t zz[TN], ss[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * WN + j * 16 + li;
-            if (kval && n < N) {
-                load_chunk_b<BITS>(packed + (size_t)n * row_words + (size_t)cg * BITS, bw[j]);
-                const int g = (cg * 32) / gs;
-                const uint32_t z = zeros ? uint32_t(zeros[(size_t)n * G + g]) : (1u << (BITS - 1));
-                zz[j] = zero_pair(z);
-                ss[j] = scale_pair(scales[(size_t)n * G + g]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < BITS; ++i) bw[j][i] = 0u;
-                zz[j] = zero_pair(0);
-                ss[j] = 0u;  // zero weight outside the matrix
-            }
-        }
-        // ---- A: global -> registers
-        u4 av[A_ITERS];
+    u4 av[A_ITERS];
+    uint32_t amask;
+    BStage<BITS, TN> bnext;
+    load_a_stage<BM, BK, A_ITERS>(av, amask, x, tid, m0, 0, M, K);
+    load_b_stage<BITS, TN, HAS_Z>(bnext, packed, scales, zeros, n_lane0, N, row_words, G, gd, lg, lg < chunks);
+
+    for (int st = 0; st < stages; ++st) {
+        uint16_t* Ab = As[st & 1];
+        // ---- activations of this stage: registers -> LDS, in pair order
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i) {
             const int t = tid + 256 * i;
             const int row = t / (BK / 8), blk = t % (BK / 8);
-            const int gm = m0 + row, gk = k0 + 8 * blk;
-            if (gm < M && gk < K)
-                av[i] = *reinterpret_cast<const u4*>(x + (size_t)gm * K + gk);
-            else
-                av[i] = u4{0u, 0u, 0u, 0u};
+            const u4 v = ((amask >> i) & 1u) ? av[i] : u4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u4*>(Ab + row * LDA + 8 * blk) = stage_block(v);
         }
-        __syncthreads();  // previous stage's fragments have been read
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i) {
-            const int t = tid + 256 * i;
-            const int row = t / (BK / 8), blk = t % (BK / 8);
-            *reinterpret_cast<u4*>(As + row * LDA + 8 * blk) = stage_block(av[i]);
+        const BStage<BITS, TN> bcur = bnext;
+        // ---- next stage's global loads stay in flight during this stage's MFMAs
+        if (st + 1 < stages) {
+            const int k1 = (st + 1) * BK;
+            load_a_stage<BM, BK, A_ITERS>(av, amask, x, tid, m0, k1, M, K);
+            const int cg = k1 / 32 + lg;
+            load_b_stage<BITS, TN, HAS_Z>(bnext, packed, scales, zeros, n_lane0, N, row_words, G, gd, cg,
+                                          cg < chunks);
         }
         __syncthreads();
 
-        // ---- dequantize B fragments: bf[j][s] = 8 fp16 of k-step s
-        h8 bf[TN][4];
+        uint32_t h[TN][16], zz[TN], ss[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            uint32_t h[16];
-            decode_chunk<BITS>(bw[j], h);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint32_t f[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) f[i] = as_u32(dequant_pair(h[4 * s + i], zz[j], ss[j]));
-                u4 fv = {f[0], f[1], f[2], f[3]};
-                bf[j][s] = __builtin_bit_cast(h8, fv);
-            }
+            decode_chunk<BITS>(bcur.w[j], h[j]);
+            zz[j] = zero_pair(bcur.z[j]);
+            ss[j] = bcur.ok[j] ? scale_pair(uint16_t(bcur.s[j])) : 0u;  // zero weight outside the matrix
         }
-        // ---- MFMA over the 4 k-steps of the stage
+        // ---- 4 k-steps of 32: dequantize block s of every chunk, then MFMA
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            h8 bf[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                uint32_t f[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f[i] = as_u32(dequant_pair(h[j][4 * s + i], zz[j], ss[j]));
+                const u4 fv = {f[0], f[1], f[2], f[3]};
+                bf[j] = __builtin_bit_cast(h8, fv);
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = wm * WM + i * 16 + li;
-                const h8 a = *reinterpret_cast<const h8*>(As + row * LDA + 32 * lg + 8 * s);
+                const h8 a = *reinterpret_cast<const h8*>(Ab + row * LDA + 32 * lg + 8 * s);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[j][s], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[j], acc[i][j], 0, 0, 0);
             }
         }
     }
@@ -178,8 +220,13 @@ template <int BITS, int BM, int BN, int WAVES_M>
 wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M>), grid, dim3(256), 0, s, x, packed, scales, zeros, y, M,
-                       N, K, gs);
+    const GroupDiv gd = wqh::group_magic(gs);
+    if (zeros)
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, true>), grid, dim3(256), 0, s, x, packed, scales, zeros,
+                           y, M, N, K, gs, gd);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, false>), grid, dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gs, gd);
     return wqh::launch_status();
 }
 
@@ -187,7 +234,9 @@ template <int BITS>
 wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     if (M <= 32) return launch_tile<BITS, 32, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    return launch_tile<BITS, 128, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (M <= 64) return launch_tile<BITS, 64, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (M <= 128) return launch_tile<BITS, 128, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    return launch_tile<BITS, 256, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
 }
 
 }  // namespace

@@ -6,15 +6,17 @@
 // single-token generation; weights stay packed and are dequantized on the
 // fly, "AutoAWQ vs The Stack v2", WQLinear_* paragraph).
 //
-// Work split: a 256-thread block owns 4*RW consecutive output columns, one
-// wavefront per RW of them.  Lanes of a wavefront stride over the 32-code
-// chunks of a weight row (consecutive lanes read consecutive 16-byte
-// pieces: coalesced 128-bit loads), so every lane holds a K-slice partial sum
-// per (column, activation row); the partials are reduced across the
-// wavefront with butterfly shuffles at the end (split-K inside the wave, no
-// atomics, deterministic).  The activations are staged once per block in
-// LDS, in the pair order the decoder produces, gathered through perm for
-// act-order; long K is processed in LDS-sized slabs.
+// Work split: a 256-thread block owns 4*R consecutive output columns, one
+// wavefront per R of them.  Lanes of a wavefront stride over the 32-code
+// chunks of a weight row (consecutive lanes read consecutive 16-byte pieces:
+// coalesced 128-bit loads), so every lane holds a K-slice partial sum per
+// (column, activation row); the partials are reduced across the wavefront
+// with butterfly shuffles at the end (split-K inside the wave, no atomics,
+// deterministic).  Each lane keeps D chunk iterations of weight loads in
+// flight (a rolling register pipeline), and the first ones are issued before
+// the activations are staged so the two latencies overlap.  Activations are
+// staged once per block in LDS, in the pair order the decoder produces,
+// gathered through perm for act-order; long K runs in LDS-sized slabs.
 #include "wq_common.h"
 
 namespace {
@@ -42,43 +44,179 @@ __device__ __forceinline__ void load_chunk(const uint32_t* p, uint32_t* w) {
     }
 }
 
+// Sum over the 64 lanes of a wavefront; the result is valid in every lane.
+// Within each row of 16 lanes the partial sums move through DPP (quad
+// permutes, then half-row and row mirrors); the four row sums are then read
+// out with readlane and added in a fixed order (deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
-template <int BITS, int MT, int RW>
-__global__ void __launch_bounds__(256) gemv_kernel(const uint16_t* __restrict__ x,
+// Per-row pointers of the R output columns a wavefront owns.
+template <int BITS, int R>
+struct Rows {
+    const uint32_t* w[R];
+    const uint16_t* s[R];
+    const uint8_t* z[R];
+    bool ok[R];
+};
+
+// Raw operands of one chunk of each of the R rows: packed words, the group's
+// zero-point byte and fp16 scale bits, and whether the chunk is real.
+template <int BITS, int R>
+struct Slot {
+    uint32_t w[R][BITS];
+    uint32_t z[R], s[R];
+    bool ok[R];
+};
+
+// Issue the loads of one chunk (32 codes) of each of the R rows.  Loads are
+// unconditional (an out-of-range row or chunk reads chunk 0 of row 0
+// instead) and their results are only converted at use, so the compiler can
+// keep all of them in flight.
+template <int BITS, int R, bool HAS_Z>
+__device__ __forceinline__ void issue_chunk(const Rows<BITS, R>& rows, GroupDiv gd, int cg, bool valid,
+                                            Slot<BITS, R>& sl) {
+    const int cgc = valid ? cg : 0;
+    const int g = chunk_group(cgc, gd);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        sl.ok[r] = valid && rows.ok[r];
+        load_chunk<BITS>(rows.w[r] + cgc * BITS, sl.w[r]);
+        sl.s[r] = rows.s[r][g];
+        if constexpr (HAS_Z)
+            sl.z[r] = rows.z[r][g];
+        else
+            sl.z[r] = 1u << (BITS - 1);
+    }
+}
+
+// Dequantize one chunk of each row and accumulate its dot product with the
+// staged activations.  LDS holds, per activation row m, four planes (one per
+// 8-code block of a chunk) of one 16-byte entry per chunk: the entry of chunk
+// c, block b, row m is xs[(m * 4 + b) * CN + c], so the lanes of a wavefront
+// (consecutive chunks) read consecutive 16-byte words.
+template <int BITS, int MT, int R>
+__device__ __forceinline__ void compute_chunk(const u4* xc, int CN, const Slot<BITS, R>& sl, float (&acc)[R][MT]) {
+    uint32_t zz[R], ss[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        zz[r] = zero_pair(sl.z[r]);
+        ss[r] = sl.ok[r] ? scale_pair(uint16_t(sl.s[r])) : 0u;  // zero weight outside the matrix
+    }
+    if constexpr (MT <= 4) {
+        uint32_t xp[MT][16];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const u4 v = xc[(m * 4 + b) * CN];
+                xp[m][4 * b] = v.x; xp[m][4 * b + 1] = v.y;
+                xp[m][4 * b + 2] = v.z; xp[m][4 * b + 3] = v.w;
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            uint32_t h[16];
+            decode_chunk<BITS>(sl.w[r], h);
+#pragma unroll
+            for (int p = 0; p < 16; ++p) {
+                const h2 wv = dequant_pair(h[p], zz[r], ss[r]);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    acc[r][m] = __builtin_amdgcn_fdot2(wv, as_h2(xp[m][p]), acc[r][m], false);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            uint32_t h[16];
+            decode_chunk<BITS>(sl.w[r], h);
+            h2 wv[16];
+#pragma unroll
+            for (int p = 0; p < 16; ++p) wv[p] = dequant_pair(h[p], zz[r], ss[r]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const u4 v = xc[(m * 4 + b) * CN];
+                    acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b], as_h2(v.x), acc[r][m], false);
+                    acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b + 1], as_h2(v.y), acc[r][m], false);
+                    acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b + 2], as_h2(v.z), acc[r][m], false);
+                    acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b + 3], as_h2(v.w), acc[r][m], false);
+                }
+            }
+        }
+    }
+}
+
+// General kernel (any K, M <= 16): R rows per wavefront, one block per 4*R
+// rows, activations staged in LDS-sized slabs, D chunk iterations of loads in
+// flight per lane.  Dequantizes every weight to fp16 exactly as wq_dequant.
+template <int BITS, int MT, int R, int D, bool HAS_Z>
+__global__ void __launch_bounds__(256) gemv_slab_kernel(const uint16_t* __restrict__ x,
                                                    const uint32_t* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros,
                                                    const int32_t* __restrict__ perm, uint16_t* __restrict__ y,
-                                                   int M, int N, int K, int gs, int slab) {
-    extern __shared__ u4 xs[];  // [MT][slab / 8] 8-element blocks, staging order
+                                                   int M, int N, int K, int gs, GroupDiv gd, int slab) {
+    extern __shared__ u4 xs[];  // [MT][4][CN] 16-byte entries, staging order
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int n_base = (blockIdx.x * 4 + wave) * RW;
+    const int n_base = (blockIdx.x * 4 + wave) * R;
     const int chunks = K / 32;
     const int G = K / gs;
-    const int slab_blocks = slab / 8;
+    const int CN = slab / 32;
+    const size_t row_words = (size_t)chunks * BITS;
 
-    float acc[RW][MT];
+    Rows<BITS, R> rows;
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int r = 0; r < R; ++r) {
+        const int n = n_base + r;
+        rows.ok[r] = n < N;
+        const int nn = rows.ok[r] ? n : 0;
+        rows.w[r] = packed + (size_t)nn * row_words;
+        rows.s[r] = scales + (size_t)nn * G;
+        rows.z[r] = HAS_Z ? zeros + (size_t)nn * G : nullptr;
+    }
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+
+    Slot<BITS, R> slot[D];
 
     for (int k0 = 0; k0 < K; k0 += slab) {
         const int kn = min(slab, K - k0);
         const int nb = kn / 8;
+        const int cn = kn / 32;
+        const int c0 = k0 / 32;
+        const int J = (cn + 63) / 64;  // chunk iterations of this lane group
+
+        // ---- weights first: the first D iterations' loads go out before the
+        // activations are staged, so both latencies overlap
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int c = lane + 64 * d;
+            issue_chunk<BITS, R, HAS_Z>(rows, gd, c0 + c, c < cn, slot[d]);
+        }
         // ---- stage x[:, k0:k0+kn] in pair order (gathered through perm)
-        for (int t = threadIdx.x; t < MT * nb; t += 256) {
-            const int m = t / nb, b = t - m * nb;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+        for (int bb = threadIdx.x; bb < nb; bb += 256) {
             u4 v = {0u, 0u, 0u, 0u};
             if (m < M) {
                 const uint16_t* xr = x + (size_t)m * K;
-                const int kk = k0 + 8 * b;
+                const int kk = k0 + 8 * bb;
                 if (perm) {
                     uint32_t e[8];
 #pragma unroll
@@ -89,76 +227,22 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t* __restrict__ 
                     v = *reinterpret_cast<const u4*>(xr + kk);
                 }
             }
-            xs[m * slab_blocks + b] = stage_block(v);
+            xs[(m * 4 + (bb & 3)) * CN + (bb >> 2)] = stage_block(v);
         }
         __syncthreads();
 
-        const int cn = kn / 32;
-        const int c0 = k0 / 32;
-        for (int c = lane; c < cn; c += 64) {
-            const int cg = c0 + c;
-            const int g = (cg * 32) / gs;
-            uint32_t w[RW][BITS];
-            uint32_t zz[RW], ss[RW];
+        // ---- rolling pipeline: compute iteration j from slot j % D, then
+        // refill that slot with iteration j + D.  The body has no branches
+        // (a chunk past the end computes with a zero scale from a clamped
+        // LDS address, and refills past the end load a valid dummy chunk),
+        // so each wait covers exactly the slot about to be used.
+        for (int j0 = 0; j0 < J; j0 += D) {
 #pragma unroll
-            for (int r = 0; r < RW; ++r) {
-                const int n = n_base + r;
-                if (n < N) {
-                    load_chunk<BITS>(packed + (size_t)n * chunks * BITS + (size_t)cg * BITS, w[r]);
-                    const uint32_t z = zeros ? uint32_t(zeros[(size_t)n * G + g]) : (1u << (BITS - 1));
-                    zz[r] = zero_pair(z);
-                    ss[r] = scale_pair(scales[(size_t)n * G + g]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < BITS; ++i) w[r][i] = 0u;
-                    zz[r] = zero_pair(0);
-                    ss[r] = 0u;
-                }
-            }
-            // activations of this chunk: 4 blocks = 16 pairs per row
-            const u4* xc = xs + 4 * c;
-            if constexpr (MT <= 4) {
-                uint32_t xp[MT][16];
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const u4 v = xc[m * slab_blocks + b];
-                        xp[m][4 * b] = v.x; xp[m][4 * b + 1] = v.y;
-                        xp[m][4 * b + 2] = v.z; xp[m][4 * b + 3] = v.w;
-                    }
-#pragma unroll
-                for (int r = 0; r < RW; ++r) {
-                    uint32_t h[16];
-                    decode_chunk<BITS>(w[r], h);
-#pragma unroll
-                    for (int p = 0; p < 16; ++p) {
-                        const h2 wv = dequant_pair(h[p], zz[r], ss[r]);
-#pragma unroll
-                        for (int m = 0; m < MT; ++m)
-                            acc[r][m] = __builtin_amdgcn_fdot2(wv, as_h2(xp[m][p]), acc[r][m], false);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < RW; ++r) {
-                    uint32_t h[16];
-                    decode_chunk<BITS>(w[r], h);
-                    h2 wv[16];
-#pragma unroll
-                    for (int p = 0; p < 16; ++p) wv[p] = dequant_pair(h[p], zz[r], ss[r]);
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            const u4 v = xc[m * slab_blocks + b];
-                            acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b], as_h2(v.x), acc[r][m], false);
-                            acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b + 1], as_h2(v.y), acc[r][m], false);
-                            acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b + 2], as_h2(v.z), acc[r][m], false);
-                            acc[r][m] = __builtin_amdgcn_fdot2(wv[4 * b + 3], as_h2(v.w), acc[r][m], false);
-                        }
-                    }
-                }
+            for (int d = 0; d < D; ++d) {
+                const int c = lane + 64 * (j0 + d);
+                compute_chunk<BITS, MT, R>(xs + min(c, cn - 1), CN, slot[d], acc);
+                const int cx = c + 64 * D;
+                issue_chunk<BITS, R, HAS_Z>(rows, gd, c0 + cx, cx < cn, slot[d]);
             }
         }
         __syncthreads();
@@ -166,30 +250,251 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t* __restrict__ 
 
     // ---- split-K reduction across the wavefront, one fp16 rounding
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        const int n = n_base + r;
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const float v = wave_sum(acc[r][m]);
-            if (lane == 0 && n < N && m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+            if (lane == 0 && rows.ok[r] && m < M)
+                y[(size_t)m * N + n_base + r] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
+    }
+}
+
+
+// Streaming kernel (M <= 4 and the whole activation row fits in LDS).
+//
+// Persistent wavefronts: the grid is sized to the machine and wavefront w of
+// the grid takes row groups w, w + W, w + 2W, ... (R output columns each).
+// A lane walks the flat sequence of (row group, chunk iteration) pairs with a
+// D-deep rolling register pipeline, so weight loads stay in flight across row
+// group boundaries; the activations and their per-chunk sums are staged once
+// per block.
+//
+// Arithmetic per chunk of 32 codes and activation row m: with h = 1024 + q
+// (exact fp16 from the exponent trick), A = sum_k x_k * h_k accumulated in
+// fp32 by fp16-pair dot products, and X = sum_k x_k of the chunk,
+//     sum_k x_k * (q_k - z) * s = s * (A - (1024 + z) * X)
+// exactly in real arithmetic; the kernel evaluates the right-hand side in
+// fp32 (one fused multiply-add each).  This skips the per-weight fp16
+// subtract and multiply; the rounding differs from multiplying by fp16
+// dequantized weights by about 2^-12 relative per weight, averaged over K.
+template <int BITS, int MT, int R, int D, bool HAS_Z>
+__global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __restrict__ x,
+                                                          const uint32_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint8_t* __restrict__ zeros,
+                                                          const int32_t* __restrict__ perm,
+                                                          uint16_t* __restrict__ y, int M, int N, int K,
+                                                          GroupDiv gd) {
+    extern __shared__ u4 xs[];  // [MT][4][CN] 16-byte entries, then float xsum[MT][CN]
+    const int CN = K / 32;      // chunks per row
+    float* xsum = reinterpret_cast<float*>(xs + MT * 4 * CN);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int G = chunk_group(CN - 1, gd) + 1;
+    const size_t row_words = (size_t)CN * BITS;
+    const int n_groups = (N + R - 1) / R;
+    const int J = (CN + 63) / 64;  // chunk iterations per row group
+
+    // ---- stage activations (pair order) and per-chunk sums, once per block
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        for (int c = threadIdx.x; c < CN; c += 256) {
+            u4 v[4];
+            const uint16_t* xr = x + (size_t)(m < M ? m : 0) * K + 32 * c;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (perm) {
+                    uint32_t e[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) e[i] = x[(size_t)(m < M ? m : 0) * K + perm[32 * c + 8 * b + i]];
+                    v[b].x = e[0] | (e[1] << 16); v[b].y = e[2] | (e[3] << 16);
+                    v[b].z = e[4] | (e[5] << 16); v[b].w = e[6] | (e[7] << 16);
+                } else {
+                    v[b] = *reinterpret_cast<const u4*>(xr + 8 * b);
+                }
+                if (m >= M) v[b] = u4{0u, 0u, 0u, 0u};
+            }
+            float sum = 0.f;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const u4 o = stage_block(v[b]);
+                xs[(m * 4 + b) * CN + c] = o;
+                const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+                sum = __builtin_amdgcn_fdot2(as_h2(o.x), one, sum, false);
+                sum = __builtin_amdgcn_fdot2(as_h2(o.y), one, sum, false);
+                sum = __builtin_amdgcn_fdot2(as_h2(o.z), one, sum, false);
+                sum = __builtin_amdgcn_fdot2(as_h2(o.w), one, sum, false);
+            }
+            xsum[m * CN + c] = sum;
+        }
+    }
+
+    const int wg0 = blockIdx.x * 4 + wave;
+    const int wstride = gridDim.x * 4;
+    const int my_groups = wg0 < n_groups ? (n_groups - wg0 + wstride - 1) / wstride : 0;
+    const int T = my_groups * J;  // flat (row group, chunk iteration) count of this wave
+
+    // issue-side and compute-side positions in the flat sequence
+    int i_rg = wg0, i_j = 0, c_rg = wg0, c_j = 0;
+
+    Slot<BITS, R> slot[D];
+    auto issue = [&](Slot<BITS, R>& sl, int t) {
+        const int c = lane + 64 * i_j;
+        const bool valid = (t < T) && c < CN;
+        const int cgc = valid ? c : 0;
+        const int g = chunk_group(cgc, gd);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = i_rg * R + r;
+            const bool ok = valid && n < N;
+            const size_t nn = ok ? size_t(n) : 0;
+            sl.ok[r] = ok;
+            load_chunk<BITS>(packed + nn * row_words + (size_t)cgc * BITS, sl.w[r]);
+            sl.s[r] = scales[nn * G + g];
+            if constexpr (HAS_Z)
+                sl.z[r] = zeros[nn * G + g];
+            else
+                sl.z[r] = 1u << (BITS - 1);
+        }
+        const bool wrap = (i_j + 1 == J);
+        i_j = wrap ? 0 : i_j + 1;
+        i_rg += wrap ? wstride : 0;
+    };
+
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(slot[d], d);
+    __syncthreads();
+
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+
+    for (int t0 = 0; t0 < T; t0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int t = t0 + d;
+            // ---- compute iteration t from slot d
+            {
+                const int c = min(lane + 64 * c_j, CN - 1);
+                uint32_t xp[MT][16];
+                float X[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const u4 v = xs[(m * 4 + b) * CN + c];
+                        xp[m][4 * b] = v.x; xp[m][4 * b + 1] = v.y;
+                        xp[m][4 * b + 2] = v.z; xp[m][4 * b + 3] = v.w;
+                    }
+                    X[m] = xsum[m * CN + c];
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    uint32_t h[16];
+                    decode_chunk<BITS>(slot[d].w[r], h);
+                    const float sf = slot[d].ok[r] ? float(__builtin_bit_cast(_Float16, uint16_t(slot[d].s[r]))) : 0.f;
+                    const float zf = float(1024u + slot[d].z[r]);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        float a = 0.f;
+#pragma unroll
+                        for (int p = 0; p < 16; ++p) a = __builtin_amdgcn_fdot2(as_h2(h[p]), as_h2(xp[m][p]), a, false);
+                        acc[r][m] = __builtin_fmaf(sf, __builtin_fmaf(-zf, X[m], a), acc[r][m]);
+                    }
+                }
+            }
+            // ---- end of a row group: reduce across the wavefront and store
+            if (c_j == J - 1 && t < T) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int n = c_rg * R + r;
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const float v = wave_sum(acc[r][m]);
+                        acc[r][m] = 0.f;
+                        if (lane == 0 && n < N && m < M)
+                            y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                    }
+                }
+            }
+            {
+                const bool wrap = (c_j + 1 == J);
+                c_j = wrap ? 0 : c_j + 1;
+                c_rg += wrap ? wstride : 0;
+            }
+            // ---- refill slot d with iteration t + D
+            issue(slot[d], t + D);
         }
     }
 }
 
 constexpr size_t kLdsBudget = 64 * 1024;
 
-template <int BITS, int MT>
-wq_status launch_mt(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                    const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
-    constexpr int RW = (MT <= 2) ? 4 : 2;
+template <int BITS, int MT, int R, int D>
+wq_status launch_cfg(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                     const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     int slab = int(kLdsBudget / (size_t(MT) * 2));
     slab = (slab / 32) * 32;
     if (slab > K) slab = K;
     const size_t lds = size_t(MT) * slab * 2;
-    const int blocks = (N + 4 * RW - 1) / (4 * RW);
-    hipLaunchKernelGGL((gemv_kernel<BITS, MT, RW>), dim3(blocks), dim3(256), lds, s, x, packed, scales, zeros, perm,
-                       y, M, N, K, gs, slab);
+    const int blocks = (N + 4 * R - 1) / (4 * R);
+    const GroupDiv gd = wqh::group_magic(gs);
+    if (zeros)
+        hipLaunchKernelGGL((gemv_slab_kernel<BITS, MT, R, D, true>), dim3(blocks), dim3(256), lds, s, x, packed,
+                           scales, zeros, perm, y, M, N, K, gs, gd, slab);
+    else
+        hipLaunchKernelGGL((gemv_slab_kernel<BITS, MT, R, D, false>), dim3(blocks), dim3(256), lds, s, x, packed,
+                           scales, zeros, perm, y, M, N, K, gs, gd, slab);
     return wqh::launch_status();
+}
+
+// LDS bytes the streaming kernel stages: fp16 activations plus one fp32 sum
+// per 32-element chunk, per activation row.
+inline size_t stream_lds_bytes(int MT, int K) { return size_t(MT) * (size_t(K) * 2 + size_t(K / 32) * 4); }
+
+constexpr int kStreamBlocksPerCU = 2;
+
+template <int BITS, int MT, int R, int D>
+wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                        const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const int n_groups = (N + R - 1) / R;
+    int blocks = (n_groups + 3) / 4;
+    if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
+    const size_t lds = stream_lds_bytes(MT, K);
+    const GroupDiv gd = wqh::group_magic(gs);
+    if (zeros)
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, true>), dim3(blocks), dim3(256), lds, s, x, packed,
+                           scales, zeros, perm, y, M, N, K, gd);
+    else
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, false>), dim3(blocks), dim3(256), lds, s, x, packed,
+                           scales, zeros, perm, y, M, N, K, gd);
+    return wqh::launch_status();
+}
+
+// Streaming kernel when the activations fit in LDS and M <= 4; otherwise the
+// slab kernel.  Rows per wavefront grow with the layer width.
+template <int BITS, int MT>
+wq_status launch_mt(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                    const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+    if constexpr (MT > 4) {
+        return launch_cfg<BITS, MT, 1, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+    } else {
+        if (stream_lds_bytes(MT, K) <= kLdsBudget) {
+            if (N < 8192) return launch_stream<BITS, MT, 1, 4>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+            return launch_stream<BITS, MT, 2, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        }
+        if (N < 8192) return launch_cfg<BITS, MT, 1, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        if (N < 16384) return launch_cfg<BITS, MT, 2, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        return launch_cfg<BITS, MT, 4, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+    }
 }
 
 template <int BITS>
