@@ -52,8 +52,9 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--only", choices=["decode", "prefill"], default=None,
-                   help="run one leg only (for profiler runs); prints that leg's figures")
+    p.add_argument("--only", choices=["decode", "prefill", "copy"], default=None,
+                   help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
+                        "copies of a known size, the reference for scaling HBM byte counters")
     return p.parse_args()
 
 
@@ -269,6 +270,16 @@ def main():
     wq.lib()
     gemm_steps = args.gemm_steps or max(10, args.steps // 5)
 
+    if args.only == "copy":
+        nbytes = 512 << 20
+        src = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"leg": "copy", "bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
+                          "copies": args.steps}), flush=True)
+        return
     if args.only == "decode":
         dec = decode_leg(wq, torch, args.steps, args.warmup)
         print(json.dumps({"leg": "decode", "ms_per_step": dec["ms"], "per_layer": dec["per_layer"]}), flush=True)

@@ -267,18 +267,26 @@ __global__ void __launch_bounds__(256) gemv_slab_kernel(const uint16_t* __restri
 // the grid takes row groups w, w + W, w + 2W, ... (R output columns each).
 // A lane walks the flat sequence of (row group, chunk iteration) pairs with a
 // D-deep rolling register pipeline, so weight loads stay in flight across row
-// group boundaries; the activations and their per-chunk sums are staged once
-// per block.
+// group boundaries; the activations and their chunk sums are staged once per
+// block.  Each slot holds CPL consecutive chunks (CPL * 32 codes, one group)
+// of each of the R rows; consecutive lanes read consecutive CPL * 16 bytes.
 //
-// Arithmetic per chunk of 32 codes and activation row m: with h = 1024 + q
-// (exact fp16 from the exponent trick), A = sum_k x_k * h_k accumulated in
-// fp32 by fp16-pair dot products, and X = sum_k x_k of the chunk,
+// Arithmetic per slot (CPL chunks of one group) and activation row m: with
+// h = 1024 + q (exact fp16 from the exponent trick), A = sum_k x_k * h_k
+// accumulated in fp32 by fp16-pair dot products, and X = sum_k x_k,
 //     sum_k x_k * (q_k - z) * s = s * (A - (1024 + z) * X)
 // exactly in real arithmetic; the kernel evaluates the right-hand side in
 // fp32 (one fused multiply-add each).  This skips the per-weight fp16
 // subtract and multiply; the rounding differs from multiplying by fp16
 // dequantized weights by about 2^-12 relative per weight, averaged over K.
-template <int BITS, int MT, int R, int D, bool HAS_Z>
+template <int BITS, int R, int CPL>
+struct WideSlot {
+    uint32_t w[R][CPL][BITS];
+    uint32_t z[R], s[R];
+    bool ok[R];
+};
+
+template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z>
 __global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __restrict__ x,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
@@ -286,71 +294,41 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ perm,
                                                           uint16_t* __restrict__ y, int M, int N, int K,
                                                           GroupDiv gd) {
-    extern __shared__ u4 xs[];  // [MT][4][CN] 16-byte entries, then float xsum[MT][CN]
-    const int CN = K / 32;      // chunks per row
+    // LDS: u4 xs[MT][4][CPL][CNP] (activation pairs), then float xsum[MT][CNP]
+    extern __shared__ u4 xs[];
+    const int CN = K / 32;       // chunks per row
+    const int CNP = CN / CPL;    // slots per row
     float* xsum = reinterpret_cast<float*>(xs + MT * 4 * CN);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int G = chunk_group(CN - 1, gd) + 1;
     const size_t row_words = (size_t)CN * BITS;
     const int n_groups = (N + R - 1) / R;
-    const int J = (CN + 63) / 64;  // chunk iterations per row group
-
-    // ---- stage activations (pair order) and per-chunk sums, once per block
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        for (int c = threadIdx.x; c < CN; c += 256) {
-            u4 v[4];
-            const uint16_t* xr = x + (size_t)(m < M ? m : 0) * K + 32 * c;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if (perm) {
-                    uint32_t e[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) e[i] = x[(size_t)(m < M ? m : 0) * K + perm[32 * c + 8 * b + i]];
-                    v[b].x = e[0] | (e[1] << 16); v[b].y = e[2] | (e[3] << 16);
-                    v[b].z = e[4] | (e[5] << 16); v[b].w = e[6] | (e[7] << 16);
-                } else {
-                    v[b] = *reinterpret_cast<const u4*>(xr + 8 * b);
-                }
-                if (m >= M) v[b] = u4{0u, 0u, 0u, 0u};
-            }
-            float sum = 0.f;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const u4 o = stage_block(v[b]);
-                xs[(m * 4 + b) * CN + c] = o;
-                const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-                sum = __builtin_amdgcn_fdot2(as_h2(o.x), one, sum, false);
-                sum = __builtin_amdgcn_fdot2(as_h2(o.y), one, sum, false);
-                sum = __builtin_amdgcn_fdot2(as_h2(o.z), one, sum, false);
-                sum = __builtin_amdgcn_fdot2(as_h2(o.w), one, sum, false);
-            }
-            xsum[m * CN + c] = sum;
-        }
-    }
+    const int J = (CNP + 63) / 64;  // slot iterations per row group
 
     const int wg0 = blockIdx.x * 4 + wave;
     const int wstride = gridDim.x * 4;
     const int my_groups = wg0 < n_groups ? (n_groups - wg0 + wstride - 1) / wstride : 0;
-    const int T = my_groups * J;  // flat (row group, chunk iteration) count of this wave
+    const int T = my_groups * J;  // flat (row group, slot iteration) count of this wave
 
     // issue-side and compute-side positions in the flat sequence
     int i_rg = wg0, i_j = 0, c_rg = wg0, c_j = 0;
 
-    Slot<BITS, R> slot[D];
-    auto issue = [&](Slot<BITS, R>& sl, int t) {
-        const int c = lane + 64 * i_j;
-        const bool valid = (t < T) && c < CN;
-        const int cgc = valid ? c : 0;
-        const int g = chunk_group(cgc, gd);
+    WideSlot<BITS, R, CPL> slot[D];
+    auto issue = [&](WideSlot<BITS, R, CPL>& sl, int t) {
+        const int cp = lane + 64 * i_j;
+        const bool valid = (t < T) && cp < CNP;
+        const int cpc = valid ? cp : 0;
+        const int g = chunk_group(cpc * CPL, gd);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = i_rg * R + r;
             const bool ok = valid && n < N;
             const size_t nn = ok ? size_t(n) : 0;
             sl.ok[r] = ok;
-            load_chunk<BITS>(packed + nn * row_words + (size_t)cgc * BITS, sl.w[r]);
+            const uint32_t* src = packed + nn * row_words + (size_t)cpc * CPL * BITS;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) load_chunk<BITS>(src + e * BITS, sl.w[r][e]);
             sl.s[r] = scales[nn * G + g];
             if constexpr (HAS_Z)
                 sl.z[r] = zeros[nn * G + g];
@@ -362,8 +340,46 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __rest
         i_rg += wrap ? wstride : 0;
     };
 
+    // ---- weight loads of the first D iterations go out first, so their HBM
+    // latency overlaps the activation staging below
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(slot[d], d);
+
+    // ---- stage activations (pair order) and per-slot sums, once per block
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const size_t xrow = (size_t)(m < M ? m : 0) * K;
+        for (int cp = threadIdx.x; cp < CNP; cp += 256) {
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                const int c = cp * CPL + e;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    u4 v;
+                    if (perm) {
+                        uint32_t el[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) el[i] = x[xrow + perm[32 * c + 8 * b + i]];
+                        v.x = el[0] | (el[1] << 16); v.y = el[2] | (el[3] << 16);
+                        v.z = el[4] | (el[5] << 16); v.w = el[6] | (el[7] << 16);
+                    } else {
+                        v = *reinterpret_cast<const u4*>(x + xrow + 32 * c + 8 * b);
+                    }
+                    if (m >= M) v = u4{0u, 0u, 0u, 0u};
+                    const u4 o = stage_block(v);
+                    xs[((m * 4 + b) * CPL + e) * CNP + cp] = o;
+                    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+                    sum = __builtin_amdgcn_fdot2(as_h2(o.x), one, sum, false);
+                    sum = __builtin_amdgcn_fdot2(as_h2(o.y), one, sum, false);
+                    sum = __builtin_amdgcn_fdot2(as_h2(o.z), one, sum, false);
+                    sum = __builtin_amdgcn_fdot2(as_h2(o.w), one, sum, false);
+                }
+            }
+            xsum[m * CNP + cp] = sum;
+        }
+    }
+
     __syncthreads();
 
     float acc[R][MT];
@@ -378,32 +394,45 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __rest
             const int t = t0 + d;
             // ---- compute iteration t from slot d
             {
-                const int c = min(lane + 64 * c_j, CN - 1);
-                uint32_t xp[MT][16];
+                const int cp = min(lane + 64 * c_j, CNP - 1);
                 float X[MT];
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
+                for (int m = 0; m < MT; ++m) X[m] = xsum[m * CNP + cp];
+                float a[R][MT];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const u4 v = xs[(m * 4 + b) * CN + c];
-                        xp[m][4 * b] = v.x; xp[m][4 * b + 1] = v.y;
-                        xp[m][4 * b + 2] = v.z; xp[m][4 * b + 3] = v.w;
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) a[r][m] = 0.f;
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) {
+                    uint32_t xp[MT][16];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const u4 v = xs[((m * 4 + b) * CPL + e) * CNP + cp];
+                            xp[m][4 * b] = v.x; xp[m][4 * b + 1] = v.y;
+                            xp[m][4 * b + 2] = v.z; xp[m][4 * b + 3] = v.w;
+                        }
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        uint32_t h[16];
+                        decode_chunk<BITS>(slot[d].w[r][e], h);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m)
+#pragma unroll
+                            for (int p = 0; p < 16; ++p)
+                                a[r][m] = __builtin_amdgcn_fdot2(as_h2(h[p]), as_h2(xp[m][p]), a[r][m], false);
                     }
-                    X[m] = xsum[m * CN + c];
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    uint32_t h[16];
-                    decode_chunk<BITS>(slot[d].w[r], h);
-                    const float sf = slot[d].ok[r] ? float(__builtin_bit_cast(_Float16, uint16_t(slot[d].s[r]))) : 0.f;
+                    const float sf =
+                        slot[d].ok[r] ? float(__builtin_bit_cast(_Float16, uint16_t(slot[d].s[r]))) : 0.f;
                     const float zf = float(1024u + slot[d].z[r]);
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        float a = 0.f;
-#pragma unroll
-                        for (int p = 0; p < 16; ++p) a = __builtin_amdgcn_fdot2(as_h2(h[p]), as_h2(xp[m][p]), a, false);
-                        acc[r][m] = __builtin_fmaf(sf, __builtin_fmaf(-zf, X[m], a), acc[r][m]);
-                    }
+                    for (int m = 0; m < MT; ++m)
+                        acc[r][m] = __builtin_fmaf(sf, __builtin_fmaf(-zf, X[m], a[r][m]), acc[r][m]);
                 }
             }
             // ---- end of a row group: reduce across the wavefront and store
@@ -452,12 +481,34 @@ wq_status launch_cfg(const uint16_t* x, const uint32_t* packed, const uint16_t* 
 }
 
 // LDS bytes the streaming kernel stages: fp16 activations plus one fp32 sum
-// per 32-element chunk, per activation row.
-inline size_t stream_lds_bytes(int MT, int K) { return size_t(MT) * (size_t(K) * 2 + size_t(K / 32) * 4); }
+// per slot, per activation row.
+inline size_t stream_lds_bytes(int MT, int K, int cpl) {
+    return size_t(MT) * (size_t(K) * 2 + size_t(K / (32 * cpl)) * 4);
+}
 
-constexpr int kStreamBlocksPerCU = 2;
+// Launch shape of the streaming kernel (blocks per CU; rows per wavefront
+// and pipeline depth for layers narrower / wider than 8192 columns).
+#ifndef WQ_GEMV_BPC
+#define WQ_GEMV_BPC 2
+#endif
+#ifndef WQ_GEMV_NARROW_R
+#define WQ_GEMV_NARROW_R 1
+#endif
+#ifndef WQ_GEMV_NARROW_D
+#define WQ_GEMV_NARROW_D 4
+#endif
+#ifndef WQ_GEMV_WIDE_R
+#define WQ_GEMV_WIDE_R 2
+#endif
+#ifndef WQ_GEMV_WIDE_D
+#define WQ_GEMV_WIDE_D 2
+#endif
+#ifndef WQ_GEMV_CPL
+#define WQ_GEMV_CPL 1
+#endif
+constexpr int kStreamBlocksPerCU = WQ_GEMV_BPC;
 
-template <int BITS, int MT, int R, int D>
+template <int BITS, int MT, int R, int D, int CPL>
 wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     int dev = 0, cus = 256;
@@ -468,29 +519,42 @@ wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_
     const int n_groups = (N + R - 1) / R;
     int blocks = (n_groups + 3) / 4;
     if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
-    const size_t lds = stream_lds_bytes(MT, K);
+    const size_t lds = stream_lds_bytes(MT, K, CPL);
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, true>), dim3(blocks), dim3(256), lds, s, x, packed,
-                           scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true>), dim3(blocks), dim3(256), lds, s, x,
+                           packed, scales, zeros, perm, y, M, N, K, gd);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, false>), dim3(blocks), dim3(256), lds, s, x, packed,
-                           scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false>), dim3(blocks), dim3(256), lds, s, x,
+                           packed, scales, zeros, perm, y, M, N, K, gd);
     return wqh::launch_status();
 }
 
-// Streaming kernel when the activations fit in LDS and M <= 4; otherwise the
-// slab kernel.  Rows per wavefront grow with the layer width.
+template <int BITS, int MT, int CPL>
+wq_status launch_stream_cpl(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                            const uint8_t* zeros, const int32_t* perm, uint16_t* y, int M, int N, int K, int gs,
+                            hipStream_t s) {
+    if (N < 8192)
+        return launch_stream<BITS, MT, WQ_GEMV_NARROW_R, WQ_GEMV_NARROW_D, CPL>(x, packed, scales, zeros, perm, y, M,
+                                                                               N, K, gs, s);
+    return launch_stream<BITS, MT, WQ_GEMV_WIDE_R, WQ_GEMV_WIDE_D, CPL>(x, packed, scales, zeros, perm, y, M, N, K,
+                                                                       gs, s);
+}
+
+// Streaming kernel when the activations fit in LDS and M <= 4 (two chunks
+// per slot when every pair of chunks shares a group); otherwise the slab
+// kernel.
 template <int BITS, int MT>
 wq_status launch_mt(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                     const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     if constexpr (MT > 4) {
         return launch_cfg<BITS, MT, 1, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
     } else {
-        if (stream_lds_bytes(MT, K) <= kLdsBudget) {
-            if (N < 8192) return launch_stream<BITS, MT, 1, 4>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
-            return launch_stream<BITS, MT, 2, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
-        }
+        constexpr int CPL = WQ_GEMV_CPL;
+        if (CPL > 1 && K % (32 * CPL) == 0 && gs % (32 * CPL) == 0 && stream_lds_bytes(MT, K, CPL) <= kLdsBudget)
+            return launch_stream_cpl<BITS, MT, CPL>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        if (stream_lds_bytes(MT, K, 1) <= kLdsBudget)
+            return launch_stream_cpl<BITS, MT, 1>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         if (N < 8192) return launch_cfg<BITS, MT, 1, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         if (N < 16384) return launch_cfg<BITS, MT, 2, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         return launch_cfg<BITS, MT, 4, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
