@@ -115,6 +115,66 @@ __device__ __forceinline__ void decode_chunk<3>(const uint32_t* w, uint32_t* h) 
     }
 }
 
+// Natural-order decode of block b (8 codes) of a chunk into four fp16 pairs
+// (1024 + q_{2i}, 1024 + q_{2i+1}), i = 0..3: consecutive codes share a pair,
+// so the pairs line up with activations in their stored order (the layout
+// matrix-core fragments read from LDS).
+template <int BITS>
+__device__ __forceinline__ void decode_block_nat(const uint32_t* w, int b, uint32_t* h);
+
+template <>
+__device__ __forceinline__ void decode_block_nat<4>(const uint32_t* w, int b, uint32_t* h) {
+    // byte i of v holds codes 2i (low nibble) and 2i+1 (high nibble); byte i
+    // of v >> 4 has code 2i+1 in its low nibble.
+    const uint32_t v = w[b], v4 = v >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t sel = 0x0C000C00u | ((4u + i) << 16) | uint32_t(i);
+        h[i] = and_or(__builtin_amdgcn_perm(v4, v, sel), 0x000F000Fu, kMagic2);
+    }
+}
+
+template <>
+__device__ __forceinline__ void decode_block_nat<8>(const uint32_t* w, int b, uint32_t* h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t v = w[2 * b + (i >> 1)];
+        const uint32_t j = 2u * (i & 1);
+        const uint32_t sel = 0x0C000C00u | ((j + 1u) << 16) | j;
+        h[i] = __builtin_amdgcn_perm(v, v, sel) | kMagic2;
+    }
+}
+
+template <>
+__device__ __forceinline__ void decode_block_nat<2>(const uint32_t* w, int b, uint32_t* h) {
+    // block b is the 16 bits at offset 16*(b&1) of word b>>1; code pair i is
+    // nibble i of the block.  Byte j of v >> 2 holds code 2i+1 where byte j
+    // of v holds code 2i.
+    const uint32_t v = w[b >> 1], v2 = v >> 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t j = 2u * (b & 1) + (i >> 1);
+        const uint32_t sel = 0x0C000C00u | ((4u + j) << 16) | j;
+        const uint32_t t = __builtin_amdgcn_perm(v2, v, sel) >> (4 * (i & 1));
+        h[i] = and_or(t, 0x00030003u, kMagic2);
+    }
+}
+
+template <>
+__device__ __forceinline__ void decode_block_nat<3>(const uint32_t* w, int b, uint32_t* h) {
+    uint32_t v;
+    if (b == 0) v = w[0] & 0x00FFFFFFu;
+    else if (b == 1) v = __builtin_amdgcn_alignbit(w[1], w[0], 24) & 0x00FFFFFFu;
+    else if (b == 2) v = __builtin_amdgcn_alignbit(w[2], w[1], 16) & 0x00FFFFFFu;
+    else v = w[2] >> 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_amdgcn_ubfe(v, 6 * i, 3);
+        const uint32_t hi = __builtin_amdgcn_ubfe(v, 6 * i + 3, 3);
+        h[i] = (lo | (hi << 16)) | kMagic2;
+    }
+}
+
 // Group of a 32-code chunk, cg / (group_size / 32), by multiply-shift with a
 // magic number from group_magic() on the host: exact for cg < 2^24 and free
 // of branches (a branch around it would make the compiler drain every load

@@ -7,12 +7,13 @@
 // without materializing fp16 weights in memory).
 //
 // Tiling: a 256-thread block owns a BM x BN output tile, split over a
-// WAVES_M x WAVES_N grid of wavefronts; K advances in stages of 128.
-//  - A (activations): each stage's BM x 128 fp16 tile goes through LDS,
-//    written in the decoder's pair order, and is read back as
-//    v_mfma_f32_16x16x32_f16 A fragments (16 rows x 32 k).  A is double
-//    buffered in LDS (one barrier per stage) and the next stage's global
-//    loads of A and B are issued before this stage's MFMAs.
+// WAVES_M x WAVES_N grid of wavefronts; K advances in stages of BK = 128.
+//  - A (activations): each stage's BM x 128 fp16 tile is copied from global
+//    memory straight into LDS by global_load_lds_dwordx4 (no registers),
+//    double buffered, one barrier per stage: the copy of stage s + 1 is in
+//    flight while stage s is multiplied.  In LDS a row is 16 units of 16
+//    bytes and unit u of row r is stored at position u ^ (r mod 16), so the
+//    sixteen rows a fragment read touches fall on distinct banks.
 //  - B (weights): for v_mfma_f32_16x16x32_f16 a lane holds 8 consecutive k
 //    of one output column, which is exactly one 8-code block of the packed
 //    row.  Each lane therefore loads its own packed chunk (32 codes: 4
@@ -21,6 +22,9 @@
 //    fragments: the dequantized tile lives in registers rather than LDS.
 //    Lane group g (lanes 16g..16g+15) takes chunk g of the stage, and the A
 //    fragments are read with the same k mapping, so the k sum is unchanged.
+//  - Tiles are numbered with M fastest and dealt to the XCDs in contiguous
+//    ranges, so the blocks sharing a column of packed weights run on the
+//    same XCD and share its L2.
 #include "wq_common.h"
 
 namespace {
@@ -46,55 +50,15 @@ __device__ __forceinline__ void load_chunk_b(const uint32_t* p, uint32_t* w) {
     }
 }
 
-// B operand of one stage for this lane: the raw packed chunk of each of its
-// TN columns plus the group's zero byte and scale bits.  Loads are
-// unconditional (out-of-range columns and chunks read row 0, chunk 0) and
-// are converted only at use, so the compiler never waits on them early.
-template <int BITS, int TN>
-struct BStage {
-    uint32_t w[TN][BITS];
-    uint32_t z[TN], s[TN];
-    bool ok[TN];
-};
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
-template <int BITS, int TN, bool HAS_Z>
-__device__ __forceinline__ void load_b_stage(BStage<BITS, TN>& b, const uint32_t* __restrict__ packed,
-                                             const uint16_t* __restrict__ scales,
-                                             const uint8_t* __restrict__ zeros, int n_lane0, int N,
-                                             size_t row_words, int G, GroupDiv gd, int cg, bool kval) {
-    const int cgc = kval ? cg : 0;
-    const int g = chunk_group(cgc, gd);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int n = n_lane0 + j * 16;
-        const bool ok = kval && n < N;
-        const size_t nn = ok ? size_t(n) : 0;
-        b.ok[j] = ok;
-        load_chunk_b<BITS>(packed + nn * row_words + (size_t)cgc * BITS, b.w[j]);
-        b.s[j] = scales[nn * G + g];
-        if constexpr (HAS_Z)
-            b.z[j] = zeros[nn * G + g];
-        else
-            b.z[j] = 1u << (BITS - 1);
-    }
-}
-
-// Activation tile of one stage: A_ITERS 16-byte pieces per thread, loaded
-// from clamped addresses; pieces outside the matrix are zeroed when written.
-template <int BM, int BK, int A_ITERS>
-__device__ __forceinline__ void load_a_stage(u4 (&av)[A_ITERS], uint32_t& amask, const uint16_t* __restrict__ x,
-                                             int tid, int m0, int k0, int M, int K) {
-    amask = 0;
-#pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) {
-        const int t = tid + 256 * i;
-        const int row = t / (BK / 8), blk = t % (BK / 8);
-        const int gm = m0 + row, gk = k0 + 8 * blk;
-        const bool ok = gm < M && gk < K;
-        amask |= ok ? (1u << i) : 0u;
-        const size_t off = ok ? (size_t)gm * K + gk : 0;
-        av[i] = *reinterpret_cast<const u4*>(x + off);
-    }
+// Tile index of block b when blocks are dealt round-robin to `parts` XCDs:
+// XCD j gets the contiguous tile range [start_j, start_j + count_j).
+__device__ __forceinline__ int xcd_tile(int b, int tiles, int parts) {
+    const int q = tiles / parts, r = tiles % parts;
+    const int xcd = b % parts, k = b / parts;
+    return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
 template <int BITS, int BM, int BN, int WAVES_M, bool HAS_Z>
@@ -102,28 +66,70 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
                                                    const uint32_t* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, uint16_t* __restrict__ y,
-                                                   int M, int N, int K, int gs, GroupDiv gd) {
+                                                   int M, int N, int K, GroupDiv gd, int m_tiles, int tiles) {
     constexpr int WAVES_N = 4 / WAVES_M;
     constexpr int BK = 128;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int LDA = BK + 8;              // halves per LDS row: 16-byte pad
-    constexpr int A_ITERS = BM * (BK / 8) / 256;
-    static_assert(TM >= 1 && TN >= 1 && A_ITERS >= 1, "tile shape");
+    constexpr int ROW_BYTES = BK * 2;          // 16 units of 16 bytes
+    constexpr int A_INSTR = BM / 16;           // 1 KB copies per wavefront per stage
+    static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1, "tile shape");
 
-    // Two A buffers: stage s is written to buffer s & 1 while the other one
-    // may still be read by slower wavefronts of stage s - 1.
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDA];
+    __shared__ __attribute__((aligned(1024))) uint8_t As[2][BM * ROW_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int li = lane & 15, lg = lane >> 4;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int G = K / gs;
+    const int tile = xcd_tile(blockIdx.x, tiles, 8);
+    const int m0 = (tile % m_tiles) * BM, n0 = (tile / m_tiles) * BN;
     const int chunks = K / 32;
+    const int G = chunk_group(chunks - 1, gd) + 1;
     const size_t row_words = (size_t)chunks * BITS;
     const int n_lane0 = n0 + wn * WN + li;
     const int stages = (K + BK - 1) / BK;
+
+    // ---- A: this wavefront's share of a stage, global -> LDS directly.
+    // Copy i of the wavefront fills units [64 * (wave * A_INSTR + i), +64):
+    // lane l writes unit 64 * (...) + l, i.e. row (unit / 16), position l % 16,
+    // which holds logical unit (l % 16) ^ (row % 16).  Rows past M and
+    // columns past K read valid in-range data instead (their products only
+    // reach output rows that are not stored, or meet zero weights).
+    auto issue_a = [&](int buf, int k0) {
+#pragma unroll
+        for (int i = 0; i < A_INSTR; ++i) {
+            const int unit0 = (wave * A_INSTR + i) * 64;
+            const int row = (unit0 >> 4) + (lane >> 4);
+            const int u = (lane & 15) ^ (row & 15);
+            const int gm = min(m0 + row, M - 1);
+            const int gk = k0 + 8 * u;
+            const uint16_t* src = x + (size_t)gm * K + (gk < K ? gk : 0);
+            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&As[buf][unit0 * 16]), 16, 0, 0);
+        }
+    };
+
+    // ---- B: raw packed chunk, zero byte and scale bits of each of the TN
+    // columns this lane feeds (zero scale outside the matrix)
+    uint32_t bw[TN][BITS], bz[TN], bs[TN];
+    bool bok[TN];
+    auto issue_b = [&](int k0) {
+        const int cg = k0 / 32 + lg;
+        const bool kval = cg < chunks;
+        const int cgc = kval ? cg : 0;
+        const int g = chunk_group(cgc, gd);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n_lane0 + j * 16;
+            const bool ok = kval && n < N;
+            const size_t nn = ok ? size_t(n) : 0;
+            bok[j] = ok;
+            load_chunk_b<BITS>(packed + nn * row_words + (size_t)cgc * BITS, bw[j]);
+            bs[j] = scales[nn * G + g];
+            if constexpr (HAS_Z)
+                bz[j] = zeros[nn * G + g];
+            else
+                bz[j] = 1u << (BITS - 1);
+        }
+    };
 
     f4 acc[TM][TN];
 #pragma unroll
@@ -131,60 +137,53 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    u4 av[A_ITERS];
-    uint32_t amask;
-    BStage<BITS, TN> bnext;
-    load_a_stage<BM, BK, A_ITERS>(av, amask, x, tid, m0, 0, M, K);
-    load_b_stage<BITS, TN, HAS_Z>(bnext, packed, scales, zeros, n_lane0, N, row_words, G, gd, lg, lg < chunks);
+    issue_a(0, 0);
+    issue_b(0);
 
     for (int st = 0; st < stages; ++st) {
-        uint16_t* Ab = As[st & 1];
-        // ---- activations of this stage: registers -> LDS, in pair order
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i) {
-            const int t = tid + 256 * i;
-            const int row = t / (BK / 8), blk = t % (BK / 8);
-            const u4 v = ((amask >> i) & 1u) ? av[i] : u4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u4*>(Ab + row * LDA + 8 * blk) = stage_block(v);
-        }
-        const BStage<BITS, TN> bcur = bnext;
-        // ---- next stage's global loads stay in flight during this stage's MFMAs
-        if (st + 1 < stages) {
-            const int k1 = (st + 1) * BK;
-            load_a_stage<BM, BK, A_ITERS>(av, amask, x, tid, m0, k1, M, K);
-            const int cg = k1 / 32 + lg;
-            load_b_stage<BITS, TN, HAS_Z>(bnext, packed, scales, zeros, n_lane0, N, row_words, G, gd, cg,
-                                          cg < chunks);
-        }
+        // every copy of stage st (all wavefronts) has landed, and every
+        // wavefront is done reading the buffer the next copy overwrites
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
 
-        uint32_t h[TN][16], zz[TN], ss[TN];
+        uint32_t cw[TN][BITS], zz[TN], ss[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            decode_chunk<BITS>(bcur.w[j], h[j]);
-            zz[j] = zero_pair(bcur.z[j]);
-            ss[j] = bcur.ok[j] ? scale_pair(uint16_t(bcur.s[j])) : 0u;  // zero weight outside the matrix
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) cw[j][i] = bw[j][i];
+            zz[j] = zero_pair(bz[j]);
+            ss[j] = bok[j] ? scale_pair(uint16_t(bs[j])) : 0u;
         }
-        // ---- 4 k-steps of 32: dequantize block s of every chunk, then MFMA
+        // next stage's copies go out now (past the last stage they reread
+        // in-range data into the idle buffer)
+        issue_a((st + 1) & 1, (st + 1) * BK);
+        issue_b((st + 1) * BK);
+
+        const uint8_t* Ab = As[st & 1];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            h8 af[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM + i * 16 + li;
+                const int u = (4 * lg + s) ^ (row & 15);
+                af[i] = *reinterpret_cast<const h8*>(Ab + row * ROW_BYTES + u * 16);
+            }
             h8 bf[TN];
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                uint32_t f[4];
+                uint32_t hq[4], f[4];
+                decode_block_nat<BITS>(cw[j], s, hq);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) f[i] = as_u32(dequant_pair(h[j][4 * s + i], zz[j], ss[j]));
+                for (int i = 0; i < 4; ++i) f[i] = as_u32(dequant_pair(hq[i], zz[j], ss[j]));
                 const u4 fv = {f[0], f[1], f[2], f[3]};
                 bf[j] = __builtin_bit_cast(h8, fv);
             }
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WM + i * 16 + li;
-                const h8 a = *reinterpret_cast<const h8*>(Ab + row * LDA + 32 * lg + 8 * s);
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[j], acc[i][j], 0, 0, 0);
-            }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
     }
 
@@ -219,14 +218,15 @@ __global__ void __launch_bounds__(256) gather_act_kernel(const uint16_t* __restr
 template <int BITS, int BM, int BN, int WAVES_M>
 wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
-    const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+    const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
+    const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros)
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, true>), grid, dim3(256), 0, s, x, packed, scales, zeros,
-                           y, M, N, K, gs, gd);
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, true>), dim3(tiles), dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gd, m_tiles, tiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, false>), grid, dim3(256), 0, s, x, packed, scales,
-                           zeros, y, M, N, K, gs, gd);
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, false>), dim3(tiles), dim3(256), 0, s, x, packed,
+                           scales, zeros, y, M, N, K, gd, m_tiles, tiles);
     return wqh::launch_status();
 }
 
