@@ -61,7 +61,12 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles, int parts) {
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
-template <int BITS, int BM, int BN, int WAVES_M, bool HAS_Z>
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+
+
+template <int BITS, int BM, int BN, int WAVES_M, int NST, bool HAS_Z>
 __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ x,
                                                    const uint32_t* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
@@ -74,8 +79,11 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     constexpr int ROW_BYTES = BK * 2;          // 16 units of 16 bytes
     constexpr int A_INSTR = BM / 16;           // 1 KB copies per wavefront per stage
     static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1, "tile shape");
+    static_assert(NST >= 2 && (NST - 2) * A_INSTR < 64, "pipeline depth");
 
-    __shared__ __attribute__((aligned(1024))) uint8_t As[2][BM * ROW_BYTES];
+    // NST activation buffers: stage s lives in buffer s % NST and its copy is
+    // issued NST - 1 stages ahead.
+    __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * ROW_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -108,10 +116,14 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     };
 
     // ---- B: raw packed chunk, zero byte and scale bits of each of the TN
-    // columns this lane feeds (zero scale outside the matrix)
-    uint32_t bw[TN][BITS], bz[TN], bs[TN];
-    bool bok[TN];
-    auto issue_b = [&](int k0) {
+    // columns this lane feeds (zero scale outside the matrix).  Two register
+    // sets alternate between stages, so the next stage's loads never land in
+    // registers the current stage still reads.
+    struct BRegs {
+        uint32_t w[TN][BITS], z[TN], s[TN];
+        bool ok[TN];
+    };
+    auto issue_b = [&](BRegs& b, int k0) {
         const int cg = k0 / 32 + lg;
         const bool kval = cg < chunks;
         const int cgc = kval ? cg : 0;
@@ -121,13 +133,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
             const int n = n_lane0 + j * 16;
             const bool ok = kval && n < N;
             const size_t nn = ok ? size_t(n) : 0;
-            bok[j] = ok;
-            load_chunk_b<BITS>(packed + nn * row_words + (size_t)cgc * BITS, bw[j]);
-            bs[j] = scales[nn * G + g];
+            b.ok[j] = ok;
+            load_chunk_b<BITS>(packed + nn * row_words + (size_t)cgc * BITS, b.w[j]);
+            b.s[j] = scales[nn * G + g];
             if constexpr (HAS_Z)
-                bz[j] = zeros[nn * G + g];
+                b.z[j] = zeros[nn * G + g];
             else
-                bz[j] = 1u << (BITS - 1);
+                b.z[j] = 1u << (BITS - 1);
         }
     };
 
@@ -137,29 +149,28 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    issue_a(0, 0);
-    issue_b(0);
-
-    for (int st = 0; st < stages; ++st) {
-        // every copy of stage st (all wavefronts) has landed, and every
-        // wavefront is done reading the buffer the next copy overwrites
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // Copies are issued in the order B(s + 1), A(s + NST - 1) at the top of
+    // stage s, so when stage s + 1 starts, everything it needs was issued
+    // before the last NST - 2 activation copies: waiting until at most that
+    // many are outstanding covers exactly stage s + 1's data.
+    // One stage: wait for its data, start the next copies, multiply.
+    auto stage = [&](int st, const BRegs& cur, BRegs& nxt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * A_INSTR));
         __syncthreads();
+        // next copies (past the last stage they reread in-range data into a
+        // buffer that is not read again)
+        issue_b(nxt, (st + 1) * BK);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a((st + NST - 1) % NST, (st + NST - 1) * BK);
+        __builtin_amdgcn_sched_barrier(0);
 
-        uint32_t cw[TN][BITS], zz[TN], ss[TN];
+        uint32_t zz[TN], ss[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int i = 0; i < BITS; ++i) cw[j][i] = bw[j][i];
-            zz[j] = zero_pair(bz[j]);
-            ss[j] = bok[j] ? scale_pair(uint16_t(bs[j])) : 0u;
+            zz[j] = zero_pair(cur.z[j]);
+            ss[j] = cur.ok[j] ? scale_pair(uint16_t(cur.s[j])) : 0u;
         }
-        // next stage's copies go out now (past the last stage they reread
-        // in-range data into the idle buffer)
-        issue_a((st + 1) & 1, (st + 1) * BK);
-        issue_b((st + 1) * BK);
-
-        const uint8_t* Ab = As[st & 1];
+        const uint8_t* Ab = As[st % NST];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             h8 af[TM];
@@ -173,7 +184,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 uint32_t hq[4], f[4];
-                decode_block_nat<BITS>(cw[j], s, hq);
+                decode_block_nat<BITS>(cur.w[j], s, hq);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) f[i] = as_u32(dequant_pair(hq[i], zz[j], ss[j]));
                 const u4 fv = {f[0], f[1], f[2], f[3]};
@@ -185,7 +196,27 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
+    };
+
+    // Copies are issued in the order B(s + 1), A(s + NST - 1) at the top of
+    // stage s, so when stage s + 1 starts, everything it needs was issued
+    // before the last NST - 2 activation copies: waiting until at most that
+    // many are outstanding covers exactly stage s + 1's data.  The first
+    // copies are waited for in full.
+    BRegs b0, b1;
+    issue_b(b0, 0);
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) issue_a(p, p * BK);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    int st = 0;
+    for (; st + 1 < stages; st += 2) {
+        stage(st, b0, b1);
+        stage(st + 1, b1, b0);
     }
+    if (st < stages) stage(st, b0, b1);
+
+    // no copy may still be writing this block's LDS when it exits
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     // ---- epilogue: lane holds rows 4*lg + r of column li of each 16x16 tile
 #pragma unroll
@@ -215,28 +246,31 @@ __global__ void __launch_bounds__(256) gather_act_kernel(const uint16_t* __restr
     }
 }
 
-template <int BITS, int BM, int BN, int WAVES_M>
+template <int BITS, int BM, int BN, int WAVES_M, int NST>
 wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros)
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, true>), dim3(tiles), dim3(256), 0, s, x, packed, scales,
-                           zeros, y, M, N, K, gd, m_tiles, tiles);
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true>), dim3(tiles), dim3(256), 0, s, x, packed,
+                           scales, zeros, y, M, N, K, gd, m_tiles, tiles);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, false>), dim3(tiles), dim3(256), 0, s, x, packed,
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false>), dim3(tiles), dim3(256), 0, s, x, packed,
                            scales, zeros, y, M, N, K, gd, m_tiles, tiles);
     return wqh::launch_status();
 }
 
+// Small M: narrow tiles for more blocks.  Large M: 128 x 256 tiles with the
+// four wavefronts side by side along N, so every packed weight column is
+// dequantized by one wavefront and each activation row is re-read from L2
+// once per 256 output columns.
 template <int BITS>
 wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
-    if (M <= 32) return launch_tile<BITS, 32, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    if (M <= 64) return launch_tile<BITS, 64, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    if (M <= 128) return launch_tile<BITS, 128, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    return launch_tile<BITS, 256, 128, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (M <= 32) return launch_tile<BITS, 32, 128, 2, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (M <= 64) return launch_tile<BITS, 64, 128, 2, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
 }
 
 }  // namespace
