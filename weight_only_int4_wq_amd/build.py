@@ -22,6 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libwq.so")
 ARCH = "gfx950"
+COMPILE_TIMEOUT_S = 600
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -46,7 +47,10 @@ def _hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
+    except subprocess.TimeoutExpired:
+        raise RuntimeError(f"hipcc took more than {COMPILE_TIMEOUT_S} s on {src}")
     # hipcc's host pass does not know the packed-fp32 feature name; drop that note
     noise = "'-packed-fp32-ops' is not a recognized feature"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

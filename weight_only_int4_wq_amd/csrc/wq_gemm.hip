@@ -171,16 +171,18 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
             ss[j] = cur.ok[j] ? scale_pair(uint16_t(cur.s[j])) : 0u;
         }
         const uint8_t* Ab = As[st % NST];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            h8 af[TM];
+        // Software pipeline over the 4 k-steps: the A fragments (LDS reads)
+        // and B fragments (decode + dequantize) of step s + 1 are produced
+        // while step s's MFMAs run.
+        auto load_a = [&](int s, h8 (&af)[TM]) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = wm * WM + i * 16 + li;
                 const int u = (4 * lg + s) ^ (row & 15);
                 af[i] = *reinterpret_cast<const h8*>(Ab + row * ROW_BYTES + u * 16);
             }
-            h8 bf[TN];
+        };
+        auto make_b = [&](int s, h8 (&bf)[TN]) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 uint32_t hq[4], f[4];
@@ -190,11 +192,22 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
                 const u4 fv = {f[0], f[1], f[2], f[3]};
                 bf[j] = __builtin_bit_cast(h8, fv);
             }
+        };
+        h8 af[2][TM], bf[2][TN];
+        load_a(0, af[0]);
+        make_b(0, bf[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int c = s & 1;
+            if (s < 3) {
+                load_a(s + 1, af[c ^ 1]);
+                make_b(s + 1, bf[c ^ 1]);
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
         }
     };
 
