@@ -22,9 +22,9 @@
 //    fragments: the dequantized tile lives in registers rather than LDS.
 //    Lane group g (lanes 16g..16g+15) takes chunk g of the stage, and the A
 //    fragments are read with the same k mapping, so the k sum is unchanged.
-//  - Tiles are numbered with M fastest and dealt to the XCDs in contiguous
-//    ranges, so the blocks sharing a column of packed weights run on the
-//    same XCD and share its L2.
+//  - Tiles are dealt to the XCDs in contiguous ranges and ordered in strips
+//    of 4 M-tiles, so the blocks resident on one XCD cover a compact
+//    rectangle of the output and reuse activations and weights from its L2.
 #include "wq_common.h"
 
 namespace {
@@ -63,6 +63,22 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles, int parts) {
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+// vmcnt(n) and lgkmcnt(0).
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
+
+// Workgroup barrier for the copy pipeline: this wavefront's LDS reads are
+// done (lgkmcnt(0)) and all but the newest n vector-memory operations -
+// among them its global->LDS copies - have landed, then s_barrier.
+// __syncthreads() would also order every outstanding LDS write, i.e. drain
+// the copies that are meant to stay in flight.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void copy_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(N));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 
 
@@ -71,7 +87,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
                                                    const uint32_t* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, uint16_t* __restrict__ y,
-                                                   int M, int N, int K, GroupDiv gd, int m_tiles, int tiles) {
+                                                   int M, int N, int K, GroupDiv gd, int m_tiles, int n_tiles,
+                                                   int tiles) {
+    constexpr int GM = 4;  // M-tiles per strip of the tile order
     constexpr int WAVES_N = 4 / WAVES_M;
     constexpr int BK = 128;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -81,15 +99,34 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1, "tile shape");
     static_assert(NST >= 2 && (NST - 2) * A_INSTR < 64, "pipeline depth");
 
-    // NST activation buffers: stage s lives in buffer s % NST and its copy is
-    // issued NST - 1 stages ahead.
-    __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * ROW_BYTES];
+    // Three activation buffers (separate LDS objects, indexed at compile
+    // time, so the compiler can tell a copy into one from reads of another):
+    // stage s lives in buffer s % 3 and its copy is issued 2 stages ahead.
+    static_assert(NST == 3, "three activation buffers");
+    __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * ROW_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t As1[BM * ROW_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t As2[BM * ROW_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int li = lane & 15, lg = lane >> 4;
-    const int tile = xcd_tile(blockIdx.x, tiles, 8);
-    const int m0 = (tile % m_tiles) * BM, n0 = (tile / m_tiles) * BN;
+    // Blocks run on XCD (block id mod 8); xcd_tile gives each XCD a
+    // contiguous range of tile numbers, and the grouped order below turns a
+    // run of consecutive numbers into a GM-tall strip of tiles (GM M-tiles
+    // by several N-tiles), so the blocks resident on one XCD at a time reuse
+    // both their activation rows and their weight columns from its L2.
+    int m_t, n_t;
+    {
+        const int t = xcd_tile(blockIdx.x, tiles, 8);
+        const int per_group = GM * n_tiles;
+        const int group = t / per_group;
+        const int first_m = group * GM;
+        const int gsm = min(m_tiles - first_m, GM);
+        const int r = t - group * per_group;
+        m_t = first_m + r % gsm;
+        n_t = r / gsm;
+    }
+    const int m0 = m_t * BM, n0 = n_t * BN;
     const int chunks = K / 32;
     const int G = chunk_group(chunks - 1, gd) + 1;
     const size_t row_words = (size_t)chunks * BITS;
@@ -102,7 +139,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     // which holds logical unit (l % 16) ^ (row % 16).  Rows past M and
     // columns past K read valid in-range data instead (their products only
     // reach output rows that are not stored, or meet zero weights).
-    auto issue_a = [&](int buf, int k0) {
+    auto issue_a = [&](uint8_t* buf, int k0) {
 #pragma unroll
         for (int i = 0; i < A_INSTR; ++i) {
             const int unit0 = (wave * A_INSTR + i) * 64;
@@ -111,7 +148,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
             const int gm = min(m0 + row, M - 1);
             const int gk = k0 + 8 * u;
             const uint16_t* src = x + (size_t)gm * K + (gk < K ? gk : 0);
-            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&As[buf][unit0 * 16]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(buf + unit0 * 16), 16, 0, 0);
         }
     };
 
@@ -154,14 +191,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     // before the last NST - 2 activation copies: waiting until at most that
     // many are outstanding covers exactly stage s + 1's data.
     // One stage: wait for its data, start the next copies, multiply.
-    auto stage = [&](int st, const BRegs& cur, BRegs& nxt) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * A_INSTR));
-        __syncthreads();
+    auto stage = [&](int st, const BRegs& cur, BRegs& nxt, uint8_t* Ab, uint8_t* An) {
+        copy_barrier<(NST - 2) * A_INSTR>();
         // next copies (past the last stage they reread in-range data into a
         // buffer that is not read again)
         issue_b(nxt, (st + 1) * BK);
         __builtin_amdgcn_sched_barrier(0);
-        issue_a((st + NST - 1) % NST, (st + NST - 1) * BK);
+        issue_a(An, (st + NST - 1) * BK);
         __builtin_amdgcn_sched_barrier(0);
 
         uint32_t zz[TN], ss[TN];
@@ -170,7 +206,6 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
             zz[j] = zero_pair(cur.z[j]);
             ss[j] = cur.ok[j] ? scale_pair(uint16_t(cur.s[j])) : 0u;
         }
-        const uint8_t* Ab = As[st % NST];
         // Software pipeline over the 4 k-steps: the A fragments (LDS reads)
         // and B fragments (decode + dequantize) of step s + 1 are produced
         // while step s's MFMAs run.
@@ -218,15 +253,25 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     // copies are waited for in full.
     BRegs b0, b1;
     issue_b(b0, 0);
-#pragma unroll
-    for (int p = 0; p < NST - 1; ++p) issue_a(p, p * BK);
+    issue_a(As0, 0);
+    issue_a(As1, BK);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // Unrolled by 6 = lcm(3 buffers, 2 weight register sets), so both are
+    // addressed at compile time.
     int st = 0;
-    for (; st + 1 < stages; st += 2) {
-        stage(st, b0, b1);
-        stage(st + 1, b1, b0);
+    for (; st + 6 <= stages; st += 6) {
+        stage(st, b0, b1, As0, As2);
+        stage(st + 1, b1, b0, As1, As0);
+        stage(st + 2, b0, b1, As2, As1);
+        stage(st + 3, b1, b0, As0, As2);
+        stage(st + 4, b0, b1, As1, As0);
+        stage(st + 5, b1, b0, As2, As1);
     }
-    if (st < stages) stage(st, b0, b1);
+    if (st < stages) stage(st, b0, b1, As0, As2);
+    if (st + 1 < stages) stage(st + 1, b1, b0, As1, As0);
+    if (st + 2 < stages) stage(st + 2, b0, b1, As2, As1);
+    if (st + 3 < stages) stage(st + 3, b1, b0, As0, As2);
+    if (st + 4 < stages) stage(st + 4, b0, b1, As1, As0);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -267,10 +312,10 @@ wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t*
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros)
         hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true>), dim3(tiles), dim3(256), 0, s, x, packed,
-                           scales, zeros, y, M, N, K, gd, m_tiles, tiles);
+                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles);
     else
         hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false>), dim3(tiles), dim3(256), 0, s, x, packed,
-                           scales, zeros, y, M, N, K, gd, m_tiles, tiles);
+                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles);
     return wqh::launch_status();
 }
 
@@ -281,8 +326,8 @@ wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t*
 template <int BITS>
 wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
-    if (M <= 32) return launch_tile<BITS, 32, 128, 2, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    if (M <= 64) return launch_tile<BITS, 64, 128, 2, 2>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (M <= 32) return launch_tile<BITS, 32, 128, 2, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (M <= 64) return launch_tile<BITS, 64, 128, 2, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
     return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
 }
 
