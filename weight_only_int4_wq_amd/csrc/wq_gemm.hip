@@ -186,18 +186,19 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // Copies are issued in the order B(s + 1), A(s + NST - 1) at the top of
-    // stage s, so when stage s + 1 starts, everything it needs was issued
-    // before the last NST - 2 activation copies: waiting until at most that
-    // many are outstanding covers exactly stage s + 1's data.
-    // One stage: wait for its data, start the next copies, multiply.
+    // Per-lane vector-memory instructions of one issue_b (at least: a
+    // 3-bit chunk may be fetched by one dwordx3 load).
+    constexpr int B_OPS = TN * ((BITS == 8 ? 2 : 1) + 1 + (HAS_Z ? 1 : 0));
+
+    // One stage: wait for its data, start the copies two stages ahead,
+    // multiply.  Stage s's weights and activations were issued at the top of
+    // stage s - 2 (in that order), so only the copies issued at the top of
+    // stage s - 1 may still be outstanding.
     auto stage = [&](int st, const BRegs& cur, BRegs& nxt, uint8_t* Ab, uint8_t* An) {
-        copy_barrier<(NST - 2) * A_INSTR>();
-        // next copies (past the last stage they reread in-range data into a
-        // buffer that is not read again)
-        issue_b(nxt, (st + 1) * BK);
+        copy_barrier<B_OPS + A_INSTR>();
+        issue_b(nxt, (st + 2) * BK);
         __builtin_amdgcn_sched_barrier(0);
-        issue_a(An, (st + NST - 1) * BK);
+        issue_a(An, (st + 2) * BK);
         __builtin_amdgcn_sched_barrier(0);
 
         uint32_t zz[TN], ss[TN];
@@ -246,32 +247,27 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
         }
     };
 
-    // Copies are issued in the order B(s + 1), A(s + NST - 1) at the top of
-    // stage s, so when stage s + 1 starts, everything it needs was issued
-    // before the last NST - 2 activation copies: waiting until at most that
-    // many are outstanding covers exactly stage s + 1's data.  The first
-    // copies are waited for in full.
-    BRegs b0, b1;
+    // Stage s uses weight register set s % 3 and activation buffer s % 3
+    // (both addressed at compile time: the loop is unrolled by 3).  The
+    // prologue issues stages 0 and 1; past the last stage the copies reread
+    // in-range data into buffers that are not read again.
+    BRegs b0, b1, b2;
     issue_b(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     issue_a(As0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(b1, BK);
+    __builtin_amdgcn_sched_barrier(0);
     issue_a(As1, BK);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // Unrolled by 6 = lcm(3 buffers, 2 weight register sets), so both are
-    // addressed at compile time.
+    __builtin_amdgcn_sched_barrier(0);
     int st = 0;
-    for (; st + 6 <= stages; st += 6) {
-        stage(st, b0, b1, As0, As2);
+    for (; st + 3 <= stages; st += 3) {
+        stage(st, b0, b2, As0, As2);
         stage(st + 1, b1, b0, As1, As0);
-        stage(st + 2, b0, b1, As2, As1);
-        stage(st + 3, b1, b0, As0, As2);
-        stage(st + 4, b0, b1, As1, As0);
-        stage(st + 5, b1, b0, As2, As1);
+        stage(st + 2, b2, b1, As2, As1);
     }
-    if (st < stages) stage(st, b0, b1, As0, As2);
+    if (st < stages) stage(st, b0, b2, As0, As2);
     if (st + 1 < stages) stage(st + 1, b1, b0, As1, As0);
-    if (st + 2 < stages) stage(st + 2, b0, b1, As2, As1);
-    if (st + 3 < stages) stage(st + 3, b1, b0, As0, As2);
-    if (st + 4 < stages) stage(st + 4, b0, b1, As1, As0);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
