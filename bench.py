@@ -67,8 +67,12 @@ def layer_bytes(M, K, N, bits=BITS, group=GROUP):
 
 
 def src_sha(name):
-    with open(os.path.join(ROOT, "weight_only_int4_wq_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source together with the shared device header."""
+    h = hashlib.sha256()
+    for part in (name, "wq_common.h"):
+        with open(os.path.join(ROOT, "weight_only_int4_wq_amd", "csrc", part), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel_src, key):
@@ -337,7 +341,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
-            "kernel": "gemv_kernel<4,1,4>", "avg_launch_us": round(launch_us, 3),
+            "kernel": "gemv_stream_kernel (4-bit, M=1; R=1 for N<8192, R=2 otherwise)", "avg_launch_us": round(launch_us, 3),
             "bytes_per_launch": dec["all_b"] / dec["n_launch"],
         },
         "gemm": {
@@ -350,7 +354,7 @@ def main():
             "roofline": {
                 "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": gtr,
-                "kernel": "gemm_kernel<4,128,128,2>", "avg_launch_us": round(pre["ms_gemm"] * 1e3, 3),
+                "kernel": "gemm_kernel<4,128,256,1,3>", "avg_launch_us": round(pre["ms_gemm"] * 1e3, 3),
                 "flops_per_launch": flops,
             },
         },
