@@ -25,62 +25,11 @@
 //  - Tiles are dealt to the XCDs in contiguous ranges and ordered in strips
 //    of 4 M-tiles, so the blocks resident on one XCD cover a compact
 //    rectangle of the output and reuse activations and weights from its L2.
-#include "wq_common.h"
+#include "wq_gemm_common.h"
 
 namespace {
 
 using namespace wq;
-
-template <int BITS>
-__device__ __forceinline__ void load_chunk_b(const uint32_t* p, uint32_t* w) {
-    if constexpr (BITS == 4) {
-        const u4 v = *reinterpret_cast<const u4*>(p);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else if constexpr (BITS == 8) {
-        const u4 a = reinterpret_cast<const u4*>(p)[0];
-        const u4 b = reinterpret_cast<const u4*>(p)[1];
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else if constexpr (BITS == 2) {
-        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-        const u2 v = *reinterpret_cast<const u2*>(p);
-        w[0] = v.x; w[1] = v.y;
-    } else {
-        w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
-    }
-}
-
-typedef __attribute__((address_space(1))) const void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-// Tile index of block b when blocks are dealt round-robin to `parts` XCDs:
-// XCD j gets the contiguous tile range [start_j, start_j + count_j).
-__device__ __forceinline__ int xcd_tile(int b, int tiles, int parts) {
-    const int q = tiles / parts, r = tiles % parts;
-    const int xcd = b % parts, k = b / parts;
-    return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
-}
-
-// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
-// vmcnt(n) and lgkmcnt(0).
-constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70; }
-
-// Workgroup barrier for the copy pipeline: this wavefront's LDS reads are
-// done (lgkmcnt(0)) and all but the newest n vector-memory operations -
-// among them its global->LDS copies - have landed, then s_barrier.
-// __syncthreads() would also order every outstanding LDS write, i.e. drain
-// the copies that are meant to stay in flight.  The empty asm statements
-// keep the compiler from moving memory accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void copy_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(N));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-
 
 template <int BITS, int BM, int BN, int WAVES_M, int NST, bool HAS_Z>
 __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ x,
@@ -110,22 +59,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int li = lane & 15, lg = lane >> 4;
-    // Blocks run on XCD (block id mod 8); xcd_tile gives each XCD a
-    // contiguous range of tile numbers, and the grouped order below turns a
-    // run of consecutive numbers into a GM-tall strip of tiles (GM M-tiles
-    // by several N-tiles), so the blocks resident on one XCD at a time reuse
-    // both their activation rows and their weight columns from its L2.
     int m_t, n_t;
-    {
-        const int t = xcd_tile(blockIdx.x, tiles, 8);
-        const int per_group = GM * n_tiles;
-        const int group = t / per_group;
-        const int first_m = group * GM;
-        const int gsm = min(m_tiles - first_m, GM);
-        const int r = t - group * per_group;
-        m_t = first_m + r % gsm;
-        n_t = r / gsm;
-    }
+    tile_coords<GM>(blockIdx.x, tiles, m_tiles, n_tiles, m_t, n_t);
     const int m0 = m_t * BM, n0 = n_t * BN;
     const int chunks = K / 32;
     const int G = chunk_group(chunks - 1, gd) + 1;
@@ -324,6 +259,7 @@ wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t*
                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     if (M <= 32) return launch_tile<BITS, 32, 128, 2, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
     if (M <= 64) return launch_tile<BITS, 64, 128, 2, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
+    if (wqh::gemm_large_fits(M, N, K, BITS)) return wqh::gemm_large(BITS, x, packed, scales, zeros, y, M, N, K, gs, s);
     return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
 }
 
