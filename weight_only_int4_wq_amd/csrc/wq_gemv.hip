@@ -279,6 +279,13 @@ __global__ void __launch_bounds__(256) gemv_slab_kernel(const uint16_t* __restri
 // fp32 (one fused multiply-add each).  This skips the per-weight fp16
 // subtract and multiply; the rounding differs from multiplying by fp16
 // dequantized weights by about 2^-12 relative per weight, averaged over K.
+// Wavefronts per block of the streaming kernel (the activations are staged
+// once per block).
+#ifndef WQ_GEMV_WPB
+#define WQ_GEMV_WPB 4
+#endif
+constexpr int kStreamWaves = WQ_GEMV_WPB;
+
 template <int BITS, int R, int CPL>
 struct WideSlot {
     uint32_t w[R][CPL][BITS];
@@ -286,8 +293,8 @@ struct WideSlot {
     bool ok[R];
 };
 
-template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z>
-__global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __restrict__ x,
+template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER>
+__global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const uint16_t* __restrict__ x,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
@@ -306,8 +313,8 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __rest
     const int n_groups = (N + R - 1) / R;
     const int J = (CNP + 63) / 64;  // slot iterations per row group
 
-    const int wg0 = blockIdx.x * 4 + wave;
-    const int wstride = gridDim.x * 4;
+    const int wg0 = blockIdx.x * kStreamWaves + wave;
+    const int wstride = gridDim.x * kStreamWaves;
     const int my_groups = wg0 < n_groups ? (n_groups - wg0 + wstride - 1) / wstride : 0;
     const int T = my_groups * J;  // flat (row group, slot iteration) count of this wave
 
@@ -340,43 +347,74 @@ __global__ void __launch_bounds__(256) gemv_stream_kernel(const uint16_t* __rest
         i_rg += wrap ? wstride : 0;
     };
 
-    // ---- weight loads of the first D iterations go out first, so their HBM
-    // latency overlaps the activation staging below
+    // ---- activation loads of the first staging pass go out before the
+    // weight loads: vector-memory loads complete in issue order, so loads
+    // issued after the weights could only be staged once every one of those
+    // weights had arrived.  Issued first, they arrive after one cache round
+    // trip and the staging overlaps the weights' HBM latency.
+    auto load_block = [&](int m, int c, int b) -> u4 {
+        const size_t xrow = (size_t)(m < M ? m : 0) * K;
+        u4 v;
+        if constexpr (GATHER) {
+            uint32_t el[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) el[i] = x[xrow + perm[32 * c + 8 * b + i]];
+            v.x = el[0] | (el[1] << 16); v.y = el[2] | (el[3] << 16);
+            v.z = el[4] | (el[5] << 16); v.w = el[6] | (el[7] << 16);
+        } else {
+            v = *reinterpret_cast<const u4*>(x + xrow + 32 * c + 8 * b);
+        }
+        return v;  // rows m >= M are zeroed when staged
+    };
+    auto stage_slot = [&](int m, int cp, const u4 (&v)[CPL][4]) {
+        float sum = 0.f;
+        const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+        for (int e = 0; e < CPL; ++e)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const u4 o = m < M ? stage_block(v[e][b]) : u4{0u, 0u, 0u, 0u};
+                xs[((m * 4 + b) * CPL + e) * CNP + cp] = o;
+                sum = __builtin_amdgcn_fdot2(as_h2(o.x), one, sum, false);
+                sum = __builtin_amdgcn_fdot2(as_h2(o.y), one, sum, false);
+                sum = __builtin_amdgcn_fdot2(as_h2(o.z), one, sum, false);
+                sum = __builtin_amdgcn_fdot2(as_h2(o.w), one, sum, false);
+            }
+        xsum[m * CNP + cp] = sum;
+    };
+    // First pass: slot threadIdx.x of every activation row, clamped to the
+    // last slot so that loads and stores are unconditional.
+    // A gather through perm needs the perm values first, so with act-order
+    // the weights still go out first.
+    const int cp0 = min(int(threadIdx.x), CNP - 1);
+    u4 xfirst[MT][CPL][4];
+    auto load_first = [&]() {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int e = 0; e < CPL; ++e)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) xfirst[m][e][b] = load_block(m, cp0 * CPL + e, b);
+    };
+    if constexpr (!GATHER) load_first();
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(slot[d], d);
+    // keep the staging arithmetic below every weight load (it would wait for
+    // the activations and hold back the loads scheduled after it)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GATHER) load_first();
 
     // ---- stage activations (pair order) and per-slot sums, once per block
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const size_t xrow = (size_t)(m < M ? m : 0) * K;
-        for (int cp = threadIdx.x; cp < CNP; cp += 256) {
-            float sum = 0.f;
+        stage_slot(m, cp0, xfirst[m]);  // threads past the last slot rewrite it with the same values
+        for (int cp = threadIdx.x + 64 * kStreamWaves; cp < CNP; cp += 64 * kStreamWaves) {
+            u4 v[CPL][4];
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                const int c = cp * CPL + e;
+            for (int e = 0; e < CPL; ++e)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    u4 v;
-                    if (perm) {
-                        uint32_t el[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) el[i] = x[xrow + perm[32 * c + 8 * b + i]];
-                        v.x = el[0] | (el[1] << 16); v.y = el[2] | (el[3] << 16);
-                        v.z = el[4] | (el[5] << 16); v.w = el[6] | (el[7] << 16);
-                    } else {
-                        v = *reinterpret_cast<const u4*>(x + xrow + 32 * c + 8 * b);
-                    }
-                    if (m >= M) v = u4{0u, 0u, 0u, 0u};
-                    const u4 o = stage_block(v);
-                    xs[((m * 4 + b) * CPL + e) * CNP + cp] = o;
-                    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-                    sum = __builtin_amdgcn_fdot2(as_h2(o.x), one, sum, false);
-                    sum = __builtin_amdgcn_fdot2(as_h2(o.y), one, sum, false);
-                    sum = __builtin_amdgcn_fdot2(as_h2(o.z), one, sum, false);
-                    sum = __builtin_amdgcn_fdot2(as_h2(o.w), one, sum, false);
-                }
-            }
-            xsum[m * CNP + cp] = sum;
+                for (int b = 0; b < 4; ++b) v[e][b] = load_block(m, cp * CPL + e, b);
+            stage_slot(m, cp, v);
         }
     }
 
@@ -517,16 +555,22 @@ wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
     const int n_groups = (N + R - 1) / R;
-    int blocks = (n_groups + 3) / 4;
+    int blocks = (n_groups + kStreamWaves - 1) / kStreamWaves;
     if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
     const size_t lds = stream_lds_bytes(MT, K, CPL);
     const GroupDiv gd = wqh::group_magic(gs);
-    if (zeros)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true>), dim3(blocks), dim3(256), lds, s, x,
+    if (zeros && perm)
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
                            packed, scales, zeros, perm, y, M, N, K, gd);
+    else if (zeros)
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+                           x, packed, scales, zeros, perm, y, M, N, K, gd);
+    else if (perm)
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+                           x, packed, scales, zeros, perm, y, M, N, K, gd);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false>), dim3(blocks), dim3(256), lds, s, x,
-                           packed, scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+                           x, packed, scales, zeros, perm, y, M, N, K, gd);
     return wqh::launch_status();
 }
 
