@@ -261,6 +261,34 @@ __global__ void __launch_bounds__(256) gemv_slab_kernel(const uint16_t* __restri
 }
 
 
+// Streaming-kernel decoder: the pair order of decode_chunk (pair i of a block
+// holds codes i and i + 4) with cheaper 4-bit extraction.  Codes sitting at
+// bits 4..7 of a 16-bit half are exposed where they are, under the exponent
+// 0x5400 (fp16 64, whose mantissa step at bit 4 is exactly 1), giving 64 + q;
+// codes at bits 0..3 get 0x6400 (1024 + q).  One shift by 8 brings the upper
+// two nibbles of each half down, so a word costs 1 shift + 4 and-or instead of
+// 3 + 4.  Pairs 0 and 2 of each block carry offset 1024, pairs 1 and 3 carry
+// kOddBase<BITS> (64 for 4-bit; other widths use decode_chunk throughout).
+template <int BITS>
+constexpr float kOddBase = BITS == 4 ? 64.f : 1024.f;
+
+template <int BITS>
+__device__ __forceinline__ void decode_chunk_split(const uint32_t* w, uint32_t* h) {
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t v = w[b], v8 = v >> 8;
+            h[4 * b + 0] = and_or(v, 0x000F000Fu, kMagic2);
+            h[4 * b + 1] = and_or(v, 0x00F000F0u, 0x54005400u);
+            h[4 * b + 2] = and_or(v8, 0x000F000Fu, kMagic2);
+            h[4 * b + 3] = and_or(v8, 0x00F000F0u, 0x54005400u);
+        }
+    } else {
+        decode_chunk<BITS>(w, h);
+    }
+}
+
+
 // Streaming kernel (M <= 4 and the whole activation row fits in LDS).
 //
 // Persistent wavefronts: the grid is sized to the machine and wavefront w of
@@ -272,9 +300,11 @@ __global__ void __launch_bounds__(256) gemv_slab_kernel(const uint16_t* __restri
 // of each of the R rows; consecutive lanes read consecutive CPL * 16 bytes.
 //
 // Arithmetic per slot (CPL chunks of one group) and activation row m: with
-// h = 1024 + q (exact fp16 from the exponent trick), A = sum_k x_k * h_k
-// accumulated in fp32 by fp16-pair dot products, and X = sum_k x_k,
-//     sum_k x_k * (q_k - z) * s = s * (A - (1024 + z) * X)
+// h = B + q the exact fp16 integers of decode_chunk_split (B = 1024 on the
+// even pairs of a block, kOddBase on the odd ones), A = sum_k x_k * h_k
+// accumulated in fp32 by fp16-pair dot products, and Xe, Xo the sums of x
+// over the even and the odd pairs,
+//     sum_k x_k * (q_k - z) * s = s * (A - (1024 + z) * Xe - (kOddBase + z) * Xo)
 // exactly in real arithmetic; the kernel evaluates the right-hand side in
 // fp32 (one fused multiply-add each).  This skips the per-weight fp16
 // subtract and multiply; the rounding differs from multiplying by fp16
@@ -301,11 +331,12 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                                                           const int32_t* __restrict__ perm,
                                                           uint16_t* __restrict__ y, int M, int N, int K,
                                                           GroupDiv gd) {
-    // LDS: u4 xs[MT][4][CPL][CNP] (activation pairs), then float xsum[MT][CNP]
+    // LDS: u4 xs[MT][4][CPL][CNP] (activation pairs), then float2 xsum[MT][CNP]
+    // (per slot: sum of x over pairs 0 and 2 of every block, over pairs 1 and 3)
     extern __shared__ u4 xs[];
     const int CN = K / 32;       // chunks per row
     const int CNP = CN / CPL;    // slots per row
-    float* xsum = reinterpret_cast<float*>(xs + MT * 4 * CN);
+    float2* xsum = reinterpret_cast<float2*>(xs + MT * 4 * CN);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int G = chunk_group(CN - 1, gd) + 1;
@@ -367,7 +398,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         return v;  // rows m >= M are zeroed when staged
     };
     auto stage_slot = [&](int m, int cp, const u4 (&v)[CPL][4]) {
-        float sum = 0.f;
+        float se = 0.f, so = 0.f;
         const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int e = 0; e < CPL; ++e)
@@ -375,12 +406,12 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
             for (int b = 0; b < 4; ++b) {
                 const u4 o = m < M ? stage_block(v[e][b]) : u4{0u, 0u, 0u, 0u};
                 xs[((m * 4 + b) * CPL + e) * CNP + cp] = o;
-                sum = __builtin_amdgcn_fdot2(as_h2(o.x), one, sum, false);
-                sum = __builtin_amdgcn_fdot2(as_h2(o.y), one, sum, false);
-                sum = __builtin_amdgcn_fdot2(as_h2(o.z), one, sum, false);
-                sum = __builtin_amdgcn_fdot2(as_h2(o.w), one, sum, false);
+                se = __builtin_amdgcn_fdot2(as_h2(o.x), one, se, false);
+                so = __builtin_amdgcn_fdot2(as_h2(o.y), one, so, false);
+                se = __builtin_amdgcn_fdot2(as_h2(o.z), one, se, false);
+                so = __builtin_amdgcn_fdot2(as_h2(o.w), one, so, false);
             }
-        xsum[m * CNP + cp] = sum;
+        xsum[m * CNP + cp] = make_float2(se, so);
     };
     // First pass: slot threadIdx.x of every activation row, clamped to the
     // last slot so that loads and stores are unconditional.
@@ -433,7 +464,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
             // ---- compute iteration t from slot d
             {
                 const int cp = min(lane + 64 * c_j, CNP - 1);
-                float X[MT];
+                float2 X[MT];
 #pragma unroll
                 for (int m = 0; m < MT; ++m) X[m] = xsum[m * CNP + cp];
                 float a[R][MT];
@@ -455,7 +486,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         uint32_t h[16];
-                        decode_chunk<BITS>(slot[d].w[r][e], h);
+                        decode_chunk_split<BITS>(slot[d].w[r][e], h);
 #pragma unroll
                         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -467,10 +498,13 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                 for (int r = 0; r < R; ++r) {
                     const float sf =
                         slot[d].ok[r] ? float(__builtin_bit_cast(_Float16, uint16_t(slot[d].s[r]))) : 0.f;
-                    const float zf = float(1024u + slot[d].z[r]);
+                    const float zf = float(slot[d].z[r]);
 #pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        acc[r][m] = __builtin_fmaf(sf, __builtin_fmaf(-zf, X[m], a[r][m]), acc[r][m]);
+                    for (int m = 0; m < MT; ++m) {
+                        float t = __builtin_fmaf(-(1024.f + zf), X[m].x, a[r][m]);
+                        t = __builtin_fmaf(-(kOddBase<BITS> + zf), X[m].y, t);
+                        acc[r][m] = __builtin_fmaf(sf, t, acc[r][m]);
+                    }
                 }
             }
             // ---- end of a row group: reduce across the wavefront and store
@@ -521,7 +555,7 @@ wq_status launch_cfg(const uint16_t* x, const uint32_t* packed, const uint16_t* 
 // LDS bytes the streaming kernel stages: fp16 activations plus one fp32 sum
 // per slot, per activation row.
 inline size_t stream_lds_bytes(int MT, int K, int cpl) {
-    return size_t(MT) * (size_t(K) * 2 + size_t(K / (32 * cpl)) * 4);
+    return size_t(MT) * (size_t(K) * 2 + size_t(K / (32 * cpl)) * 8);
 }
 
 // Launch shape of the streaming kernel (blocks per CU; rows per wavefront
