@@ -60,6 +60,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Sum over the 64 lanes of a wavefront, valid in lane 63 only: DPP steps
+// within each row of 16 lanes (quad permutes, half-row and row mirrors) leave
+// the row sum in every lane of the row, then row broadcasts add row 0 into
+// row 1, row 2 into row 3, and rows 0+1 into rows 2 and 3.  Six instructions,
+// fixed order (deterministic).
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    return v;
+}
+
 // Per-row pointers of the R output columns a wavefront owns.
 template <int BITS, int R>
 struct Rows {
@@ -338,7 +353,9 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int CNP = CN / CPL;    // slots per row
     float2* xsum = reinterpret_cast<float2*>(xs + MT * 4 * CN);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform (readfirstlane): row-group positions and row addresses
+    // live in scalar registers, lanes only add their chunk offset
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int G = chunk_group(CN - 1, gd) + 1;
     const size_t row_words = (size_t)CN * BITS;
     const int n_groups = (N + R - 1) / R;
@@ -354,22 +371,24 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
 
     WideSlot<BITS, R, CPL> slot[D];
     auto issue = [&](WideSlot<BITS, R, CPL>& sl, int t) {
+        const bool tv = t < T;  // wave-uniform
         const int cp = lane + 64 * i_j;
-        const bool valid = (t < T) && cp < CNP;
+        const bool valid = tv && cp < CNP;
         const int cpc = valid ? cp : 0;
         const int g = chunk_group(cpc * CPL, gd);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = i_rg * R + r;
-            const bool ok = valid && n < N;
-            const size_t nn = ok ? size_t(n) : 0;
-            sl.ok[r] = ok;
-            const uint32_t* src = packed + nn * row_words + (size_t)cpc * CPL * BITS;
+            const bool nok = tv && n < N;  // wave-uniform
+            const int nn = nok ? n : 0;
+            sl.ok[r] = valid && nok;
+            const uint32_t* rowp = packed + (size_t)nn * row_words;
+            const uint32_t* src = rowp + cpc * (CPL * BITS);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) load_chunk<BITS>(src + e * BITS, sl.w[r][e]);
-            sl.s[r] = scales[nn * G + g];
+            sl.s[r] = (scales + (size_t)nn * G)[g];
             if constexpr (HAS_Z)
-                sl.z[r] = zeros[nn * G + g];
+                sl.z[r] = (zeros + (size_t)nn * G)[g];
             else
                 sl.z[r] = 1u << (BITS - 1);
         }
@@ -514,9 +533,9 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                     const int n = c_rg * R + r;
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        const float v = wave_sum(acc[r][m]);
+                        const float v = wave_sum_last(acc[r][m]);
                         acc[r][m] = 0.f;
-                        if (lane == 0 && n < N && m < M)
+                        if (lane == 63 && n < N && m < M)
                             y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
                     }
                 }
