@@ -432,33 +432,47 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
             }
         xsum[m * CNP + cp] = make_float2(se, so);
     };
-    // First pass: slot threadIdx.x of every activation row, clamped to the
-    // last slot so that loads and stores are unconditional.
-    // A gather through perm needs the perm values first, so with act-order
-    // the weights still go out first.
-    const int cp0 = min(int(threadIdx.x), CNP - 1);
-    u4 xfirst[MT][CPL][4];
-    auto load_first = [&]() {
+    // The first PRE passes (slot threadIdx.x + p * NT of every activation
+    // row) are loaded up front, clamped to the last slot so that loads and
+    // stores are unconditional; a pass that starts past the last slot is
+    // skipped.  A gather through perm needs the perm values first, so with
+    // act-order the weights still go out first.
+    constexpr int NT = 64 * kStreamWaves;
+    constexpr int PRE = (MT == 1 && !GATHER) ? 2 : 1;
+    u4 xpre[PRE][MT][CPL][4];
+    auto load_pre = [&]() {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int p = 0; p < PRE; ++p) {
+            if (p > 0 && p * NT >= CNP) break;  // wave-uniform
+            const int cp = min(int(threadIdx.x) + p * NT, CNP - 1);
 #pragma unroll
-            for (int e = 0; e < CPL; ++e)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) xfirst[m][e][b] = load_block(m, cp0 * CPL + e, b);
+                for (int e = 0; e < CPL; ++e)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) xpre[p][m][e][b] = load_block(m, cp * CPL + e, b);
+        }
     };
-    if constexpr (!GATHER) load_first();
+    if constexpr (!GATHER) load_pre();
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(slot[d], d);
     // keep the staging arithmetic below every weight load (it would wait for
     // the activations and hold back the loads scheduled after it)
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (GATHER) load_first();
+    if constexpr (GATHER) load_pre();
 
-    // ---- stage activations (pair order) and per-slot sums, once per block
+    // ---- stage activations (pair order) and per-slot sums, once per block;
+    // threads past the last slot rewrite it with the same values
+#pragma unroll
+    for (int p = 0; p < PRE; ++p) {
+        if (p > 0 && p * NT >= CNP) break;
+        const int cp = min(int(threadIdx.x) + p * NT, CNP - 1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) stage_slot(m, cp, xpre[p][m]);
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        stage_slot(m, cp0, xfirst[m]);  // threads past the last slot rewrite it with the same values
-        for (int cp = threadIdx.x + 64 * kStreamWaves; cp < CNP; cp += 64 * kStreamWaves) {
+        for (int cp = threadIdx.x + PRE * NT; cp < CNP; cp += NT) {
             u4 v[CPL][4];
 #pragma unroll
             for (int e = 0; e < CPL; ++e)
@@ -580,13 +594,13 @@ inline size_t stream_lds_bytes(int MT, int K, int cpl) {
 // Launch shape of the streaming kernel (blocks per CU; rows per wavefront
 // and pipeline depth for layers narrower / wider than 8192 columns).
 #ifndef WQ_GEMV_BPC
-#define WQ_GEMV_BPC 2
+#define WQ_GEMV_BPC 3
 #endif
 #ifndef WQ_GEMV_NARROW_R
-#define WQ_GEMV_NARROW_R 1
+#define WQ_GEMV_NARROW_R 2
 #endif
 #ifndef WQ_GEMV_NARROW_D
-#define WQ_GEMV_NARROW_D 4
+#define WQ_GEMV_NARROW_D 2
 #endif
 #ifndef WQ_GEMV_WIDE_R
 #define WQ_GEMV_WIDE_R 2
