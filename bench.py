@@ -66,24 +66,31 @@ def layer_bytes(M, K, N, bits=BITS, group=GROUP):
     return packed, packed + meta + act
 
 
-def src_sha(name):
-    """Hash of a kernel source together with the shared device header."""
+# Device sources each timed kernel is built from (kernel file + shared headers).
+GEMV_SOURCES = ("wq_gemv.hip", "wq_common.h")
+GEMM_SOURCES = ("wq_gemm_large.hip", "wq_gemm_common.h", "wq_common.h")
+GEMV_KERNEL = "gemv_stream_kernel<4,1,2,2,1,true,false>"
+GEMM_KERNEL = "gemm_large_kernel<4,true,true>"
+
+
+def src_sha(parts):
+    """Hash of the device sources a kernel is compiled from."""
     h = hashlib.sha256()
-    for part in (name, "wq_common.h"):
+    for part in parts:
         with open(os.path.join(ROOT, "weight_only_int4_wq_amd", "csrc", part), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src, key):
+def traffic_from_profile(parts, key):
     """HBM bytes per launch measured by rocprofv3 counters, if the committed
-    summary was taken on the current kernel source; else None."""
+    summary was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             data = json.load(f)
         entry = data[key]
-        if entry.get("kernel_source_sha") != src_sha(kernel_src):
+        if entry.get("kernel_source_sha") != src_sha(parts):
             return None
         return entry.get("hbm_bytes_per_launch")
     except (OSError, KeyError, ValueError):
@@ -213,11 +220,31 @@ def prefill_leg(wq, torch, steps, warmup):
         p = pool[i]
         wq.scale_act(p["x"], s, out=p["xs"])
 
+    # Context: the vendor dense fp16 GEMM (torch.matmul -> hipBLASLt) at the
+    # same M, N, K with dense fp16 weights, timed eagerly (launch gaps are
+    # negligible at this size) over four distinct operand copies.
+    dense = [(torch.randn(M, K, dtype=torch.float16, device="cuda"),
+              torch.randn(N, K, dtype=torch.float16, device="cuda"),
+              torch.empty(M, N, dtype=torch.float16, device="cuda")) for _ in range(4)]
+    for i in range(8):
+        a, b, c = dense[i % 4]
+        torch.matmul(a, b.t(), out=c)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        a, b, c = dense[i % 4]
+        torch.matmul(a, b.t(), out=c)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_dense = ev0.elapsed_time(ev1) / steps
+    del dense
+
     ms_full = timed(torch, full, copies, steps, warmup)
     ms_gemm = timed(torch, gemm_only, copies, steps, warmup)
     ms_act = timed(torch, act_only, copies, steps, warmup)
     torch.cuda.synchronize()
-    return dict(ms_full=ms_full, ms_gemm=ms_gemm, ms_act=ms_act, copies=copies)
+    return dict(ms_full=ms_full, ms_gemm=ms_gemm, ms_act=ms_act, copies=copies, ms_dense=ms_dense)
 
 
 # -------------------------------------------------------- CPU baseline ----
@@ -303,13 +330,13 @@ def main():
     value = dec["packed_b"] / (ms * 1e-3) / 1e9
     launch_us = ms * 1e3 / dec["n_launch"]
     achieved = dec["all_b"] / dec["n_launch"] / (launch_us * 1e-6) / 1e9
-    tr = traffic_from_profile("wq_gemv.hip", "gemv_decode_step")
+    tr = traffic_from_profile(GEMV_SOURCES, "gemv_decode_step")
 
     M, K, N = PREFILL["M"], PREFILL["K"], PREFILL["N"]
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (pre["ms_gemm"] * 1e-3) / 1e12
     step_tflops = flops / (pre["ms_full"] * 1e-3) / 1e12
-    gtr = traffic_from_profile("wq_gemm.hip", "gemm_prefill")
+    gtr = traffic_from_profile(GEMM_SOURCES, "gemm_prefill")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -341,7 +368,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
-            "kernel": "gemv_stream_kernel (4-bit, M=1; R=1 for N<8192, R=2 otherwise)", "avg_launch_us": round(launch_us, 3),
+            "kernel": GEMV_KERNEL + " (every decode projection)", "avg_launch_us": round(launch_us, 3),
             "bytes_per_launch": dec["all_b"] / dec["n_launch"],
         },
         "gemm": {
@@ -351,10 +378,14 @@ def main():
             "step_tflops_incl_act_scaling": round(step_tflops, 1),
             "ms_gemm": round(pre["ms_gemm"], 5), "ms_scale_act": round(pre["ms_act"], 5),
             "ms_step": round(pre["ms_full"], 5), "pool_copies": pre["copies"],
+            "context_dense_fp16": {
+                "what": "torch.matmul fp16 (hipBLASLt) at the same M, N, K on dense fp16 weights",
+                "us": round(pre["ms_dense"] * 1e3, 2),
+                "tflops": round(flops / (pre["ms_dense"] * 1e-3) / 1e12, 1)},
             "roofline": {
                 "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": gtr,
-                "kernel": "gemm_kernel<4,128,256,1,3>", "avg_launch_us": round(pre["ms_gemm"] * 1e3, 3),
+                "kernel": GEMM_KERNEL, "avg_launch_us": round(pre["ms_gemm"] * 1e3, 3),
                 "flops_per_launch": flops,
             },
         },
