@@ -52,9 +52,10 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--only", choices=["decode", "prefill", "copy"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs"], default=None,
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
-                        "copies of a known size, the reference for scaling HBM byte counters")
+                        "copies of a known size, the reference for scaling HBM byte counters; "
+                        "'configs' times every case of the five synthetic workloads")
     return p.parse_args()
 
 
@@ -247,6 +248,83 @@ def prefill_leg(wq, torch, steps, warmup):
     return dict(ms_full=ms_full, ms_gemm=ms_gemm, ms_act=ms_act, copies=copies, ms_dense=ms_dense)
 
 
+def config_cases():
+    """Every (shape, M, format) case of the five synthetic workloads."""
+    cases = [dict(cfg="single-gemv", K=4096, N=4096, M=1, bits=4, group=128, sigma=0.02)]
+    for _, K, N in DECODE_SHAPES:
+        for M in (1, 4, 16):
+            cases.append(dict(cfg="llama7b-decode", K=K, N=N, M=M, bits=4, group=128, sigma=0.02))
+    cases.append(dict(cfg="prefill-awq", K=4096, N=11008, M=2048, bits=4, group=128, sigma=0.02, awq=True))
+    for K, N in ((8192, 28672), (28672, 8192), (8192, 10240)):
+        for M in (1, 8, 32, 512):
+            cases.append(dict(cfg="70b-layer", K=K, N=N, M=M, bits=4, group=128, sigma=0.015))
+    for bits in (2, 3, 8):
+        for group in (32, 128, -1):
+            for act in ((False, True) if group != -1 else (False,)):
+                for M in (1, 256):
+                    cases.append(dict(cfg="gptq-variant", K=4096, N=4096, M=M, bits=bits, group=group,
+                                      sigma=0.02, sym=True, act_order=act))
+    return cases
+
+
+def configs_leg(wq, torch, launches):
+    """Time wq_linear on every config case (rotating weight pools of at least
+    1 GiB, graph replays, HIP events); one JSON line per case."""
+    rows = []
+    for ci, c in enumerate(config_cases()):
+        K, N, M, bits, group = c["K"], c["N"], c["M"], c["bits"], c["group"]
+        seed = (7, ci)
+        x = torch.from_numpy(I.activations(seed, M, K)).cuda()
+        act_scale = None
+        if c.get("awq"):
+            xo = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+            act_scale = wq.awq_scales(torch.from_numpy(xo).cuda(), 0.5)
+            x = wq.scale_act(torch.from_numpy(xo).cuda(), act_scale)
+        w = torch.from_numpy(I.weights(seed, N, K, c["sigma"])).cuda()
+        g_idx = None
+        if c.get("act_order"):
+            g_idx = torch.from_numpy(I.act_order_gidx(seed, K, group)).cuda()
+        layer = wq.QuantizedLinear.from_float(w, bits=bits, group_size=group, g_idx=g_idx,
+                                              symmetric=bool(c.get("sym")), act_scale=act_scale)
+        del w
+        zeros = layer.zeros if not c.get("sym") else None
+        G = 1 if group == -1 else K // group
+        packed_b = N * K * bits // 8
+        all_b = packed_b + N * G * 2 + (N * G if zeros is not None else 0) + M * K * 2 + M * N * 2 + \
+            (4 * K if layer.perm is not None else 0)
+        per_copy = packed_b + N * G * 3
+        copies = max(2, -(-POOL_BYTES // per_copy))
+        pool = [(layer.packed, layer.scales, zeros)] + [
+            (layer.packed.clone(), layer.scales.clone(), None if zeros is None else zeros.clone())
+            for _ in range(copies - 1)]
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        need = wq.workspace_size(M, N, K, bits, layer.perm is not None)
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device="cuda")
+
+        def call(i):
+            p, sc, z = pool[i]
+            wq.linear(x, p, sc, z, bits, group, perm=layer.perm, out=y, workspace=ws if need else None)
+
+        n = max(copies, launches)
+        ms = timed(torch, call, copies, n, copies)
+        flops = 2.0 * M * N * K
+        t = ms * 1e-3
+        bound = "hbm" if all_b / (HBM_PEAK_GBS * 1e9) > flops / (FP16_MFMA_PEAK_TFLOPS * 1e12) else "mfma"
+        row = dict(cfg=c["cfg"], K=K, N=N, M=M, bits=bits, group=group, sym=bool(c.get("sym")),
+                   act_order=bool(c.get("act_order")), awq=bool(c.get("awq")),
+                   kernel="gemv" if M <= wq.gemv_max_m() else "gemm", us=round(ms * 1e3, 2),
+                   packed_GBs=round(packed_b / t / 1e9, 1), all_GBs=round(all_b / t / 1e9, 1),
+                   TFLOPs=round(flops / t / 1e12, 2), bound=bound,
+                   frac=round(all_b / t / 1e9 / HBM_PEAK_GBS if bound == "hbm" else
+                              flops / t / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+                   pool_copies=copies)
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del pool, layer, x, y, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 # -------------------------------------------------------- CPU baseline ----
 
 def cpu_baseline(target_s):
@@ -314,6 +392,9 @@ def main():
     if args.only == "decode":
         dec = decode_leg(wq, torch, args.steps, args.warmup)
         print(json.dumps({"leg": "decode", "ms_per_step": dec["ms"], "per_layer": dec["per_layer"]}), flush=True)
+        return
+    if args.only == "configs":
+        configs_leg(wq, torch, max(args.steps, 1))
         return
     if args.only == "prefill":
         pre = prefill_leg(wq, torch, gemm_steps, max(5, args.warmup // 5))

@@ -139,10 +139,17 @@ wq_status wq_dequant(const uint32_t* packed, const uint16_t* scales, const uint8
 wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t K,
                        uint16_t* x_out, void* stream);
 
-/* Bytes of device workspace wq_gemv / wq_gemm / wq_linear need for these
- * arguments (0 when none is needed; currently only wq_gemm with act-order
- * uses it, for the gathered activations). */
-size_t wq_workspace_size(int32_t M, int32_t K, int32_t has_perm);
+/* Bytes of device workspace wq_gemm (and wq_linear when it dispatches to
+ * wq_gemm) uses for these arguments on the current device; 0 when none.
+ * Layout: with act-order (has_perm != 0) the gathered activations
+ * x[:, perm], M*K fp16 values rounded up to 256 bytes; then, when the launch
+ * has too few output tiles to fill the GPU, fp32 partial outputs of a K
+ * split (splits*M*N floats; the split count is chosen on the host from the
+ * shape and the number of compute units).  The act-order part is required;
+ * the split part is optional: with less workspace wq_gemm does not split K
+ * (same result up to fp32 summation order, slower).  wq_gemv never uses
+ * workspace.  Returns 0 for non-positive sizes or unsupported bit widths. */
+size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t has_perm);
 
 /* y fp16 [M][N] = x fp16 [M][K] . dequant(packed)^T with fp32 accumulation
  * and one rounding of the sum to fp16.
@@ -157,8 +164,12 @@ size_t wq_workspace_size(int32_t M, int32_t K, int32_t has_perm);
  * wq_linear: picks wq_gemv for M <= wq_gemv_max_m() and wq_gemm otherwise
  *   (the batch-size dispatch).
  *
- * workspace: device memory of at least wq_workspace_size(M, K, perm != NULL)
- * bytes, or NULL when that size is 0.  y must not overlap any input. */
+ * workspace: device memory of wq_workspace_size(M, N, K, bits, perm != NULL)
+ * bytes (16-byte aligned), or NULL when that size is 0; WQ_ERR_ARG if
+ * act-order needs it and it is missing or short.  Split-K partials are
+ * summed in a fixed order, so results are deterministic.  Calls that share
+ * a workspace must be ordered on one stream.  y must not overlap any input
+ * or the workspace. */
 wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                   const uint8_t* zeros, const int32_t* perm, uint16_t* y,
                   int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,

@@ -34,8 +34,19 @@ def test_status_strings_and_version():
 
 
 def test_workspace_size():
-    assert wq.workspace_size(2048, 4096, False) == 0
-    assert wq.workspace_size(256, 4096, True) == 256 * 4096 * 2
+    # enough output tiles to fill the GPU: no split, no workspace
+    assert wq.workspace_size(2048, 11008, 4096, 4, False) == 0
+    # act-order gather (M*K fp16) plus, with few tiles, whole fp32 copies of y
+    ws = wq.workspace_size(256, 4096, 4096, 4, True)
+    gather = 256 * 4096 * 2
+    assert ws > gather and (ws - gather) % (256 * 4096 * 4) == 0
+    assert 2 <= (ws - gather) // (256 * 4096 * 4) <= 16
+    # few tiles along a long K: split partials only
+    ws = wq.workspace_size(32, 8192, 28672, 4, False)
+    assert ws > 0 and ws % (32 * 8192 * 4) == 0
+    # invalid arguments
+    assert wq.workspace_size(0, 4096, 4096, 4, False) == 0
+    assert wq.workspace_size(256, 4096, 4096, 5, False) == 0
 
 
 def _mm(name, x=FAKE, packed=FAKE, scales=FAKE, zeros=None, perm=None, y=FAKE, M=1, N=64, K=128, bits=4,

@@ -193,6 +193,31 @@ def test_gemm_ragged_shapes(M, N, K):
     check_y(run("gemm", x, L, 4, gs), O.linear_ref(x, ref["w_hat"]), f"gemm M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K,gs", [(20, 256, 8192, 128), (100, 300, 4096, 128), (100, 300, 4128, 32),
+                                      (1, 72, 4128, 32), (64, 4104, 2048, 64)])
+def test_split_k_matches_unsplit(M, N, K, gs):
+    # Few output tiles: wq_gemm splits K across blocks into the workspace
+    # and sums the fp32 partials in order.  Without room for the partials it
+    # does not split; both must meet the tolerance and agree to rounding.
+    seed = (108, M, N, K)
+    w = I.weights(seed, N, K, 0.02)
+    ref = O.quantize_linear_layer(w, 4, gs)
+    L = gpu_layer(w, 4, gs)
+    x = I.activations(seed, M, K)
+    need = wq.workspace_size(M, N, K, 4, False)
+    assert need > 0, "shape expected to split"
+    xd = dev(x)
+    ys = wq.gemm(xd, L["packed"], L["scales"], L["zeros"], 4, gs,
+                 workspace=torch.empty((need,), dtype=torch.uint8, device="cuda"))
+    yn = wq.gemm(xd, L["packed"], L["scales"], L["zeros"], 4, gs,
+                 workspace=torch.empty((16,), dtype=torch.uint8, device="cuda"))
+    y_ref = O.linear_ref(x, ref["w_hat"])
+    check_y(ys, y_ref, f"split M={M} N={N} K={K}")
+    check_y(yn, y_ref, f"unsplit M={M} N={N} K={K}")
+    d = np.abs(host(ys).astype(np.float64) - host(yn).astype(np.float64))
+    assert d.max() <= 1e-2 * max(1.0, np.abs(y_ref).max()), d.max()
+
+
 VARIANTS = [(b, g, a) for b in (2, 3, 8) for g in (32, 128, -1) for a in (False, True) if not (a and g == -1)]
 
 

@@ -40,7 +40,7 @@ _SIG = {
     "wq_unpack": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP]),
     "wq_dequant": (ctypes.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP]),
     "wq_scale_act": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _VP]),
-    "wq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "wq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "wq_gemv_max_m": (_I32, []),
 }
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
@@ -252,8 +252,10 @@ def scale_act(x, s, out=None):
     return out
 
 
-def workspace_size(M: int, K: int, has_perm: bool) -> int:
-    return int(lib().wq_workspace_size(M, K, int(bool(has_perm))))
+def workspace_size(M: int, N: int, K: int, bits: int, has_perm: bool) -> int:
+    """Bytes of workspace wq_gemm uses for these arguments (act-order gather
+    and split-K partials); 0 when none."""
+    return int(lib().wq_workspace_size(M, N, K, bits, int(bool(has_perm))))
 
 
 def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, out=None, workspace=None):
@@ -268,7 +270,8 @@ def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, o
     _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
     y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
         _dev(out, torch.float16, "out", 2)
-    need = workspace_size(M, K, perm is not None)
+    uses_gemm = entry == "wq_gemm" or (entry == "wq_linear" and M > gemv_max_m())
+    need = workspace_size(M, N, K, bits, perm is not None) if uses_gemm else 0
     ws_bytes = 0
     if need:
         if workspace is None:

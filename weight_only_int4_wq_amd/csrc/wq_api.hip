@@ -6,8 +6,11 @@
 #include "wq_common.h"
 
 namespace {
-// Largest activation row count sent to the GEMV kernel by wq_linear.
-constexpr int kGemvMaxM = 16;
+// Largest activation row count sent to the GEMV kernel by wq_linear.  The
+// GEMV's dot products cost M fp16-pair instructions per weight pair, the
+// matrix-core GEMM's dequantization a fixed few: measured on the decode and
+// 70B layer shapes, the GEMV is faster up to M = 4 and the GEMM from M = 8.
+constexpr int kGemvMaxM = 4;
 }  // namespace
 
 namespace wqh {

@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ scales,
                                                    const uint8_t* __restrict__ zeros, uint16_t* __restrict__ y,
                                                    int M, int N, int K, GroupDiv gd, int m_tiles, int n_tiles,
-                                                   int tiles) {
+                                                   int tiles, int sps, float* __restrict__ part) {
     constexpr int GM = 4;  // M-tiles per strip of the tile order
     constexpr int WAVES_N = 4 / WAVES_M;
     constexpr int BK = 128;
@@ -67,6 +67,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     const size_t row_words = (size_t)chunks * BITS;
     const int n_lane0 = n0 + wn * WN + li;
     const int stages = (K + BK - 1) / BK;
+    // split-K: this block's range of stages (blockIdx.y), all of K unsplit
+    const int st_begin = blockIdx.y * sps;
+    const int st_end = min(st_begin + sps, stages);
 
     // ---- A: this wavefront's share of a stage, global -> LDS directly.
     // Copy i of the wavefront fills units [64 * (wave * A_INSTR + i), +64):
@@ -187,27 +190,29 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     // prologue issues stages 0 and 1; past the last stage the copies reread
     // in-range data into buffers that are not read again.
     BRegs b0, b1, b2;
-    issue_b(b0, 0);
+    issue_b(b0, st_begin * BK);
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(As0, 0);
+    issue_a(As0, st_begin * BK);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(b1, BK);
+    issue_b(b1, (st_begin + 1) * BK);
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(As1, BK);
+    issue_a(As1, (st_begin + 1) * BK);
     __builtin_amdgcn_sched_barrier(0);
-    int st = 0;
-    for (; st + 3 <= stages; st += 3) {
+    int st = st_begin;
+    for (; st + 3 <= st_end; st += 3) {
         stage(st, b0, b2, As0, As2);
         stage(st + 1, b1, b0, As1, As0);
         stage(st + 2, b2, b1, As2, As1);
     }
-    if (st < stages) stage(st, b0, b2, As0, As2);
-    if (st + 1 < stages) stage(st + 1, b1, b0, As1, As0);
+    if (st < st_end) stage(st, b0, b2, As0, As2);
+    if (st + 1 < st_end) stage(st + 1, b1, b0, As1, As0);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-    // ---- epilogue: lane holds rows 4*lg + r of column li of each 16x16 tile
+    // ---- epilogue: lane holds rows 4*lg + r of column li of each 16x16
+    // tile; fp16 y, or this range's fp32 partial
+    float* pr = part ? part + (size_t)blockIdx.y * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -216,10 +221,25 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + wm * WM + i * 16 + 4 * lg + r;
-                if (row < M && col < N)
-                    y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                if (row < M && col < N) {
+                    if (pr)
+                        pr[(size_t)row * N + col] = acc[i][j][r];
+                    else
+                        y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                }
             }
         }
+}
+
+// y = fp16 of the sum of the split-K partials, ranges added in order.
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ part, int splits, long long mn,
+                                                            uint16_t* __restrict__ y) {
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < mn;
+         t += (long long)gridDim.x * blockDim.x) {
+        float v = part[t];
+        for (int r = 1; r < splits; ++r) v += part[t + r * mn];
+        y[t] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
 }
 
 // x_out[m][k'] = x[m][perm[k']]: activations in packed column order.
@@ -235,32 +255,84 @@ __global__ void __launch_bounds__(256) gather_act_kernel(const uint16_t* __restr
     }
 }
 
+// Blocks of gemm_kernel resident per CU, by tile height: the register file
+// (512 per lane per SIMD, one wavefront of each block per SIMD) holds three
+// 16-row, two 32-row and one 64- or 128-row block.
+constexpr int small_tile_blocks_per_cu(int BM) { return BM <= 16 ? 3 : BM <= 32 ? 2 : 1; }
+
+template <int BM, int BN>
+wqh::SplitPlan tile_plan(int M, int N, int K, int bits, size_t ws_avail) {
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return wqh::plan_split(M, N, K, bits, BM, BN, tiles, wqh::gemm_slots(small_tile_blocks_per_cu(BM)), ws_avail);
+}
+
 template <int BITS, int BM, int BN, int WAVES_M, int NST>
 wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                      uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+                      uint16_t* y, int M, int N, int K, int gs, float* part, size_t part_bytes, hipStream_t s) {
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
+    const wqh::SplitPlan plan = tile_plan<BM, BN>(M, N, K, BITS, part ? part_bytes : 0);
+    const bool split = plan.splits > 1;
+    const dim3 grid(tiles, plan.splits);
+    float* pp = split ? part : nullptr;
     if (zeros)
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true>), dim3(tiles), dim3(256), 0, s, x, packed,
-                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles);
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true>), grid, dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false>), dim3(tiles), dim3(256), 0, s, x, packed,
-                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles);
-    return wqh::launch_status();
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false>), grid, dim3(256), 0, s, x, packed,
+                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    const wq_status st = wqh::launch_status();
+    if (st != WQ_OK || !split) return st;
+    return wqh::splitk_reduce(part, plan.splits, M, N, y, s);
 }
 
 // Small M: narrow tiles for more blocks.  Large M: 128 x 256 tiles with the
 // four wavefronts side by side along N, so every packed weight column is
 // dequantized by one wavefront and each activation row is re-read from L2
-// once per 256 output columns.
+// once per 256 output columns.  Any of them splits K across blocks when there
+// are too few tiles to fill the machine and the workspace holds the partials.
+enum class TileKind { k16, k32, k64, kLarge, k128 };
+
+inline TileKind tile_kind(int M, int N, int K, int bits) {
+    if (M <= 16) return TileKind::k16;
+    if (M <= 32) return TileKind::k32;
+    if (M <= 64) return TileKind::k64;
+    if (wqh::gemm_large_fits(M, N, K, bits)) return TileKind::kLarge;
+    return TileKind::k128;
+}
+
+// Bytes of fp32 partials the chosen kernel's split plan needs (0: no split).
+inline size_t split_bytes(int M, int N, int K, int bits) {
+    wqh::SplitPlan p;
+    const size_t inf = ~size_t(0);
+    switch (tile_kind(M, N, K, bits)) {
+        case TileKind::k16: p = tile_plan<16, 128>(M, N, K, bits, inf); break;
+        case TileKind::k32: p = tile_plan<32, 128>(M, N, K, bits, inf); break;
+        case TileKind::k64: p = tile_plan<64, 128>(M, N, K, bits, inf); break;
+        case TileKind::kLarge: p = wqh::gemm_large_plan(M, N, K, bits, inf); break;
+        default: p = tile_plan<128, 256>(M, N, K, bits, inf); break;
+    }
+    return p.splits > 1 ? size_t(p.splits) * size_t(M) * size_t(N) * 4 : 0;
+}
+
 template <int BITS>
 wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                      uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
-    if (M <= 32) return launch_tile<BITS, 32, 128, 2, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    if (M <= 64) return launch_tile<BITS, 64, 128, 2, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    if (wqh::gemm_large_fits(M, N, K, BITS)) return wqh::gemm_large(BITS, x, packed, scales, zeros, y, M, N, K, gs, s);
-    return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, s);
+                      uint16_t* y, int M, int N, int K, int gs, float* part, size_t part_bytes, hipStream_t s) {
+    switch (tile_kind(M, N, K, BITS)) {
+        case TileKind::k16:
+            return launch_tile<BITS, 16, 128, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+        case TileKind::k32:
+            return launch_tile<BITS, 32, 128, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+        case TileKind::k64:
+            return launch_tile<BITS, 64, 128, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+        case TileKind::kLarge: {
+            const wqh::SplitPlan plan = wqh::gemm_large_plan(M, N, K, BITS, part ? part_bytes : 0);
+            return wqh::gemm_large(BITS, x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+        }
+        default:
+            return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+    }
 }
 
 }  // namespace
@@ -270,9 +342,38 @@ wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uin
                             int M, int N, int K, int bits, int group_size, int* gs_out);
 }
 
-extern "C" size_t wq_workspace_size(int32_t M, int32_t K, int32_t has_perm) {
-    if (!has_perm || M <= 0 || K <= 0) return 0;
-    return size_t(M) * size_t(K) * 2;
+namespace wqh {
+
+int gemm_slots(int blocks_per_cu) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return cus * blocks_per_cu;
+}
+
+wq_status splitk_reduce(const float* part, int splits, int M, int N, uint16_t* y, hipStream_t s) {
+    const long long mn = (long long)M * N;
+    long long blocks = (mn + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(int(blocks)), dim3(256), 0, s, part, splits, mn, y);
+    return launch_status();
+}
+
+}  // namespace wqh
+
+// Workspace layout: [gathered activations, act-order only, rounded up to 256
+// bytes] [split-K fp32 partials, when the launch splits K].
+static size_t gather_bytes(int M, int K, int has_perm) {
+    if (!has_perm) return 0;
+    return (size_t(M) * size_t(K) * 2 + 255) & ~size_t(255);
+}
+
+extern "C" size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t has_perm) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return 0;
+    return gather_bytes(M, K, has_perm) + split_bytes(M, N, K, bits);
 }
 
 extern "C" wq_status wq_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
@@ -282,11 +383,12 @@ extern "C" wq_status wq_gemm(const uint16_t* x, const uint32_t* packed, const ui
     const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
     if (st != WQ_OK) return st;
     if (M == 0 || N == 0) return WQ_OK;
+    if (workspace && !wqh::aligned16(workspace)) return WQ_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* xa = x;
+    const size_t gb = gather_bytes(M, K, perm != nullptr);
     if (perm) {
-        const size_t need = wq_workspace_size(M, K, 1);
-        if (!workspace || workspace_bytes < need || !wqh::aligned16(workspace)) return WQ_ERR_ARG;
+        if (!workspace || workspace_bytes < size_t(M) * size_t(K) * 2) return WQ_ERR_ARG;
         uint16_t* xg = static_cast<uint16_t*>(workspace);
         long long total = (long long)M * K;
         long long blocks = (total + 255) / 256;
@@ -296,10 +398,18 @@ extern "C" wq_status wq_gemm(const uint16_t* x, const uint32_t* packed, const ui
         if (ls != WQ_OK) return ls;
         xa = xg;
     }
+    // split-K partials go after the gathered activations; without room for
+    // them the launch does not split
+    float* part = nullptr;
+    size_t part_bytes = 0;
+    if (workspace && workspace_bytes > gb) {
+        part = reinterpret_cast<float*>(static_cast<char*>(workspace) + gb);
+        part_bytes = workspace_bytes - gb;
+    }
     switch (bits) {
-        case 2: return launch_bits<2>(xa, packed, scales, zeros, y, M, N, K, gs, s);
-        case 3: return launch_bits<3>(xa, packed, scales, zeros, y, M, N, K, gs, s);
-        case 4: return launch_bits<4>(xa, packed, scales, zeros, y, M, N, K, gs, s);
-        default: return launch_bits<8>(xa, packed, scales, zeros, y, M, N, K, gs, s);
+        case 2: return launch_bits<2>(xa, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+        case 3: return launch_bits<3>(xa, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+        case 4: return launch_bits<4>(xa, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+        default: return launch_bits<8>(xa, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
     }
 }

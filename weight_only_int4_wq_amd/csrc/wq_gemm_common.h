@@ -1,6 +1,8 @@
 // Device helpers shared by the prefill GEMM kernels (gfx950 only).
 #pragma once
 
+#include <algorithm>
+
 #include "wq_common.h"
 
 namespace wq {
@@ -74,10 +76,59 @@ __device__ __forceinline__ void tile_coords(int b, int tiles, int m_tiles, int n
 
 namespace wqh {
 
+// Split-K plan of one GEMM launch: the K stages (128 deep) are cut into
+// `splits` ranges of `sps` stages; with splits > 1 every block writes its
+// fp32 partial tile to the workspace and splitk_reduce sums the ranges.
+struct SplitPlan {
+    int splits = 1, sps = 0;
+};
+
+// Pick the split count that minimizes a simple time model: one tile over all
+// of K takes `unit_us`; `tiles * S` blocks run in rounds of `slots` resident
+// blocks, each doing 1/S of the work; every extra range costs writing and
+// re-reading an fp32 copy of y plus the reduction launch.  Ranges keep at
+// least 4 stages, and the partials must fit in `ws_avail` bytes.
+inline SplitPlan plan_split(int M, int N, int K, int bits, int BM, int BN, int tiles, int slots, size_t ws_avail) {
+    SplitPlan best;
+    const int stages = (K + 127) / 128;
+    best.sps = stages;
+    if (tiles <= 0 || slots <= 0 || stages < 8) return best;
+    const double flops_tile = 2.0 * BM * BN * double(K);
+    const double bytes_tile = double(BN) * K * bits / 8.0;
+    const double unit_us = std::max(flops_tile / 3.5e12, bytes_tile / 15e9) * 1e6;
+    const double part_bytes = double(M) * N * 4.0;
+    const double part_us = 2.0 * part_bytes / 4e12 * 1e6;
+    double best_cost = unit_us * double((tiles + slots - 1) / slots);
+    for (int S = 2; S <= 16 && S * 4 <= stages; ++S) {
+        const int sps = (stages + S - 1) / S;
+        const int Se = (stages + sps - 1) / sps;  // ranges actually used
+        if (double(Se) * part_bytes > double(ws_avail)) break;
+        const long long blocks = (long long)tiles * Se;
+        const double rounds = double((blocks + slots - 1) / slots);
+        const double cost = unit_us * rounds * double(sps) / stages + Se * part_us + 2.0;
+        if (cost < best_cost * 0.97) {
+            best_cost = cost;
+            best.splits = Se;
+            best.sps = sps;
+        }
+    }
+    return best;
+}
+
+// Resident blocks of a GEMM kernel on the current device.
+int gemm_slots(int blocks_per_cu);
+
+// y[m][n] = fp16(sum over ranges r = 0..splits-1, in order, of part[r][m][n]).
+wq_status splitk_reduce(const float* part, int splits, int M, int N, uint16_t* y, hipStream_t s);
+
 // Large-M prefill GEMM (128 x 256 tiles on 32x32x16 instructions).  Its
 // offsets are 32-bit: usable when gemm_large_fits().
 bool gemm_large_fits(int M, int N, int K, int bits);
+// Split plan of the large-M kernel for these arguments (ws_avail: bytes of
+// workspace available for partials).
+SplitPlan gemm_large_plan(int M, int N, int K, int bits, size_t ws_avail);
 wq_status gemm_large(int bits, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-                     const uint8_t* zeros, uint16_t* y, int M, int N, int K, int gs, hipStream_t s);
+                     const uint8_t* zeros, uint16_t* y, int M, int N, int K, int gs, SplitPlan plan,
+                     float* part, hipStream_t s);
 
 }  // namespace wqh

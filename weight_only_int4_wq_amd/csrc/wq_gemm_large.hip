@@ -70,7 +70,8 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ scales,
                                                          const uint8_t* __restrict__ zeros,
                                                          uint16_t* __restrict__ y, int M, int N, int K, GroupDiv gd,
-                                                         int m_tiles, int n_tiles, int tiles) {
+                                                         int m_tiles, int n_tiles, int tiles, int sps,
+                                                         float* __restrict__ part) {
     constexpr int GM = 4;
     constexpr int BM = 128, BN = 256, BK = 128, WN = 64;
     constexpr int TM = BM / 32, TN = WN / 32;
@@ -96,6 +97,9 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
     const int chunks = K / 32;
     const int G = chunk_group(chunks - 1, gd) + 1;
     const int stages = (K + BK - 1) / BK;
+    // split-K: this block's range of stages (blockIdx.y), all of K unsplit
+    const int st_begin = blockIdx.y * sps;
+    const int st_end = min(st_begin + sps, stages);
 
     // ---- activation copies: byte offset of each copy's source from x + k0
     // (rows past M read row M - 1; their outputs are not stored).  With
@@ -256,7 +260,7 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
     // loads of stage st + 2 go to `fill` / Af.
     auto stage = [&](int st, const BRegs& cur, const BRegs& nxt, BRegs& fill, const uint8_t* Ab,
                      const uint8_t* An, uint8_t* Af) {
-        const int sf = min(st + 2, stages - 1);
+        const int sf = min(st + 2, st_end - 1);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cb = t & 1;
@@ -294,29 +298,31 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
     // loop is unrolled by 3).  Past the last stage, copies and loads re-read
     // the last stage into buffers and registers that are not used again.
     BRegs b0, b1, b2;
-    issue_b_all(b0, 0);
-    issue_a(As0, 0, 0, A_INSTR);
-    issue_b_all(b1, min(1, stages - 1));
-    issue_a(As1, min(1, stages - 1) * BK, 0, A_INSTR);
+    const int st_next = min(st_begin + 1, st_end - 1);
+    issue_b_all(b0, st_begin);
+    issue_a(As0, st_begin * BK, 0, A_INSTR);
+    issue_b_all(b1, st_next);
+    issue_a(As1, st_next * BK, 0, A_INSTR);
     copy_barrier<B_OPS + A_INSTR>();
     make_q(b0, q);
     load_a(As0, 0, af[0]);
     make_b(b0, q, 0, bf[0]);
 
-    int st = 0;
-    for (; st + 3 <= stages; st += 3) {
+    int st = st_begin;
+    for (; st + 3 <= st_end; st += 3) {
         stage(st, b0, b1, b2, As0, As1, As2);
         stage(st + 1, b1, b2, b0, As1, As2, As0);
         stage(st + 2, b2, b0, b1, As2, As0, As1);
     }
-    if (st < stages) stage(st, b0, b1, b2, As0, As1, As2);
-    if (st + 1 < stages) stage(st + 1, b1, b2, b0, As1, As2, As0);
+    if (st < st_end) stage(st, b0, b1, b2, As0, As1, As2);
+    if (st + 1 < st_end) stage(st + 1, b1, b2, b0, As1, As2, As0);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     // ---- epilogue: acc[i][j][r] is row 32i + 8(r/4) + 4h + r%4, column
-    // 32j + c of the wavefront's tile
+    // 32j + c of the wavefront's tile; fp16 y, or this range's fp32 partial
+    float* pr = part ? part + (size_t)blockIdx.y * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -325,34 +331,43 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (row < M && col < N)
-                    y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                if (row < M && col < N) {
+                    if (pr)
+                        pr[(size_t)row * N + col] = acc[i][j][r];
+                    else
+                        y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
+                }
             }
         }
 }
 
 template <int BITS, bool HAS_Z>
 wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                   uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+                   uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, hipStream_t s) {
     constexpr int BM = 128, BN = 256;
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
     const bool fast = (K % 128 == 0) && (gs % 128 == 0);
+    const bool split = plan.splits > 1;
+    const dim3 grid(tiles, plan.splits);
+    float* pp = split ? part : nullptr;
     if (fast)
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true>), dim3(tiles), dim3(256), 0, s, x, packed, scales,
-                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles);
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true>), grid, dim3(256), 0, s, x, packed, scales, zeros, y,
+                           M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false>), dim3(tiles), dim3(256), 0, s, x, packed, scales,
-                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles);
-    return wqh::launch_status();
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false>), grid, dim3(256), 0, s, x, packed, scales, zeros,
+                           y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    const wq_status st = wqh::launch_status();
+    if (st != WQ_OK || !split) return st;
+    return wqh::splitk_reduce(part, plan.splits, M, N, y, s);
 }
 
 template <int BITS>
 wq_status launch_large(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                       uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
-    if (zeros) return launch_z<BITS, true>(x, packed, scales, zeros, y, M, N, K, gs, s);
-    return launch_z<BITS, false>(x, packed, scales, zeros, y, M, N, K, gs, s);
+                       uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, hipStream_t s) {
+    if (zeros) return launch_z<BITS, true>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+    return launch_z<BITS, false>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
 }
 
 }  // namespace
@@ -366,13 +381,20 @@ bool gemm_large_fits(int M, int N, int K, int bits) {
            uint64_t(N) * uint64_t(K / 32) < lim;
 }
 
+SplitPlan gemm_large_plan(int M, int N, int K, int bits, size_t ws_avail) {
+    constexpr int BM = 128, BN = 256;
+    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return plan_split(M, N, K, bits, BM, BN, tiles, gemm_slots(1), ws_avail);
+}
+
 wq_status gemm_large(int bits, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
-                     const uint8_t* zeros, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+                     const uint8_t* zeros, uint16_t* y, int M, int N, int K, int gs, SplitPlan plan, float* part,
+                     hipStream_t s) {
     switch (bits) {
-        case 2: return launch_large<2>(x, packed, scales, zeros, y, M, N, K, gs, s);
-        case 3: return launch_large<3>(x, packed, scales, zeros, y, M, N, K, gs, s);
-        case 4: return launch_large<4>(x, packed, scales, zeros, y, M, N, K, gs, s);
-        default: return launch_large<8>(x, packed, scales, zeros, y, M, N, K, gs, s);
+        case 2: return launch_large<2>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+        case 3: return launch_large<3>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+        case 4: return launch_large<4>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+        default: return launch_large<8>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
     }
 }
 
