@@ -14,9 +14,11 @@ from .wq_oracle import (  # noqa: F401
     unpack,
     dequant,
     dequant_fp64_path,
+    awq_alpha_grid,
     awq_channel_scales,
     awq_fold_weight,
     awq_scale_act,
+    awq_search,
     linear_ref,
     quantize_linear_layer,
     f64_to_f16_nearest,

@@ -21,6 +21,9 @@ What it computes, and where each step comes from:
   activation magnitude raised to alpha; the layer output is unchanged in exact
   arithmetic.  "GPTQ, AWQ and the rules of post-training quantization",
   section "AWQ: find the one percent that matters".
+* AWQ's search for alpha: a 20-point grid on [0, 1], each point scored by
+  the squared output error of the rescaled, quantized layer against the
+  original layer on the calibration activations (same section).
 * Packing of codes into 32-bit words, dequantization (q - z) * s and the
   product y = x . dequant(Wq)^T.  Weights stay packed and are dequantized on
   the fly inside the product: "AutoAWQ vs The Stack v2", paragraph on the
@@ -283,6 +286,48 @@ def quantize_linear_layer(w, bits: int, group_size: int, g_idx=None, symmetric: 
         packed=pack(packed_codes, bits),
         w_hat=dequant(codes, scales, zeros, bits, group_size, g_idx),
     )
+
+
+def awq_alpha_grid(n_grid: int = 20) -> np.ndarray:
+    """The AWQ exponent grid: n_grid evenly spaced points on [0, 1], both
+    ends included ("GPTQ, AWQ and the rules of post-training quantization",
+    section "AWQ: find the one percent that matters": a grid search of 20
+    points on the interval from 0 to 1; the pages do not say whether the
+    ends are included, and the plain reading of points on the closed
+    interval is taken)."""
+    if n_grid < 2:
+        raise ValueError("the grid needs at least 2 points")
+    return np.arange(n_grid, dtype=F64) / F64(n_grid - 1)
+
+
+def awq_search(x, w, bits: int, group_size: int, n_grid: int = 20, symmetric: bool = False):
+    """AWQ's grid search for the scaling exponent alpha (same section).
+
+    For every alpha on awq_alpha_grid(n_grid): s_h = AWQ channel scales of
+    x with that alpha, W' = W folded by s_h, x' = x divided by s_h, W'
+    RTN-quantized and dequantized to w_hat', and the loss is the squared
+    output error of the quantized layer against the original one,
+        loss = sum over m, n of (x' . w_hat'^T - x . W^T)[m][n]^2,
+    both products exact in float64 from the fp16 operands.  The pages say
+    the rescaling reduces the quantization error and that alpha comes from a
+    20-point search; they do not state the search objective, and the layer
+    output error on the calibration activations is the reading taken.
+    Returns (alphas float64 [n_grid], losses float64 [n_grid], best index =
+    first minimum).
+    """
+    x = np.asarray(x, dtype=F16)
+    w = np.asarray(w, dtype=F16)
+    alphas = awq_alpha_grid(n_grid)
+    y_ref = linear_ref(x, w)
+    losses = np.empty(n_grid, dtype=F64)
+    for i, a in enumerate(alphas):
+        _, s_h = awq_channel_scales(x, float(a))
+        w_f = awq_fold_weight(w, s_h)
+        x_f = awq_scale_act(x, s_h)
+        q = quantize_linear_layer(w_f, bits, group_size, symmetric=symmetric)
+        d = linear_ref(x_f, q["w_hat"]) - y_ref
+        losses[i] = np.sum(d * d)
+    return alphas, losses, int(np.argmin(losses))
 
 
 def f64_to_f16_nearest(v: float) -> np.float16:

@@ -317,6 +317,78 @@ def test_awq_reduces_error_on_outlier_channels():
     assert e_awq < 0.8 * e_plain
 
 
+# ------------------------------------------------------------ AWQ search
+
+def test_awq_alpha_grid_closed_form():
+    # twenty evenly spaced points on the closed interval [0, 1]
+    g = O.awq_alpha_grid(20)
+    assert g.shape == (20,)
+    assert g[0] == 0.0 and g[-1] == 1.0
+    assert np.allclose(np.diff(g), 1.0 / 19.0, rtol=0, atol=1e-15)
+
+
+def test_awq_search_at_alpha_zero_is_plain_rtn():
+    # alpha = 0 gives s = a^0 = 1 for every channel: the fold and the
+    # division are identities, so the first loss is the plain RTN output
+    # error, computed here without any AWQ step.
+    M, K, N = 16, 256, 24
+    seed = (44,)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    _, losses, _ = O.awq_search(x, w, 4, 128, n_grid=4)
+    q = O.quantize_linear_layer(w, 4, 128)
+    d = x.astype(np.float64) @ (q["w_hat"].astype(np.float64) - w.astype(np.float64)).T
+    assert np.isclose(losses[0], np.sum(d * d), rtol=1e-12, atol=0)
+
+
+def test_awq_search_bruteforce_tiny():
+    # Every step written out with scalar loops on a tiny layer (one group):
+    # channel statistics, scale rounding, fold, division, quantization by
+    # the pinned RTN, and the squared output error against the original.
+    M, K, N = 3, 32, 2
+    seed = (45,)
+    x = I.activations(seed, M, K)
+    w = I.weights(seed, N, K, 0.05)
+    alphas, losses, best = O.awq_search(x, w, 4, 32, n_grid=3)
+    assert list(alphas) == [0.0, 0.5, 1.0]
+    for i, a in enumerate(alphas):
+        s_h = np.zeros(K, dtype=np.float16)
+        for k in range(K):
+            mean = sum(abs(float(x[m, k])) for m in range(M)) / M
+            s_h[k] = np.float16(mean ** a)
+        wf = np.zeros((N, K), dtype=np.float16)
+        xf = np.zeros((M, K), dtype=np.float16)
+        for k in range(K):
+            for n in range(N):
+                wf[n, k] = np.float16(np.float32(w[n, k]) * np.float32(s_h[k]))
+            for m in range(M):
+                xf[m, k] = np.float16(np.float32(x[m, k]) / np.float32(s_h[k]))
+        codes, scales, zeros = O.rtn_quantize(wf, 4, 32)
+        loss = 0.0
+        for m in range(M):
+            for n in range(N):
+                yq = sum(float(xf[m, k]) * float(np.float16(np.float32(int(codes[n, k]) - int(zeros[n, 0]))
+                                                             * np.float32(scales[n, 0])))
+                         for k in range(K))
+                yr = sum(float(x[m, k]) * float(w[n, k]) for k in range(K))
+                loss += (yq - yr) ** 2
+        assert np.isclose(losses[i], loss, rtol=1e-10, atol=0), (i, losses[i], loss)
+    assert best == int(np.argmin(losses))
+
+
+def test_awq_search_prefers_rescaling_on_outlier_channels():
+    # With a few high-magnitude input channels the search settles on a
+    # positive alpha whose output error is clearly below plain RTN's
+    # (the rescaling claim of "AWQ: find the one percent that matters").
+    M, K, N = 128, 1024, 128
+    seed = (46,)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    alphas, losses, best = O.awq_search(x, w, 4, 128, n_grid=20)
+    assert alphas[best] > 0.0
+    assert losses[best] < 0.8 * losses[0]
+
+
 # ------------------------------------------------------------------ matmul
 
 def test_linear_matches_bruteforce_triple_loop():
