@@ -102,6 +102,33 @@ wq_status wq_awq_scales(const uint16_t* x, int32_t M, int32_t K, double alpha,
 wq_status wq_awq_fold(const uint16_t* w, const uint16_t* s, int32_t N, int32_t K,
                       uint16_t* w_out, void* stream);
 
+/* AWQ's search for the scaling exponent ("GPTQ, AWQ and the rules of
+ * post-training quantization", section "AWQ: find the one percent that
+ * matters": s = (mean |x|)^alpha per input channel, alpha from a grid of
+ * 20 points on [0, 1]).  For alpha_i = i / (n_grid - 1), i = 0..n_grid-1:
+ * s = wq_awq_scales(x, alpha_i), W' = wq_awq_fold(w, s),
+ * x' = wq_scale_act(x, s), W' RTN-quantized (wq_quantize_rtn, bits,
+ * group_size, symmetric) and packed, and
+ *   losses[i] = sum over m, n of (x' . dequant(W')^T - x . w^T)[m][n]^2,
+ * each product accumulated in fp32 by the matrix cores, the squares summed
+ * in float64 in a fixed order (deterministic).  *best (nullable) = the first
+ * index of the smallest loss.
+ * x fp16 [M][K] (calibration activations), w fp16 [N][K]; losses: HOST
+ * memory, n_grid doubles; workspace: device memory of at least
+ * wq_awq_search_workspace_size(...) bytes, 16-byte aligned.  2 <= n_grid
+ * <= 4096; group_size as for wq_quantize_rtn (-1 = one group per row).
+ * Set-up time: this call SYNCHRONIZES `stream` (it copies the losses back).
+ * Returns WQ_ERR_ARG for null/misaligned pointers, bad sizes or a short
+ * workspace, WQ_ERR_UNSUPPORTED for other bit widths. */
+wq_status wq_awq_search(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N, int32_t K,
+                        int32_t bits, int32_t group_size, int32_t symmetric, int32_t n_grid,
+                        double* losses, int32_t* best, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Bytes of device workspace wq_awq_search needs (0 for invalid arguments). */
+size_t wq_awq_search_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits,
+                                    int32_t group_size, int32_t n_grid);
+
 /* Act-order packing order: perm = stable sort of k by g_idx[k].  Checks that
  * every g_idx lies in [0, K/group_size) and every group holds exactly
  * group_size channels; returns WQ_ERR_ARG otherwise.  This call SYNCHRONIZES

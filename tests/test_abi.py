@@ -17,7 +17,8 @@ def test_library_exports_every_declared_symbol():
     names = wq.exported_names()
     expected = {"wq_status_str", "wq_version", "wq_quantize_rtn", "wq_awq_scales", "wq_awq_fold",
                 "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
-                "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m"}
+                "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m",
+                "wq_awq_search", "wq_awq_search_workspace_size"}
     assert set(names) == expected
     handle = wq.lib()
     for name in names:
@@ -75,6 +76,24 @@ def test_matmul_argument_checks(name):
     assert _mm(name, M=0) == WQ_OK
     assert _mm(name, N=0) == WQ_OK
     assert _mm(name, M=0, x=None, y=None) == WQ_OK   # an empty tensor may have no storage
+
+
+def test_awq_search_argument_checks():
+    L = wq.lib()
+    size = L.wq_awq_search_workspace_size
+    assert size(64, 32, 256, 4, 128, 20) > 0
+    assert size(64, 32, 256, 4, 128, 1) == 0       # a grid needs two points
+    assert size(64, 32, 250, 4, 128, 20) == 0      # K not a multiple of 32
+    assert size(64, 32, 256, 5, 128, 20) == 0      # unsupported width
+    assert size(64, 32, 256, 4, 96, 20) == 0       # group does not divide K
+    losses = (ctypes.c_double * 20)()
+    lp = ctypes.cast(losses, ctypes.c_void_p)
+    assert L.wq_awq_search(None, FAKE, 64, 32, 256, 4, 128, 0, 20, lp, None, FAKE, 1 << 30, None) == WQ_ERR_ARG
+    assert L.wq_awq_search(FAKE, FAKE, 64, 32, 256, 4, 128, 0, 20, None, None, FAKE, 1 << 30, None) == WQ_ERR_ARG
+    assert L.wq_awq_search(FAKE_MIS, FAKE, 64, 32, 256, 4, 128, 0, 20, lp, None, FAKE, 1 << 30, None) == WQ_ERR_ARG
+    assert L.wq_awq_search(FAKE, FAKE, 64, 32, 256, 5, 128, 0, 20, lp, None, FAKE, 1 << 30, None) == WQ_ERR_UNSUPPORTED
+    need = size(64, 32, 256, 4, 128, 20)
+    assert L.wq_awq_search(FAKE, FAKE, 64, 32, 256, 4, 128, 0, 20, lp, None, FAKE, need - 1, None) == WQ_ERR_ARG
 
 
 def test_gemv_rejects_large_m():

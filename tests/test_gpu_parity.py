@@ -318,3 +318,44 @@ def test_prefill_awq_gemm_sampled():
 def test_70b_layer_shapes_sampled(K, N):
     sampled_check((4, K, N), K, N, 0.015, (1, 8, 32, 512),
                   lambda M: ("linear", "gemv", "gemm") if M <= 16 else ("linear", "gemm"))
+
+
+# ------------------------------------------------------------ AWQ search ----
+
+@pytest.mark.parametrize("M,N,K,bits,gs,sym", [(64, 96, 512, 4, 128, False), (256, 256, 1024, 4, 128, False),
+                                              (48, 40, 256, 3, 32, True), (32, 24, 256, 8, -1, True)])
+def test_awq_search_matches_oracle(M, N, K, bits, gs, sym):
+    # Every grid point's loss against the float64 oracle (the GPU sums fp32
+    # matrix-core products, so losses agree to a relative 2e-3), and the
+    # chosen alpha is a minimum of the oracle's losses within that tolerance.
+    seed = (109, M, N, K)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    alphas_o, losses_o, best_o = O.awq_search(x, w, bits, gs, n_grid=20, symmetric=sym)
+    alphas, losses, best = wq.awq_search(dev(x), dev(w), bits, gs, n_grid=20, symmetric=sym)
+    assert np.allclose(alphas, alphas_o, rtol=0, atol=1e-15)
+    losses = np.asarray(losses)
+    assert np.all(np.isfinite(losses)) and np.all(losses > 0)
+    rel = np.abs(losses - losses_o) / losses_o
+    assert rel.max() <= 2e-3, (rel.max(), int(np.argmax(rel)))
+    assert best == int(np.argmin(losses))
+    assert losses_o[best] <= losses_o[best_o] * (1 + 4e-3), (best, best_o)
+
+
+def test_awq_search_then_quantize_prefill():
+    # The search on prefill-shaped calibration data (outlier channels) picks
+    # a rescaling that beats plain RTN, and quantizing with the chosen alpha
+    # reproduces the oracle's codes for sampled rows.
+    M, N, K = 512, 1024, 4096
+    seed = (110,)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    alphas, losses, best = wq.awq_search(dev(x), dev(w), 4, 128)
+    assert best > 0 and losses[best] < losses[0]
+    s_d = wq.awq_scales(dev(x), alphas[best])
+    _, s_h = O.awq_channel_scales(x, alphas[best])
+    assert np.array_equal(host(s_d).view(np.uint16), s_h.view(np.uint16))
+    rows = np.array([0, 7, 511, N - 1])
+    codes, _, _ = wq.quantize_rtn(wq.awq_fold(dev(w), s_d), 4, 128)
+    ref = O.rtn_quantize(O.awq_fold_weight(w[rows], s_h), 4, 128)
+    assert np.array_equal(host(codes)[rows], ref[0])

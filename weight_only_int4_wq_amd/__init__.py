@@ -16,7 +16,7 @@ import re
 
 __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
-    "quantize_rtn", "awq_scales", "awq_fold", "act_order_perm", "pack", "unpack",
+    "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "act_order_perm", "pack", "unpack",
     "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_max_m",
     "status_str", "version", "QuantizedLinear",
 ]
@@ -42,6 +42,9 @@ _SIG = {
     "wq_scale_act": (ctypes.c_int, [_VP, _VP, _I32, _I32, _VP, _VP]),
     "wq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
     "wq_gemv_max_m": (_I32, []),
+    "wq_awq_search": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP,
+                                     ctypes.c_size_t, _VP]),
+    "wq_awq_search_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
 }
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
     _SIG[_name] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
@@ -170,6 +173,30 @@ def awq_fold(w, s, out=None):
     out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2)
     _check(lib().wq_awq_fold(_ptr(w), _ptr(s), N, K, _ptr(out), _stream(w.device)), "wq_awq_fold")
     return out
+
+
+def awq_search(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, symmetric: bool = False):
+    """AWQ's grid search for alpha on calibration activations x fp16 [M][K]
+    and weights w fp16 [N][K].  Returns (alphas list, losses list, best
+    index); alpha_i = i / (n_grid - 1).  Synchronizes the stream."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    w = _dev(w, torch.float16, "w", 2)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N][K] with the K of x")
+    need = int(lib().wq_awq_search_workspace_size(M, N, K, bits, group_size, n_grid))
+    if need == 0:
+        raise ValueError("invalid AWQ search arguments")
+    ws = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    losses = (ctypes.c_double * n_grid)()
+    best = ctypes.c_int32(-1)
+    _check(lib().wq_awq_search(_ptr(x), _ptr(w), M, N, K, bits, group_size, int(bool(symmetric)), n_grid,
+                               ctypes.cast(losses, _VP), ctypes.cast(ctypes.byref(best), _VP), _ptr(ws), need,
+                               _stream(x.device)), "wq_awq_search")
+    alphas = [i / (n_grid - 1) for i in range(n_grid)]
+    return alphas, list(losses), int(best.value)
 
 
 def act_order_perm(g_idx, group_size: int):

@@ -46,15 +46,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     constexpr int ROW_BYTES = BK * 2;          // 16 units of 16 bytes
     constexpr int A_INSTR = BM / 16;           // 1 KB copies per wavefront per stage
     static_assert(TM >= 1 && TN >= 1 && A_INSTR >= 1, "tile shape");
-    static_assert(NST >= 2 && (NST - 2) * A_INSTR < 64, "pipeline depth");
-
-    // Three activation buffers (separate LDS objects, indexed at compile
-    // time, so the compiler can tell a copy into one from reads of another):
-    // stage s lives in buffer s % 3 and its copy is issued 2 stages ahead.
-    static_assert(NST == 3, "three activation buffers");
-    __shared__ __attribute__((aligned(1024))) uint8_t As0[BM * ROW_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t As1[BM * ROW_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t As2[BM * ROW_BYTES];
+    // NST activation buffers and weight register sets: stage s lives in
+    // buffer and set s % NST, and its loads are issued NST - 1 stages ahead
+    // (indices are compile-time after unrolling, so the compiler can tell a
+    // copy into one buffer from reads of another).
+    constexpr int AHEAD = NST - 1;
+    static_assert(NST >= 3 && NST <= 8, "pipeline depth");
+    __shared__ __attribute__((aligned(1024))) uint8_t As[NST][BM * ROW_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -127,16 +125,17 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     // Per-lane vector-memory instructions of one issue_b (at least: a
     // 3-bit chunk may be fetched by one dwordx3 load).
     constexpr int B_OPS = TN * ((BITS == 8 ? 2 : 1) + 1 + (HAS_Z ? 1 : 0));
+    static_assert((AHEAD - 1) * (B_OPS + A_INSTR) < 64, "vmcnt range");
 
-    // One stage: wait for its data, start the copies two stages ahead,
+    // One stage: wait for its data, start the loads AHEAD stages ahead,
     // multiply.  Stage s's weights and activations were issued at the top of
-    // stage s - 2 (in that order), so only the copies issued at the top of
-    // stage s - 1 may still be outstanding.
+    // stage s - AHEAD (in that order), so only the loads issued at the tops
+    // of the AHEAD - 1 stages since may still be outstanding.
     auto stage = [&](int st, const BRegs& cur, BRegs& nxt, uint8_t* Ab, uint8_t* An) {
-        copy_barrier<B_OPS + A_INSTR>();
-        issue_b(nxt, (st + 2) * BK);
+        copy_barrier<(AHEAD - 1) * (B_OPS + A_INSTR)>();
+        issue_b(nxt, (st + AHEAD) * BK);
         __builtin_amdgcn_sched_barrier(0);
-        issue_a(An, (st + 2) * BK);
+        issue_a(An, (st + AHEAD) * BK);
         __builtin_amdgcn_sched_barrier(0);
 
         uint32_t zz[TN], ss[TN];
@@ -185,27 +184,27 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
         }
     };
 
-    // Stage s uses weight register set s % 3 and activation buffer s % 3
-    // (both addressed at compile time: the loop is unrolled by 3).  The
-    // prologue issues stages 0 and 1; past the last stage the copies reread
-    // in-range data into buffers that are not read again.
-    BRegs b0, b1, b2;
-    issue_b(b0, st_begin * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(As0, st_begin * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(b1, (st_begin + 1) * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(As1, (st_begin + 1) * BK);
-    __builtin_amdgcn_sched_barrier(0);
-    int st = st_begin;
-    for (; st + 3 <= st_end; st += 3) {
-        stage(st, b0, b2, As0, As2);
-        stage(st + 1, b1, b0, As1, As0);
-        stage(st + 2, b2, b1, As2, As1);
+    // Stage st_begin + i uses weight register set i % NST and activation
+    // buffer i % NST (both addressed at compile time: the loop is unrolled
+    // by NST).  The prologue issues the first AHEAD stages; past the range
+    // the loads reread in-range data (or chunk 0 past K, with zero weight)
+    // into buffers and sets that are not read again.
+    BRegs b[NST];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) {
+        issue_b(b[i], (st_begin + i) * BK);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(As[i], (st_begin + i) * BK);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    if (st < st_end) stage(st, b0, b2, As0, As2);
-    if (st + 1 < st_end) stage(st + 1, b1, b0, As1, As0);
+    int st = st_begin;
+    for (; st + NST <= st_end; st += NST) {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) stage(st + i, b[i], b[(i + AHEAD) % NST], As[i], As[(i + AHEAD) % NST]);
+    }
+#pragma unroll
+    for (int i = 0; i < NST - 1; ++i)
+        if (st + i < st_end) stage(st + i, b[i], b[(i + AHEAD) % NST], As[i], As[(i + AHEAD) % NST]);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -266,16 +265,18 @@ wqh::SplitPlan tile_plan(int M, int N, int K, int bits, size_t ws_avail) {
     return wqh::plan_split(M, N, K, bits, BM, BN, tiles, wqh::gemm_slots(small_tile_blocks_per_cu(BM)), ws_avail);
 }
 
+// With out32 the product is written unrounded as fp32 [M][N] (no split).
 template <int BITS, int BM, int BN, int WAVES_M, int NST>
 wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                      uint16_t* y, int M, int N, int K, int gs, float* part, size_t part_bytes, hipStream_t s) {
+                      uint16_t* y, int M, int N, int K, int gs, float* part, size_t part_bytes, float* out32,
+                      hipStream_t s) {
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
-    const wqh::SplitPlan plan = tile_plan<BM, BN>(M, N, K, BITS, part ? part_bytes : 0);
+    const wqh::SplitPlan plan = tile_plan<BM, BN>(M, N, K, BITS, (part && !out32) ? part_bytes : 0);
     const bool split = plan.splits > 1;
     const dim3 grid(tiles, plan.splits);
-    float* pp = split ? part : nullptr;
+    float* pp = out32 ? out32 : (split ? part : nullptr);
     if (zeros)
         hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true>), grid, dim3(256), 0, s, x, packed, scales,
                            zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
@@ -293,6 +294,12 @@ wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t*
 // once per 256 output columns.  Any of them splits K across blocks when there
 // are too few tiles to fill the machine and the workspace holds the partials.
 enum class TileKind { k16, k32, k64, kLarge, k128 };
+
+// Pipeline depth (stages in flight + 1) of the small-M tiles.
+#ifndef WQ_GEMM_SMALL_NST
+#define WQ_GEMM_SMALL_NST 3
+#endif
+constexpr int kSmallNst = WQ_GEMM_SMALL_NST;
 
 inline TileKind tile_kind(int M, int N, int K, int bits) {
     if (M <= 16) return TileKind::k16;
@@ -318,20 +325,25 @@ inline size_t split_bytes(int M, int N, int K, int bits) {
 
 template <int BITS>
 wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                      uint16_t* y, int M, int N, int K, int gs, float* part, size_t part_bytes, hipStream_t s) {
+                      uint16_t* y, int M, int N, int K, int gs, float* part, size_t part_bytes, hipStream_t s,
+                      float* out32 = nullptr) {
     switch (tile_kind(M, N, K, BITS)) {
         case TileKind::k16:
-            return launch_tile<BITS, 16, 128, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+            return launch_tile<BITS, 16, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
+                                                            out32, s);
         case TileKind::k32:
-            return launch_tile<BITS, 32, 128, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+            return launch_tile<BITS, 32, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
+                                                            out32, s);
         case TileKind::k64:
-            return launch_tile<BITS, 64, 128, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+            return launch_tile<BITS, 64, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
+                                                            out32, s);
         case TileKind::kLarge: {
-            const wqh::SplitPlan plan = wqh::gemm_large_plan(M, N, K, BITS, part ? part_bytes : 0);
-            return wqh::gemm_large(BITS, x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+            const wqh::SplitPlan plan = wqh::gemm_large_plan(M, N, K, BITS, (part && !out32) ? part_bytes : 0);
+            return wqh::gemm_large(BITS, x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
         }
         default:
-            return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes, s);
+            return launch_tile<BITS, 128, 256, 1, 3>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
+                                                            out32, s);
     }
 }
 
@@ -359,6 +371,16 @@ wq_status splitk_reduce(const float* part, int splits, int M, int N, uint16_t* y
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(int(blocks)), dim3(256), 0, s, part, splits, mn, y);
     return launch_status();
+}
+
+wq_status gemm_f32(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                   float* y32, int M, int N, int K, int bits, int gs, hipStream_t s) {
+    switch (bits) {
+        case 2: return launch_bits<2>(x, packed, scales, zeros, nullptr, M, N, K, gs, nullptr, 0, s, y32);
+        case 3: return launch_bits<3>(x, packed, scales, zeros, nullptr, M, N, K, gs, nullptr, 0, s, y32);
+        case 4: return launch_bits<4>(x, packed, scales, zeros, nullptr, M, N, K, gs, nullptr, 0, s, y32);
+        default: return launch_bits<8>(x, packed, scales, zeros, nullptr, M, N, K, gs, nullptr, 0, s, y32);
+    }
 }
 
 }  // namespace wqh

@@ -127,8 +127,14 @@ bool gemm_large_fits(int M, int N, int K, int bits);
 // Split plan of the large-M kernel for these arguments (ws_avail: bytes of
 // workspace available for partials).
 SplitPlan gemm_large_plan(int M, int N, int K, int bits, size_t ws_avail);
+// With out32 the unrounded product goes to fp32 [M][N] instead of y (no split).
 wq_status gemm_large(int bits, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                      const uint8_t* zeros, uint16_t* y, int M, int N, int K, int gs, SplitPlan plan,
-                     float* part, hipStream_t s);
+                     float* part, float* out32, hipStream_t s);
+
+// The GEMM with the unrounded fp32 product y32 [M][N] as output (inputs
+// already checked by the caller; packed column order = original order).
+wq_status gemm_f32(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                   float* y32, int M, int N, int K, int bits, int gs, hipStream_t s);
 
 }  // namespace wqh

@@ -343,15 +343,17 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
 
 template <int BITS, bool HAS_Z>
 wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                   uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, hipStream_t s) {
+                   uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, float* out32,
+                   hipStream_t s) {
     constexpr int BM = 128, BN = 256;
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
     const bool fast = (K % 128 == 0) && (gs % 128 == 0);
+    if (out32) plan = wqh::SplitPlan{1, (K + 127) / 128};
     const bool split = plan.splits > 1;
     const dim3 grid(tiles, plan.splits);
-    float* pp = split ? part : nullptr;
+    float* pp = out32 ? out32 : (split ? part : nullptr);
     if (fast)
         hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true>), grid, dim3(256), 0, s, x, packed, scales, zeros, y,
                            M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
@@ -365,9 +367,10 @@ wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* sc
 
 template <int BITS>
 wq_status launch_large(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                       uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, hipStream_t s) {
-    if (zeros) return launch_z<BITS, true>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
-    return launch_z<BITS, false>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+                       uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, float* out32,
+                       hipStream_t s) {
+    if (zeros) return launch_z<BITS, true>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+    return launch_z<BITS, false>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
 }
 
 }  // namespace
@@ -389,12 +392,12 @@ SplitPlan gemm_large_plan(int M, int N, int K, int bits, size_t ws_avail) {
 
 wq_status gemm_large(int bits, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                      const uint8_t* zeros, uint16_t* y, int M, int N, int K, int gs, SplitPlan plan, float* part,
-                     hipStream_t s) {
+                     float* out32, hipStream_t s) {
     switch (bits) {
-        case 2: return launch_large<2>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
-        case 3: return launch_large<3>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
-        case 4: return launch_large<4>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
-        default: return launch_large<8>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, s);
+        case 2: return launch_large<2>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+        case 3: return launch_large<3>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+        case 4: return launch_large<4>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+        default: return launch_large<8>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
     }
 }
 
