@@ -52,10 +52,11 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq"], default=None,
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
                         "copies of a known size, the reference for scaling HBM byte counters; "
-                        "'configs' times every case of the five synthetic workloads")
+                        "'configs' times every case of the five synthetic workloads; 'awq' times "
+                        "AWQ's alpha search on the prefill layer")
     return p.parse_args()
 
 
@@ -325,6 +326,39 @@ def configs_leg(wq, torch, launches):
     return rows
 
 
+def awq_leg(wq, torch, repeats, cpu):
+    """AWQ's alpha search (20 grid points) on the prefill layer's calibration
+    batch: M = 2048, K = 4096, N = 11008, 1% outlier channels x20, 4-bit,
+    group 128.  The search synchronizes, so it is timed by the wall clock
+    around whole searches.  With cpu, the oracle's search on a sample of the
+    layer's output columns, timed the same way."""
+    M, K, N = PREFILL["M"], PREFILL["K"], PREFILL["N"]
+    seed = (3, 1)
+    x_np = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w_np = I.weights(seed, N, K, 0.02)
+    x, w = torch.from_numpy(x_np).cuda(), torch.from_numpy(w_np).cuda()
+    alphas, losses, best = wq.awq_search(x, w, BITS, GROUP)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        alphas, losses, best = wq.awq_search(x, w, BITS, GROUP)
+    gpu_s = (time.perf_counter() - t0) / repeats
+    out = dict(leg="awq_search", workload="prefill-awq-w4g128 calibration: M=2048 K=4096 N=11008, 20 alphas",
+               gpu_ms_per_search=round(gpu_s * 1e3, 2), gpu_ms_per_alpha=round(gpu_s * 1e3 / len(alphas), 3),
+               gpu_columns_per_s=round(N / gpu_s, 1), best_alpha=round(alphas[best], 4),
+               loss_best_over_rtn=round(losses[best] / losses[0], 4))
+    if cpu:
+        import oracle as O
+        cols = 32
+        t0 = time.perf_counter()
+        a_o, l_o, b_o = O.awq_search(x_np, w_np[:cols], BITS, GROUP)
+        cpu_s = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(kind="oracle", sample=f"{cols} output columns of the same layer, full M and K, "
+                                                          f"20 alphas", seconds=round(cpu_s, 2),
+                                   columns_per_s=round(cols / cpu_s, 2), best_alpha=round(float(a_o[b_o]), 4))
+    return out
+
+
 # -------------------------------------------------------- CPU baseline ----
 
 def cpu_baseline(target_s):
@@ -392,6 +426,9 @@ def main():
     if args.only == "decode":
         dec = decode_leg(wq, torch, args.steps, args.warmup)
         print(json.dumps({"leg": "decode", "ms_per_step": dec["ms"], "per_layer": dec["per_layer"]}), flush=True)
+        return
+    if args.only == "awq":
+        print(json.dumps(awq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)
         return
     if args.only == "configs":
         configs_leg(wq, torch, max(args.steps, 1))

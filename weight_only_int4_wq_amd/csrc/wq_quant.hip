@@ -89,14 +89,98 @@ __global__ void __launch_bounds__(256) rtn_kernel(const uint16_t* __restrict__ w
     }
 }
 
+// Same quantizer, one block per output row, for the common case without a
+// group permutation: (1) 16-byte loads of 8 weights record each 8-weight
+// unit's min and max in LDS; (2) one thread per group reduces its units and
+// derives scale and zero exactly as rtn_kernel does; (3) every unit is read
+// again (from cache) and its 8 codes written as 8 bytes.  Same arithmetic,
+// same results, bit for bit.
+template <int BITS, bool SYM>
+__global__ void __launch_bounds__(256) rtn_row_kernel(const uint16_t* __restrict__ w, int K, int gs,
+                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                      uint8_t* __restrict__ zeros) {
+    constexpr int qmax = (1 << BITS) - 1;
+    extern __shared__ float rtn_lds[];
+    const int U = K / 8, G = K / gs, upg = gs / 8;
+    float* umin = rtn_lds;
+    float* umax = rtn_lds + U;
+    float* gsc = rtn_lds + 2 * U;
+    float* gz = gsc + G;
+    const int n = blockIdx.x;
+    const u4* row = reinterpret_cast<const u4*>(w + (size_t)n * K);
+    for (int u = threadIdx.x; u < U; u += 256) {
+        const u4 v = row[u];
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = h2f(uint16_t(in[i])), b = h2f(uint16_t(in[i] >> 16));
+            mn = fminf(mn, fminf(a, b));
+            mx = fmaxf(mx, fmaxf(a, b));
+        }
+        umin[u] = mn;
+        umax[u] = mx;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < G; j += 256) {
+        float mn = INFINITY, mx = -INFINITY;
+        for (int u = j * upg; u < (j + 1) * upg; ++u) {
+            mn = fminf(mn, umin[u]);
+            mx = fmaxf(mx, umax[u]);
+        }
+        const float amax = fmaxf(fabsf(mn), fabsf(mx));
+        const float s32 = SYM ? __fdiv_rn(2.0f * amax, float(qmax)) : __fdiv_rn(mx - mn, float(qmax));
+        uint16_t sh = f2h(s32);
+        if ((sh & 0x7FFFu) == 0) sh = 0x0400u;  // 2^-14
+        const float sc = h2f(sh);
+        float z;
+        if (SYM) {
+            z = float(1 << (BITS - 1));
+        } else {
+            z = fminf(fmaxf(rintf(__fdiv_rn(-mn, sc)), 0.f), float(qmax));
+            zeros[(size_t)n * G + j] = uint8_t(z);
+        }
+        scales[(size_t)n * G + j] = sh;
+        gsc[j] = sc;
+        gz[j] = z;
+    }
+    __syncthreads();
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    u2* crow = reinterpret_cast<u2*>(codes + (size_t)n * K);
+    for (int u = threadIdx.x; u < U; u += 256) {
+        const u4 v = row[u];
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        const int j = u / upg;
+        const float sc = gsc[j], z = gz[j];
+        uint32_t q[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            q[2 * i] = uint32_t(fminf(fmaxf(rintf(__fdiv_rn(h2f(uint16_t(in[i])), sc)) + z, 0.f), float(qmax)));
+            q[2 * i + 1] =
+                uint32_t(fminf(fmaxf(rintf(__fdiv_rn(h2f(uint16_t(in[i] >> 16)), sc)) + z, 0.f), float(qmax)));
+        }
+        crow[u] = u2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24), q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+    }
+}
+
 // --------------------------------------------------------------- AWQ ----
-// One thread per input channel k: float64 sum of |x| down the column.
-__global__ void __launch_bounds__(256) awq_scales_kernel(const uint16_t* __restrict__ x, int M, int K,
-                                                         double alpha, uint16_t* __restrict__ s_out) {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= K) return;
+// Float64 mean of |x| down each input channel.  A block owns 64 channels
+// and 1024 threads: thread (c, r) = (t % 64, t / 64) sums rows r, r + 16,
+// ... of channel c (a wavefront reads 64 consecutive channels of one row),
+// then the 16 partial sums of a channel are added in phase order.
+__global__ void __launch_bounds__(1024) awq_scales_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                          double alpha, uint16_t* __restrict__ s_out) {
+    __shared__ double part[16][64];
+    const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
+    const int k = blockIdx.x * 64 + c;
     double acc = 0.0;
-    for (int m = 0; m < M; ++m) acc += fabs(double(h2f(x[(size_t)m * K + k])));
+    if (k < K)
+        for (int m = r; m < M; m += 16) acc += fabs(double(h2f(x[(size_t)m * K + k])));
+    part[r][c] = acc;
+    __syncthreads();
+    if (r != 0 || k >= K) return;
+    acc = part[0][c];
+    for (int i = 1; i < 16; ++i) acc += part[i][c];
     const double a = acc / double(M);
     const double s = (alpha == 0.5) ? sqrt(a) : pow(a, alpha);
     uint16_t h = f64_to_f16_rne(s);
@@ -146,6 +230,18 @@ int grid_for(long long work, int block, long long cap = 65536) {
 template <int BITS>
 wq_status launch_rtn(const uint16_t* w, const int32_t* perm, int N, int K, int gs, bool sym, uint8_t* codes,
                      uint16_t* scales, uint8_t* zeros, hipStream_t s) {
+    // per-row kernel: no permutation, 16-byte weight rows, 8-byte code rows,
+    // unit and group tables within 64 KB of LDS
+    const size_t lds = size_t(K / 8) * 8 + size_t(K / gs) * 8;
+    if (!perm && wqh::aligned16(w) && (reinterpret_cast<uintptr_t>(codes) & 7u) == 0 && lds <= 65536) {
+        if (sym)
+            hipLaunchKernelGGL((rtn_row_kernel<BITS, true>), dim3(N), dim3(256), lds, s, w, K, gs, codes, scales,
+                               zeros);
+        else
+            hipLaunchKernelGGL((rtn_row_kernel<BITS, false>), dim3(N), dim3(256), lds, s, w, K, gs, codes, scales,
+                               zeros);
+        return wqh::launch_status();
+    }
     const long long work = (long long)N * (K / gs);
     const dim3 grid(grid_for(work, 256)), block(256);
     if (sym)
@@ -178,7 +274,7 @@ extern "C" wq_status wq_awq_scales(const uint16_t* x, int32_t M, int32_t K, doub
                                    void* stream) {
     if (!x || !s_out || M <= 0 || K <= 0) return WQ_ERR_ARG;
     if (!(alpha >= 0.0 && alpha <= 1.0)) return WQ_ERR_ARG;
-    hipLaunchKernelGGL(awq_scales_kernel, dim3((K + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+    hipLaunchKernelGGL(awq_scales_kernel, dim3((K + 63) / 64), dim3(1024), 0, static_cast<hipStream_t>(stream), x,
                        int(M), int(K), alpha, s_out);
     return wqh::launch_status();
 }
