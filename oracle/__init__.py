@@ -20,6 +20,7 @@ from .wq_oracle import (  # noqa: F401
     awq_scale_act,
     awq_search,
     linear_ref,
+    silu_mul_ref,
     quantize_linear_layer,
     f64_to_f16_nearest,
 )

@@ -267,6 +267,27 @@ def linear_ref(x, w_hat, chunk: int = 8192) -> np.ndarray:
     return y
 
 
+def silu_mul_ref(x, w_hat) -> np.ndarray:
+    """Fused gate/up projection with its activation, in float64.
+
+    w_hat holds the two projections stacked, 2I rows: rows [0, I) the gate,
+    rows [I, 2I) the up projection.  With g = x . W_gate^T and u = x . W_up^T
+    (exact float64 sums), y = silu(g) * u, silu(v) = v / (1 + e^-v).  The
+    pages describe fusing several of a block's operations into one kernel to
+    cut launches and intermediate tensors ("AutoAWQ vs The Stack v2",
+    paragraph on fused transformer blocks); which operations, and SiLU as
+    the gate's activation, is the reading taken (the gated MLP of the
+    LLaMA-shaped layers the workloads use).
+    """
+    y = linear_ref(x, w_hat)
+    two_i = y.shape[1]
+    if two_i % 2:
+        raise ValueError("the stacked gate/up weight needs an even row count")
+    half = two_i // 2
+    g, u = y[:, :half], y[:, half:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
 def quantize_linear_layer(w, bits: int, group_size: int, g_idx=None, symmetric: bool = False):
     """RTN-quantize w[N][K] and pack it the way the packed format stores it.
 

@@ -389,6 +389,42 @@ def test_awq_search_prefers_rescaling_on_outlier_channels():
     assert losses[best] < 0.8 * losses[0]
 
 
+# ------------------------------------------------------- fused gate / up
+
+def test_silu_mul_closed_forms():
+    # y = silu(g) * u with g, u the two halves of one stacked product: pick
+    # x and w so that g and u are known numbers.  silu(0) = 0, silu(1) =
+    # 1 / (1 + 1/e), silu(-1) = -1 / (1 + e), and u scales the result.
+    K = 32
+    x = np.zeros((1, K), dtype=np.float16)
+    x[0, 0] = 1.0
+    w = np.zeros((6, K), dtype=np.float16)
+    w[0, 0], w[1, 0], w[2, 0] = 0.0, 1.0, -1.0     # gate values 0, 1, -1
+    w[3, 0], w[4, 0], w[5, 0] = 5.0, 2.0, 3.0      # up values
+    y = O.silu_mul_ref(x, w)
+    e = np.e
+    assert y.shape == (1, 3)
+    assert y[0, 0] == 0.0
+    assert np.isclose(y[0, 1], 2.0 / (1.0 + 1.0 / e), rtol=1e-15)
+    assert np.isclose(y[0, 2], -3.0 / (1.0 + e), rtol=1e-15)
+
+
+def test_silu_mul_halves_follow_the_stacking():
+    # swapping the gate and up halves changes the result (the gate goes
+    # through silu, the up projection does not)
+    seed = (47,)
+    x = I.activations(seed, 2, 64)
+    w = I.weights(seed, 8, 64, 0.5)
+    y = O.silu_mul_ref(x, w)
+    g = x.astype(np.float64) @ w[:4].astype(np.float64).T
+    u = x.astype(np.float64) @ w[4:].astype(np.float64).T
+    assert np.allclose(y, g * u / (1 + np.exp(-g)), rtol=1e-12, atol=0)
+    swapped = O.silu_mul_ref(x, np.concatenate([w[4:], w[:4]]))
+    assert not np.allclose(swapped, y)
+    with pytest.raises(ValueError):
+        O.silu_mul_ref(x, w[:7])
+
+
 # ------------------------------------------------------------------ matmul
 
 def test_linear_matches_bruteforce_triple_loop():
