@@ -52,11 +52,11 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq", "silu"], default=None,
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
                         "copies of a known size, the reference for scaling HBM byte counters; "
                         "'configs' times every case of the five synthetic workloads; 'awq' times "
-                        "AWQ's alpha search on the prefill layer")
+                        "AWQ's alpha search on the prefill layer; 'silu' the fused gate/up decode projection")
     return p.parse_args()
 
 
@@ -326,6 +326,44 @@ def configs_leg(wq, torch, launches):
     return rows
 
 
+def silu_leg(wq, torch, steps):
+    """Fused gate/up + SiLU decode projection (K = 4096, 2 x 11008 rows,
+    M = 1, 4-bit, group 128): one wq_gemv_silu_mul launch against the plain
+    GEMV of the stacked weight followed by torch's silu(g) * u, both over a
+    rotating pool of weight copies in graph replays."""
+    K, N = 4096, 22016
+    w = torch.from_numpy(I.weights((2, K, N), N, K, 0.02)).cuda()
+    L = wq.QuantizedLinear.from_float(w, bits=BITS, group_size=GROUP)
+    del w
+    x = torch.from_numpy(I.activations((2, K, N), 1, K)).cuda()
+    per_copy = L.packed.numel() * 4 + L.scales.numel() * 3
+    copies = max(2, -(-POOL_BYTES // per_copy))
+    pool = [(L.packed, L.scales, L.zeros)] + [(L.packed.clone(), L.scales.clone(), L.zeros.clone())
+                                              for _ in range(copies - 1)]
+    y_full = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    y_half = torch.empty((1, N // 2), dtype=torch.float16, device="cuda")
+
+    def fused(i):
+        p, sc, z = pool[i]
+        wq.gemv_silu_mul(x, p, sc, z, BITS, GROUP, out=y_half)
+
+    def plain(i):
+        p, sc, z = pool[i]
+        wq.gemv(x, p, sc, z, BITS, GROUP, out=y_full)
+
+    def unfused(i):
+        plain(i)
+        g, u = y_full[:, :N // 2], y_full[:, N // 2:]
+        torch.mul(torch.nn.functional.silu(g), u, out=y_half)
+
+    res = {}
+    for name, fn in (("fused_us", fused), ("gemv_only_us", plain), ("gemv_then_torch_silu_mul_us", unfused)):
+        res[name] = round(timed(torch, fn, copies, max(steps, copies), copies) * 1e3, 3)
+    packed_b = N * K * BITS // 8
+    res["fused_packed_GBs"] = round(packed_b / (res["fused_us"] * 1e-6) / 1e9, 1)
+    return dict(leg="gate_up_silu", workload="llama7b gate+up 4096x(2x11008), M=1, 4-bit g128", **res)
+
+
 def awq_leg(wq, torch, repeats, cpu):
     """AWQ's alpha search (20 grid points) on the prefill layer's calibration
     batch: M = 2048, K = 4096, N = 11008, 1% outlier channels x20, 4-bit,
@@ -426,6 +464,9 @@ def main():
     if args.only == "decode":
         dec = decode_leg(wq, torch, args.steps, args.warmup)
         print(json.dumps({"leg": "decode", "ms_per_step": dec["ms"], "per_layer": dec["per_layer"]}), flush=True)
+        return
+    if args.only == "silu":
+        print(json.dumps(silu_leg(wq, torch, max(args.steps, 200))), flush=True)
         return
     if args.only == "awq":
         print(json.dumps(awq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)

@@ -212,6 +212,23 @@ wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const uint16_t* s
                     int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Fused gate/up projection with its activation, for decode batches
+ * (1 <= M <= 4): the N rows of packed/scales/zeros are a gate projection
+ * (rows 0 .. N/2-1) stacked over an up projection (rows N/2 .. N-1), and
+ *   y fp16 [M][N/2]: y[m][j] = fp16(silu(g) * u),  silu(v) = v / (1 + e^-v),
+ * with g, u the fp32-accumulated rows j and j + N/2 of x . dequant(packed)^T.
+ * One launch of the decode GEMV with a fused epilogue instead of a GEMV
+ * writing both halves plus an elementwise pass ("AutoAWQ vs The Stack v2",
+ * paragraph on fused transformer blocks: fewer launches, no intermediate
+ * tensor; SiLU as the gate activation is the gated MLP of LLaMA-shaped
+ * layers).  Same argument rules as wq_gemv; N must be even (WQ_ERR_ARG),
+ * WQ_ERR_UNSUPPORTED for M > 4 or when x's rows do not fit the kernel's
+ * 64 KB activation stage (K up to about 16k at M = 1). */
+wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                           const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                           int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
+                           void* stream);
+
 /* Largest M that wq_linear sends to wq_gemv. */
 int32_t wq_gemv_max_m(void);
 

@@ -18,7 +18,7 @@ def test_library_exports_every_declared_symbol():
     expected = {"wq_status_str", "wq_version", "wq_quantize_rtn", "wq_awq_scales", "wq_awq_fold",
                 "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
                 "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m",
-                "wq_awq_search", "wq_awq_search_workspace_size"}
+                "wq_awq_search", "wq_awq_search_workspace_size", "wq_gemv_silu_mul"}
     assert set(names) == expected
     handle = wq.lib()
     for name in names:
@@ -94,6 +94,16 @@ def test_awq_search_argument_checks():
     assert L.wq_awq_search(FAKE, FAKE, 64, 32, 256, 5, 128, 0, 20, lp, None, FAKE, 1 << 30, None) == WQ_ERR_UNSUPPORTED
     need = size(64, 32, 256, 4, 128, 20)
     assert L.wq_awq_search(FAKE, FAKE, 64, 32, 256, 4, 128, 0, 20, lp, None, FAKE, need - 1, None) == WQ_ERR_ARG
+
+
+def test_gemv_silu_mul_argument_checks():
+    L = wq.lib()
+    f = L.wq_gemv_silu_mul
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 1, 63, 128, 4, 128, None) == WQ_ERR_ARG       # odd N
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 5, 64, 128, 4, 128, None) == WQ_ERR_UNSUPPORTED
+    assert f(None, FAKE, FAKE, None, None, FAKE, 1, 64, 128, 4, 128, None) == WQ_ERR_ARG
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 1, 64, 128, 5, 128, None) == WQ_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, None, None, FAKE, 0, 64, 128, 4, 128, None) == WQ_OK
 
 
 def test_gemv_rejects_large_m():

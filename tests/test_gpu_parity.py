@@ -359,3 +359,38 @@ def test_awq_search_then_quantize_prefill():
     codes, _, _ = wq.quantize_rtn(wq.awq_fold(dev(w), s_d), 4, 128)
     ref = O.rtn_quantize(O.awq_fold_weight(w[rows], s_h), 4, 128)
     assert np.array_equal(host(codes)[rows], ref[0])
+
+
+# ------------------------------------------------- fused gate/up + SiLU ----
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits,gs,sym,act,I_,K", [(4, 128, False, False, 100, 4096), (4, 128, False, True, 64, 1024),
+                                                 (3, 32, True, False, 40, 512), (8, -1, True, False, 33, 256)])
+def test_gemv_silu_mul_matches_oracle(M, bits, gs, sym, act, I_, K):
+    seed = (111, M, bits, I_, K)
+    w = I.weights(seed, 2 * I_, K, 0.02)
+    g_idx = I.act_order_gidx(seed, K, gs) if act else None
+    ref = O.quantize_linear_layer(w, bits, gs, g_idx=g_idx, symmetric=sym)
+    L = gpu_layer(w, bits, gs, g_idx, sym=sym)
+    x = I.activations(seed, M, K)
+    y = wq.gemv_silu_mul(dev(x), L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"])
+    check_y(y, O.silu_mul_ref(x, ref["w_hat"]), f"silu_mul M={M} b={bits} g={gs} act={act}")
+
+
+def test_gemv_silu_mul_llama_gate_up_sampled():
+    # the fused 4096 x 22016 gate+up layer: sampled outputs j need gate row
+    # j and up row j + 11008
+    K, N = 4096, 22016
+    half = N // 2
+    seed = (112,)
+    w = I.weights(seed, N, K, 0.02)
+    codes, scales, zeros = wq.quantize_rtn(dev(w), 4, 128)
+    packed, _ = wq.pack(codes, 4)
+    js = np.unique(np.concatenate([[0, half - 1], np.random.default_rng(7).choice(half, 40)]))
+    rows = np.concatenate([js, js + half])
+    ref = O.quantize_linear_layer(w[rows], 4, 128)
+    for M in (1, 4):
+        x = I.activations(seed, M, K)
+        y = wq.gemv_silu_mul(dev(x), packed, scales, zeros, 4, 128)
+        assert y.shape == (M, half)
+        check_y(y[:, torch.from_numpy(js).cuda()], O.silu_mul_ref(x, ref["w_hat"]), f"gate_up M={M}")

@@ -17,7 +17,7 @@ import re
 __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
     "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "act_order_perm", "pack", "unpack",
-    "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_max_m",
+    "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_max_m",
     "status_str", "version", "QuantizedLinear",
 ]
 
@@ -46,6 +46,7 @@ _SIG = {
                                      ctypes.c_size_t, _VP]),
     "wq_awq_search_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
 }
+_SIG["wq_gemv_silu_mul"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
     _SIG[_name] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                                   _VP, ctypes.c_size_t, _VP])
@@ -326,6 +327,27 @@ def gemm(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=No
 def linear(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
     """Batch-size dispatch between gemv and gemm."""
     return _matmul("wq_linear", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
+
+
+def gemv_silu_mul(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None):
+    """Fused gate/up decode projection: packed holds the gate rows stacked
+    over the up rows (N = 2I); returns fp16 [M][I] = silu(gate) * up."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    packed = _dev(packed, torch.int32, "packed", 2)
+    scales = _dev(scales, torch.float16, "scales", 2)
+    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    M, K = x.shape
+    N = packed.shape[0]
+    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
+    if N % 2:
+        raise ValueError("the stacked gate/up weight needs an even row count")
+    y = torch.empty((M, N // 2), dtype=torch.float16, device=x.device) if out is None else \
+        _dev(out, torch.float16, "out", 2)
+    _check(lib().wq_gemv_silu_mul(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(y), M, N, K,
+                                  bits, group_size, _stream(x.device)), "wq_gemv_silu_mul")
+    return y
 
 
 class QuantizedLinear:

@@ -338,7 +338,7 @@ struct WideSlot {
     bool ok[R];
 };
 
-template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER>
+template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER, bool SILU = false>
 __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const uint16_t* __restrict__ x,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
@@ -358,7 +358,12 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int G = chunk_group(CN - 1, gd) + 1;
     const size_t row_words = (size_t)CN * BITS;
-    const int n_groups = (N + R - 1) / R;
+    // With SILU the N rows are a stacked gate (rows [0, N/2)) and up
+    // (rows [N/2, N)) projection: row group g is the pair (g, g + N/2) and
+    // the epilogue writes y[m][g] = silu(gate) * up, N/2 outputs per row.
+    static_assert(!SILU || R == 2, "the fused gate/up epilogue pairs two rows");
+    const int half = N / 2;
+    const int n_groups = SILU ? half : (N + R - 1) / R;
     const int J = (CNP + 63) / 64;  // slot iterations per row group
 
     const int wg0 = blockIdx.x * kStreamWaves + wave;
@@ -378,7 +383,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         const int g = chunk_group(cpc * CPL, gd);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int n = i_rg * R + r;
+            const int n = SILU ? i_rg + r * half : i_rg * R + r;
             const bool nok = tv && n < N;  // wave-uniform
             const int nn = nok ? n : 0;
             sl.ok[r] = valid && nok;
@@ -542,15 +547,29 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
             }
             // ---- end of a row group: reduce across the wavefront and store
             if (c_j == J - 1 && t < T) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int n = c_rg * R + r;
+                if constexpr (SILU) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        const float v = wave_sum_last(acc[r][m]);
-                        acc[r][m] = 0.f;
-                        if (lane == 63 && n < N && m < M)
-                            y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        const float g = wave_sum_last(acc[0][m]);
+                        const float u = wave_sum_last(acc[1][m]);
+                        acc[0][m] = 0.f;
+                        acc[1][m] = 0.f;
+                        if (lane == 63 && m < M) {
+                            const float v = g / (1.0f + expf(-g)) * u;
+                            y[(size_t)m * half + c_rg] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int n = c_rg * R + r;
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            const float v = wave_sum_last(acc[r][m]);
+                            acc[r][m] = 0.f;
+                            if (lane == 63 && n < N && m < M)
+                                y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                        }
                     }
                 }
             }
@@ -613,7 +632,7 @@ inline size_t stream_lds_bytes(int MT, int K, int cpl) {
 #endif
 constexpr int kStreamBlocksPerCU = WQ_GEMV_BPC;
 
-template <int BITS, int MT, int R, int D, int CPL>
+template <int BITS, int MT, int R, int D, int CPL, bool SILU = false>
 wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     int dev = 0, cus = 256;
@@ -621,22 +640,22 @@ wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    const int n_groups = (N + R - 1) / R;
+    const int n_groups = SILU ? N / 2 : (N + R - 1) / R;
     int blocks = (n_groups + kStreamWaves - 1) / kStreamWaves;
     if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
     const size_t lds = stream_lds_bytes(MT, K, CPL);
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros && perm)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
                            packed, scales, zeros, perm, y, M, N, K, gd);
     else if (zeros)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
                            x, packed, scales, zeros, perm, y, M, N, K, gd);
     else if (perm)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
                            x, packed, scales, zeros, perm, y, M, N, K, gd);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
                            x, packed, scales, zeros, perm, y, M, N, K, gd);
     return wqh::launch_status();
 }
@@ -682,6 +701,18 @@ wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t*
     return launch_mt<BITS, 16>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
 }
 
+// Fused gate/up projection with SiLU: the streaming kernel with the paired
+// rows (g, g + N/2) and the silu(gate) * up epilogue.
+template <int BITS>
+wq_status launch_silu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                      const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+    const int MT = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+    if (stream_lds_bytes(MT, K, 1) > kLdsBudget) return WQ_ERR_UNSUPPORTED;
+    if (M <= 1) return launch_stream<BITS, 1, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+    if (M <= 2) return launch_stream<BITS, 2, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+    return launch_stream<BITS, 4, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+}
+
 }  // namespace
 
 namespace wqh {
@@ -705,5 +736,23 @@ extern "C" wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const ui
         case 3: return launch_bits<3>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         case 4: return launch_bits<4>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         default: return launch_bits<8>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+    }
+}
+
+extern "C" wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                                      const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
+                                      int32_t K, int32_t bits, int32_t group_size, void* stream) {
+    int gs = 0;
+    const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
+    if (st != WQ_OK) return st;
+    if (N % 2) return WQ_ERR_ARG;
+    if (M > 4) return WQ_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return WQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (bits) {
+        case 2: return launch_silu<2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        case 3: return launch_silu<3>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        case 4: return launch_silu<4>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+        default: return launch_silu<8>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
     }
 }
