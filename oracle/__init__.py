@@ -19,6 +19,7 @@ from .wq_oracle import (  # noqa: F401
     awq_fold_weight,
     awq_scale_act,
     awq_search,
+    gptq_quantize,
     linear_ref,
     silu_mul_ref,
     quantize_linear_layer,

@@ -24,6 +24,11 @@ What it computes, and where each step comes from:
 * AWQ's search for alpha: a 20-point grid on [0, 1], each point scored by
   the squared output error of the rescaled, quantized layer against the
   original layer on the calibration activations (same section).
+* GPTQ: columns quantized in a fixed order, each rounding error compensated
+  on the remaining columns through the upper Cholesky factor of the
+  inverse Hessian of the layer's reconstruction loss ("GPTQ, AWQ and the
+  rules of post-training quantization", section "GPTQ: pay for the error
+  with the other weights").
 * Packing of codes into 32-bit words, dequantization (q - z) * s and the
   product y = x . dequant(Wq)^T.  Weights stay packed and are dequantized on
   the fly inside the product: "AutoAWQ vs The Stack v2", paragraph on the
@@ -349,6 +354,84 @@ def awq_search(x, w, bits: int, group_size: int, n_grid: int = 20, symmetric: bo
         d = linear_ref(x_f, q["w_hat"]) - y_ref
         losses[i] = np.sum(d * d)
     return alphas, losses, int(np.argmin(losses))
+
+
+def _group_params_f32(wg, bits: int, symmetric: bool):
+    """The RTN rule of rtn_quantize for one group per row, on float32 values
+    wg [N][n]: returns (s_h fp16 [N], z float32 [N])."""
+    qmax = F32((1 << bits) - 1)
+    if symmetric:
+        s32 = (F32(2.0) * np.max(np.abs(wg), axis=1)) / qmax
+    else:
+        mn = np.min(wg, axis=1)
+        s32 = (np.max(wg, axis=1) - mn) / qmax
+    s_h = s32.astype(F16)
+    s_h[s_h == 0] = _SCALE_FLOOR
+    if symmetric:
+        z = np.full(wg.shape[0], F32(1 << (bits - 1)), dtype=F32)
+    else:
+        z = np.clip(np.rint((-mn) / s_h.astype(F32)), F32(0), qmax)
+    return s_h, z
+
+
+def gptq_quantize(w, x, bits: int, group_size: int, symmetric: bool = False, damp: float = 0.01):
+    """GPTQ ("GPTQ, AWQ and the rules of post-training quantization",
+    section "GPTQ: pay for the error with the other weights"): columns are
+    quantized one at a time in a fixed order (index order), and each
+    column's rounding error is compensated on the columns not yet quantized
+    through the inverse Hessian of the layer's reconstruction loss, written
+    with a Cholesky factor.
+
+    H = x^T x (float64; the loss's Hessian up to a factor 2 that cancels).
+    A channel with H[k][k] = 0 gets H[k][k] = 1 and W[:, k] = 0; then
+    H += damp * mean(diag H) * I.  U = the upper Cholesky factor of H^-1
+    (H^-1 = U^T U).  For i = 0 .. K-1: at the first column of a group, its
+    scale and zero come from the group's current weights by the RTN rule;
+    the column's codes q and dequantized weights w_hat are taken with that
+    rule (decisions on the float32 value of the running weights);
+    err = (W[:, i] - w_hat) / U[i][i];  W[:, i+1:] -= err U[i, i+1:].
+    The lazy batching of the updates is an ordering of the same arithmetic
+    and is left out here.  The pages outline the method; the damping (1 %
+    of the mean diagonal), the dead-channel rule and groups taken from the
+    running weights at their first column are the published method's
+    choices, read as the plain ones.
+    Returns a dict like quantize_linear_layer's (codes, scales, zeros,
+    w_hat; no act-order).
+    """
+    qmax = _check_bits(bits)
+    W = np.asarray(w, dtype=F16).astype(F64).copy()
+    X = np.asarray(x, dtype=F16).astype(F64)
+    N, K = W.shape
+    gs = K if group_size == -1 else int(group_size)
+    if gs <= 0 or K % gs:
+        raise ValueError("group_size must divide K")
+    H = X.T @ X
+    dead = np.diag(H) == 0
+    H[dead, dead] = 1.0
+    W[:, dead] = 0.0
+    H[np.diag_indices(K)] += damp * np.mean(np.diag(H))
+    U = np.linalg.cholesky(np.linalg.inv(H)).T
+    G = K // gs
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, G), dtype=F16)
+    zeros = None if symmetric else np.zeros((N, G), dtype=np.uint8)
+    w_hat = np.zeros((N, K), dtype=F16)
+    s_f = z = None
+    for i in range(K):
+        if i % gs == 0:
+            s_h, z = _group_params_f32(W[:, i:i + gs].astype(F32), bits, symmetric)
+            scales[:, i // gs] = s_h
+            if not symmetric:
+                zeros[:, i // gs] = z.astype(np.uint8)
+            s_f = s_h.astype(F32)
+        col = W[:, i].astype(F32)
+        q = np.clip(np.rint(col / s_f) + z, F32(0), qmax)
+        codes[:, i] = q.astype(np.uint8)
+        wq = ((q - z) * s_f).astype(F16)
+        w_hat[:, i] = wq
+        err = (W[:, i] - wq.astype(F64)) / U[i, i]
+        W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+    return dict(codes=codes, scales=scales, zeros=zeros, w_hat=w_hat)
 
 
 def f64_to_f16_nearest(v: float) -> np.float16:

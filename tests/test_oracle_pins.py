@@ -389,6 +389,91 @@ def test_awq_search_prefers_rescaling_on_outlier_channels():
     assert losses[best] < 0.8 * losses[0]
 
 
+# ------------------------------------------------------------------ GPTQ
+
+def test_gptq_with_uncorrelated_inputs_is_rtn():
+    # x = c * I makes H a multiple of the identity: every off-diagonal entry
+    # of the inverse Hessian's Cholesky factor is 0, no error is carried to
+    # other columns, and GPTQ must return plain RTN's codes, scales, zeros.
+    K, N = 256, 40
+    seed = (48,)
+    w = I.weights(seed, N, K, 0.02)
+    x = (np.eye(K) * 3.0).astype(np.float16)
+    for bits, gs, sym in ((4, 128, False), (3, 32, True), (8, -1, True)):
+        g = O.gptq_quantize(w, x, bits, gs, symmetric=sym)
+        codes, scales, zeros = O.rtn_quantize(w, bits, gs, symmetric=sym)
+        assert np.array_equal(g["codes"], codes), (bits, gs)
+        assert np.array_equal(g["scales"].view(np.uint16), scales.view(np.uint16)), (bits, gs)
+        if not sym:
+            assert np.array_equal(g["zeros"], zeros)
+
+
+def _obs_reference(w, x, bits, gs, damp=0.01):
+    # The same column-by-column compensation written with the explicit
+    # inverse Hessian (Optimal Brain Surgeon form): after quantizing column
+    # i, W[:, j] -= err_i * Hinv[i][j] / Hinv[i][i] for the remaining j, and
+    # column i is eliminated from Hinv.  Mathematically the Cholesky form's
+    # update; written independently with scalar loops.
+    W = w.astype(np.float64).copy()
+    X = x.astype(np.float64)
+    N, K = W.shape
+    H = X.T @ X
+    for k in range(K):
+        if H[k, k] == 0:
+            H[k, k] = 1.0
+            W[:, k] = 0.0
+    mean_diag = sum(H[k, k] for k in range(K)) / K
+    for k in range(K):
+        H[k, k] += damp * mean_diag
+    Hinv = np.linalg.inv(H)
+    qmax = (1 << bits) - 1
+    codes = np.zeros((N, K), dtype=np.int64)
+    for i in range(K):
+        if i % gs == 0:
+            grp = W[:, i:i + gs].astype(np.float32)
+            mn, mx = grp.min(axis=1), grp.max(axis=1)
+            s_h = ((mx - mn) / np.float32(qmax)).astype(np.float16)
+            s_f = s_h.astype(np.float32)
+            z = np.clip(np.rint(-mn / s_f), 0, qmax).astype(np.float32)
+        for n in range(N):
+            v = np.float32(W[n, i])
+            q = min(max(np.rint(v / s_f[n]) + z[n], 0), qmax)
+            codes[n, i] = int(q)
+            what = float(np.float16(np.float32(q - z[n]) * s_f[n]))
+            e = (W[n, i] - what) / Hinv[i, i]
+            for j in range(i + 1, K):
+                W[n, j] -= e * Hinv[i, j]
+        # eliminate column i from the inverse Hessian
+        Hinv = Hinv - np.outer(Hinv[:, i], Hinv[i, :]) / Hinv[i, i]
+    return codes
+
+
+def test_gptq_cholesky_form_matches_inverse_hessian_form():
+    K, N, M = 16, 5, 64
+    seed = (49,)
+    rng = np.random.default_rng(list(seed))
+    x = (rng.standard_normal((M, K)) @ rng.standard_normal((K, K)) * 0.3).astype(np.float16)
+    w = I.weights(seed, N, K, 0.05)
+    g = O.gptq_quantize(w, x, 4, 8)
+    assert np.array_equal(g["codes"].astype(np.int64), _obs_reference(w, x, 4, 8))
+
+
+def test_gptq_beats_rtn_on_correlated_inputs():
+    # compensation lowers the layer's output error below plain rounding's
+    K, N, M = 256, 64, 512
+    seed = (50,)
+    rng = np.random.default_rng(list(seed))
+    mix = np.eye(K) + 0.3 * rng.standard_normal((K, K)) / np.sqrt(K)
+    x = (rng.standard_normal((M, K)) @ mix).astype(np.float16)
+    w = I.weights(seed, N, K, 0.02)
+    y = O.linear_ref(x, w)
+    g = O.gptq_quantize(w, x, 4, 128)
+    r = O.quantize_linear_layer(w, 4, 128)
+    e_g = np.linalg.norm(O.linear_ref(x, g["w_hat"]) - y)
+    e_r = np.linalg.norm(O.linear_ref(x, r["w_hat"]) - y)
+    assert e_g < 0.9 * e_r, (e_g, e_r)
+
+
 # ------------------------------------------------------- fused gate / up
 
 def test_silu_mul_closed_forms():
