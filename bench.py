@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq", "silu"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq", "silu", "gptq"], default=None,
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
                         "copies of a known size, the reference for scaling HBM byte counters; "
                         "'configs' times every case of the five synthetic workloads; 'awq' times "
@@ -397,6 +397,50 @@ def awq_leg(wq, torch, repeats, cpu):
     return out
 
 
+def gptq_leg(wq, torch, repeats, cpu):
+    """GPTQ of the prefill layer (K = 4096, N = 11008, 4-bit, group 128) on
+    M = 2048 calibration tokens with correlated input channels, timed by the
+    wall clock around whole calls (synchronized).  Reports the layer's output
+    error relative to plain RTN's on the same tokens.  With cpu, the oracle on
+    a sample of weight rows (its Hessian, inverse and Cholesky factor are
+    computed in full), timed the same way."""
+    M, K, N = PREFILL["M"], PREFILL["K"], PREFILL["N"]
+    seed = (3, 2)
+    x_np = I.correlated_activations(seed, M, K)
+    w_np = I.weights(seed, N, K, 0.02)
+    x, w = torch.from_numpy(x_np).cuda(), torch.from_numpy(w_np).cuda()
+    codes, scales, zeros = wq.gptq_quantize(w, x, BITS, GROUP)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        codes, scales, zeros = wq.gptq_quantize(w, x, BITS, GROUP)
+    torch.cuda.synchronize()
+    gpu_s = (time.perf_counter() - t0) / repeats
+
+    def out_err(c, sc, z):
+        # || x . (w_hat - w)^T || in fp32 (measurement only)
+        g = K // GROUP
+        wh = (c.float().view(N, g, GROUP) - z.float().view(N, g, 1)) * sc.float().view(N, g, 1)
+        d = wh.view(N, K).half().float() - w.float()
+        return float(torch.linalg.norm(x.float() @ d.t()))
+
+    rc, rs, rz = wq.quantize_rtn(w, BITS, GROUP)
+    ratio = out_err(codes, scales, zeros) / out_err(rc, rs, rz)
+    out = dict(leg="gptq", workload="prefill-gptq-w4g128 calibration: M=2048 K=4096 N=11008, correlated channels",
+               gpu_ms_per_layer=round(gpu_s * 1e3, 2), gpu_rows_per_s=round(N / gpu_s, 1),
+               out_err_gptq_over_rtn=round(ratio, 4))
+    if cpu:
+        import oracle as O
+        rows = 64
+        t0 = time.perf_counter()
+        O.gptq_quantize(w_np[:rows], x_np, BITS, GROUP)
+        cpu_s = time.perf_counter() - t0
+        out["cpu_baseline"] = dict(kind="oracle", sample=f"{rows} weight rows of the same layer, full M and K "
+                                                          f"(Hessian, inverse and factor in full)",
+                                   seconds=round(cpu_s, 2), rows_per_s=round(rows / cpu_s, 2))
+    return out
+
+
 # -------------------------------------------------------- CPU baseline ----
 
 def cpu_baseline(target_s):
@@ -470,6 +514,9 @@ def main():
         return
     if args.only == "awq":
         print(json.dumps(awq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)
+        return
+    if args.only == "gptq":
+        print(json.dumps(gptq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)
         return
     if args.only == "configs":
         configs_leg(wq, torch, max(args.steps, 1))

@@ -129,6 +129,36 @@ wq_status wq_awq_search(const uint16_t* x, const uint16_t* w, int32_t M, int32_t
 size_t wq_awq_search_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits,
                                     int32_t group_size, int32_t n_grid);
 
+/* GPTQ ("GPTQ, AWQ and the rules of post-training quantization", section
+ * "GPTQ: pay for the error with the other weights"): quantize w fp16 [N][K]
+ * one input column at a time in index order, compensating each column's
+ * rounding error on the columns not yet quantized.  H = x^T x (fp32 sums of
+ * exact fp16 products); a channel with H[k][k] = 0 gets H[k][k] = 1 and a
+ * zero weight column; H += damp * mean(diag H) * I; U = the upper Cholesky
+ * factor of H^-1.  For column i: at the first column of a group, scale and
+ * zero by wq_quantize_rtn's rule from the group's running weights; the
+ * column's codes and w_hat by that rule; err = (w - w_hat) / U[i][i]; the
+ * later columns -= err * U[i][later], applied in blocks of 64 columns.
+ * All in fp32 (the float64 reference agrees in error, not bit for bit).
+ * x fp16 [M][K] (calibration activations, M a multiple of 32); outputs as
+ * wq_quantize_rtn's: codes uint8 [N][K], scales fp16 [N][G], zeros uint8
+ * [N][G] (NULL when symmetric, required otherwise), ready for wq_pack.
+ * group_size: -1 (one group per row) or a multiple of 32 dividing K that
+ * divides 64 or is a multiple of 64.  0 <= damp < 1 (0.01 is usual).
+ * workspace: device memory of at least wq_gptq_workspace_size(M, N, K)
+ * bytes, 16-byte aligned (about 5 K^2 floats plus N*K floats); codes 16-byte
+ * aligned.
+ * Asynchronous on `stream`.  Returns WQ_ERR_ARG for null/misaligned
+ * pointers, bad sizes or a short workspace, WQ_ERR_UNSUPPORTED for other
+ * bit widths. */
+wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N, int32_t K,
+                           int32_t bits, int32_t group_size, int32_t symmetric, double damp,
+                           uint8_t* codes, uint16_t* scales, uint8_t* zeros, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace wq_gptq_quantize needs (0 for invalid sizes). */
+size_t wq_gptq_workspace_size(int32_t M, int32_t N, int32_t K);
+
 /* Act-order packing order: perm = stable sort of k by g_idx[k].  Checks that
  * every g_idx lies in [0, K/group_size) and every group holds exactly
  * group_size channels; returns WQ_ERR_ARG otherwise.  This call SYNCHRONIZES

@@ -18,7 +18,8 @@ def test_library_exports_every_declared_symbol():
     expected = {"wq_status_str", "wq_version", "wq_quantize_rtn", "wq_awq_scales", "wq_awq_fold",
                 "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
                 "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m",
-                "wq_awq_search", "wq_awq_search_workspace_size", "wq_gemv_silu_mul"}
+                "wq_awq_search", "wq_awq_search_workspace_size", "wq_gemv_silu_mul",
+                "wq_gptq_quantize", "wq_gptq_workspace_size"}
     assert set(names) == expected
     handle = wq.lib()
     for name in names:
@@ -139,3 +140,27 @@ def test_setup_entry_points_check_arguments():
 def test_binding_raises_on_status():
     with pytest.raises(wq.WQError):
         wq._check(WQ_ERR_ARG, "wq_gemv")
+
+
+def test_gptq_argument_checks():
+    L = wq.lib()
+    size = L.wq_gptq_workspace_size
+    assert size(64, 32, 256) > 5 * 256 * 256 * 4
+    assert size(0, 32, 256) == 0
+
+    def call(x=FAKE, w=FAKE, M=64, N=32, K=256, bits=4, gs=128, sym=0, damp=0.01, zeros=FAKE, ws=FAKE,
+             wsb=1 << 30):
+        return L.wq_gptq_quantize(x, w, M, N, K, bits, gs, sym, damp, FAKE, FAKE, zeros, ws, wsb, None)
+
+    assert call(x=None) == WQ_ERR_ARG
+    assert call(ws=None) == WQ_ERR_ARG
+    assert call(M=48) == WQ_ERR_ARG                # M not a multiple of 32
+    assert call(K=250) == WQ_ERR_ARG
+    assert call(gs=96, K=384) == WQ_ERR_ARG        # neither divides nor is a multiple of the 64-column block
+    assert call(bits=5) == WQ_ERR_UNSUPPORTED
+    assert call(sym=1) == WQ_ERR_ARG               # symmetric takes no zeros
+    assert call(zeros=None) == WQ_ERR_ARG          # asymmetric needs zeros
+    assert call(damp=-0.1) == WQ_ERR_ARG
+    assert call(damp=1.0) == WQ_ERR_ARG
+    assert call(x=FAKE_MIS) == WQ_ERR_ARG
+    assert call(wsb=size(64, 32, 256) - 1) == WQ_ERR_ARG

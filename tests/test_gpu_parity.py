@@ -394,3 +394,84 @@ def test_gemv_silu_mul_llama_gate_up_sampled():
         y = wq.gemv_silu_mul(dev(x), packed, scales, zeros, 4, 128)
         assert y.shape == (M, half)
         check_y(y[:, torch.from_numpy(js).cuda()], O.silu_mul_ref(x, ref["w_hat"]), f"gate_up M={M}")
+
+
+# ------------------------------------------------------------------ GPTQ ----
+#
+# The GPU runs GPTQ in float32 (matrix-core Hessian, blocked Cholesky and
+# triangular inverse, blocked column walk); the oracle runs the unblocked
+# steps in float64.  Rounding decisions can differ where a running weight
+# sits within float32 noise of a rounding boundary, and such a flip changes
+# the later compensation of its row slightly, so the comparison is on the
+# agreement of codes and scales and on the layer's output error.  Where the
+# Hessian is diagonal no error is carried and the GPU must reproduce RTN bit
+# for bit.
+
+def _gptq_out_err(w, x, w_hat):
+    xf = x.astype(np.float64)
+    return np.linalg.norm(xf @ (w_hat.astype(np.float64) - w.astype(np.float64)).T)
+
+
+def _gptq_w_hat(codes, scales, zeros, bits, gs):
+    return O.dequant(codes, scales, zeros, bits, gs)
+
+
+@pytest.mark.parametrize("bits,gs,sym", [(4, 128, False), (3, 32, True), (8, -1, True), (2, 64, False), (4, 192, False)])
+def test_gptq_with_diagonal_hessian_is_rtn(bits, gs, sym):
+    # x = 3 * I: H = 9 I (+ damping), U diagonal, nothing carried.
+    K, N = 384, 100
+    seed = (120, bits, K)
+    w = I.weights(seed, N, K, 0.02)
+    x = (3.0 * np.eye(K)).astype(np.float16)
+    codes, scales, zeros = wq.gptq_quantize(dev(w), dev(x), bits, gs, symmetric=sym)
+    rc, rs, rz = O.rtn_quantize(w, bits, gs, symmetric=sym)
+    assert np.array_equal(host(codes), rc)
+    assert np.array_equal(host(scales).view(np.uint16), rs.view(np.uint16))
+    if not sym:
+        assert np.array_equal(host(zeros), rz)
+
+
+@pytest.mark.parametrize("M,N,K,bits,gs,sym", [(256, 96, 384, 4, 128, False), (128, 70, 256, 3, 32, True),
+                                               (512, 64, 320, 8, -1, True), (256, 130, 448, 2, 64, False),
+                                               (96, 64, 512, 4, 128, False)])
+def test_gptq_matches_oracle(M, N, K, bits, gs, sym):
+    seed = (121, M, N, K, bits)
+    x = I.correlated_activations(seed, M, K)
+    x[:, 5] = 0                                      # a dead input channel
+    w = I.weights(seed, N, K, 0.02)
+    ref = O.gptq_quantize(w, x, bits, gs, symmetric=sym)
+    codes, scales, zeros = wq.gptq_quantize(dev(w), dev(x), bits, gs, symmetric=sym)
+    c = host(codes)
+    agree = np.mean(c == ref["codes"])
+    s_agree = np.mean(host(scales).view(np.uint16) == ref["scales"].view(np.uint16))
+    w_hat = _gptq_w_hat(c, host(scales), None if sym else host(zeros), bits, gs)
+    assert np.all(w_hat[:, 5] == 0)                  # the dead channel's weights are zeroed
+    e_gpu, e_ref = _gptq_out_err(w, x, w_hat), _gptq_out_err(w, x, ref["w_hat"])
+    rc, rs, rz = O.rtn_quantize(w, bits, gs, symmetric=sym)
+    e_rtn = _gptq_out_err(w, x, _gptq_w_hat(rc, rs, rz, bits, gs))
+    print(f"codes {agree:.5f} scales {s_agree:.5f} err gpu/ref {e_gpu / e_ref:.5f} gptq/rtn {e_ref / e_rtn:.4f}")
+    # 2-bit codes are the most sensitive: a float32 run of the same blocked
+    # steps on the CPU agrees with the float64 oracle on 99.83 % of them for
+    # the 2-bit case here, and on all of them for the others
+    assert agree >= 0.997 and s_agree >= 0.99, (agree, s_agree)
+    assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)
+    assert e_gpu < e_rtn
+
+
+def test_gptq_llama_layer_sampled_rows():
+    # 4096 x 4096 projection, 2048 calibration tokens: the oracle quantizes
+    # sampled weight rows (rows are independent given the Hessian).
+    M, N, K = 2048, 4096, 4096
+    seed = (122,)
+    x = I.correlated_activations(seed, M, K)
+    w = I.weights(seed, N, K, 0.02)
+    codes, scales, zeros = wq.gptq_quantize(dev(w), dev(x), 4, 128)
+    rows = np.array([0, 1, 2047, 4095])
+    ref = O.gptq_quantize(w[rows], x, 4, 128)
+    c = host(codes)[rows]
+    agree = np.mean(c == ref["codes"])
+    w_hat = _gptq_w_hat(c, host(scales)[rows], host(zeros)[rows], 4, 128)
+    e_gpu, e_ref = _gptq_out_err(w[rows], x, w_hat), _gptq_out_err(w[rows], x, ref["w_hat"])
+    print(f"codes {agree:.5f} err gpu/ref {e_gpu / e_ref:.5f}")
+    assert agree >= 0.997, agree
+    assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)

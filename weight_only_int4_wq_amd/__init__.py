@@ -16,7 +16,7 @@ import re
 
 __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
-    "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "act_order_perm", "pack", "unpack",
+    "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "gptq_quantize", "act_order_perm", "pack", "unpack",
     "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_max_m",
     "status_str", "version", "QuantizedLinear",
 ]
@@ -45,6 +45,9 @@ _SIG = {
     "wq_awq_search": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP,
                                      ctypes.c_size_t, _VP]),
     "wq_awq_search_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "wq_gptq_quantize": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _VP, _VP,
+                                        _VP, _VP, ctypes.c_size_t, _VP]),
+    "wq_gptq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
 }
 _SIG["wq_gemv_silu_mul"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
@@ -198,6 +201,31 @@ def awq_search(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, sym
                                _stream(x.device)), "wq_awq_search")
     alphas = [i / (n_grid - 1) for i in range(n_grid)]
     return alphas, list(losses), int(best.value)
+
+
+def gptq_quantize(w, x, bits: int = 4, group_size: int = 128, symmetric: bool = False, damp: float = 0.01):
+    """GPTQ of fp16 w [N][K] on calibration activations x fp16 [M][K] ->
+    (codes u8 [N][K], scales fp16 [N][G], zeros u8 [N][G] or None), the
+    layout quantize_rtn returns."""
+    torch = _torch()
+    w = _dev(w, torch.float16, "w", 2)
+    x = _dev(x, torch.float16, "x", 2)
+    N, K = w.shape
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K] with the K of w")
+    need = int(lib().wq_gptq_workspace_size(M, N, K))
+    if need == 0:
+        raise ValueError("invalid GPTQ sizes")
+    G = _groups(K, group_size)
+    ws = torch.empty((need,), dtype=torch.uint8, device=w.device)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=w.device)
+    zeros = None if symmetric else torch.empty((N, G), dtype=torch.uint8, device=w.device)
+    _check(lib().wq_gptq_quantize(_ptr(x), _ptr(w), M, N, K, bits, group_size, int(bool(symmetric)), float(damp),
+                                  _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(ws), need, _stream(w.device)),
+           "wq_gptq_quantize")
+    return codes, scales, zeros
 
 
 def act_order_perm(g_idx, group_size: int):

@@ -140,6 +140,12 @@ bool search_args_ok(int M, int N, int K, int bits, int group_size, int n_grid, i
 
 }  // namespace
 
+wq_status wqh::dense_f32(const uint16_t* x, const uint16_t* w, float* y32, int M, int N, int K, hipStream_t s) {
+    if (M <= 0 || N <= 0) return WQ_OK;
+    hipLaunchKernelGGL(dense_ref_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, x, w, y32, M, N, K);
+    return wqh::launch_status();
+}
+
 extern "C" size_t wq_awq_search_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
                                                int32_t n_grid) {
     int gs = 0;
@@ -175,8 +181,7 @@ extern "C" wq_status wq_awq_search(const uint16_t* x, const uint16_t* w, int32_t
     const long long mn = (long long)M * N;
 
     // the original layer's output, once
-    hipLaunchKernelGGL(dense_ref_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, x, w, yref, M, N, K);
-    wq_status st = wqh::launch_status();
+    wq_status st = wqh::dense_f32(x, w, yref, M, N, K, s);
     if (st != WQ_OK) return st;
 
     for (int i = 0; i < n_grid; ++i) {

@@ -137,4 +137,8 @@ wq_status gemm_large(int bits, const uint16_t* x, const uint32_t* packed, const 
 wq_status gemm_f32(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                    float* y32, int M, int N, int K, int bits, int gs, hipStream_t s);
 
+// Plain fp16 product y32[m][n] = sum_k x[m][k] w[n][k] in fp32 (matrix
+// cores); K a multiple of 32, rows 16-byte aligned.
+wq_status dense_f32(const uint16_t* x, const uint16_t* w, float* y32, int M, int N, int K, hipStream_t s);
+
 }  // namespace wqh

@@ -54,6 +54,18 @@ def with_outliers(x: np.ndarray, channels: np.ndarray, factor: float = 20.0) -> 
     return y
 
 
+def correlated_activations(seed: tuple, M: int, K: int, rank: int = 16, strength: float = 1.0) -> np.ndarray:
+    """fp16 x[M][K] = z + strength * f . V with z, f, V standard normal (z
+    [M][K], f [M][rank], V [rank][K] / sqrt(rank)), drawn and summed in
+    fp32: input channels correlated through a shared low-rank component, so
+    the calibration Hessian x^T x has large off-diagonal entries."""
+    g = rng(*seed, STREAM_X, 1)
+    z = g.standard_normal((M, K), dtype=np.float32)
+    f = g.standard_normal((M, rank), dtype=np.float32)
+    v = g.standard_normal((rank, K), dtype=np.float32) / np.float32(np.sqrt(rank))
+    return (z + np.float32(strength) * (f @ v)).astype(np.float16)
+
+
 def act_order_gidx(seed: tuple, K: int, group_size: int) -> np.ndarray:
     """Act-order group map: g_idx[k] = pi[k] // group_size for a seeded random
     permutation pi of the K input channels (equal-size groups)."""
