@@ -9,8 +9,8 @@
 //   H = x^T x (float32, matrix cores); a channel with H[k][k] = 0 gets
 //   H[k][k] = 1 and a zero weight column; H += damp * mean(diag H) * I.
 //   U = the upper Cholesky factor of H^-1 (H^-1 = U^T U), computed as
-//   U = P L^-1 P with L L^T = P H P and P the index reversal: one blocked
-//   Cholesky and one triangular inverse by recursive halving.
+//   U = P L^-1 P with L L^T = P H P and P the index reversal, the factor
+//   and its inverse by recursive halving (large fp32 matrix-core products).
 //   For each block of 64 columns, one thread per weight row walks the
 //   block's columns in order: at the first column of a group, the RTN scale
 //   and zero from the group's running weights; the column's code and
@@ -32,7 +32,8 @@ __device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_ca
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 constexpr int kCholB = 32;   // Cholesky / inverse block
-constexpr int kGptqB = 64;   // lazy-update block of columns
+constexpr int kGptqB = 64;   // columns walked by one launch
+constexpr int kGptqOuter = 256;  // outer lazy-update block
 
 // ------------------------------------------------------------ helpers ----
 
@@ -267,22 +268,29 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(const float* __restrict_
     }
 }
 
-// Li[n0 + n) x [n0 + n) = the inverse of the lower-triangular L block of the
-// same place, whose kCholB-sized diagonal blocks Li already holds:
-// inv([[L11, 0], [L21, L22]]) = [[Li11, 0], [-Li22 . L21 . Li11, Li22]],
-// halves inverted first.  tmp: room for n * n / 4 floats.
-wq_status tri_inverse(const float* L, float* Li, int K, int n0, int n, float* tmp, hipStream_t s) {
-    if (n <= kCholB) return WQ_OK;
-    const int h = ((n / kCholB + 1) / 2) * kCholB, n2 = n - h;
+// Recursive Cholesky with the inverse of the factor, on the block
+// [n0, n0 + n) of A (lower part read; the trailing block is overwritten by
+// its Schur complement):  with halves 1 and 2,
+//   L11 = chol(A11), L21 = A21 . L11^-T, L22 = chol(A22 - L21 . L21^T),
+//   inv(L) = [[Li11, 0], [-Li22 . L21 . Li11, Li22]].
+// Blocks of kCholB go to chol_diag_kernel; everything else is large fp32
+// products.  tmp: room for n * n / 4 floats.
+wq_status chol_inverse(float* A, float* L, float* Li, int K, int n0, int n, float* tmp, hipStream_t s) {
+    if (n <= kCholB) {
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, A, K, n0, n, L, Li);
+        return wqh::launch_status();
+    }
+    const int h = ((n / kCholB + 1) / 2) * kCholB, n2 = n - h, r0 = n0 + h;
+    float* L21 = L + (size_t)r0 * K + n0;
+    const float* Li11 = Li + (size_t)n0 * K + n0;
     wq_status st;
-    if ((st = tri_inverse(L, Li, K, n0, h, tmp, s)) != WQ_OK) return st;
-    if ((st = tri_inverse(L, Li, K, n0 + h, n2, tmp, s)) != WQ_OK) return st;
+    if ((st = chol_inverse(A, L, Li, K, n0, h, tmp, s)) != WQ_OK) return st;
+    if ((st = sgemm<true>(n2, h, h, 1.f, A + (size_t)r0 * K + n0, K, Li11, K, 0.f, L21, K, s)) != WQ_OK) return st;
+    if ((st = sgemm<true>(n2, n2, h, -1.f, L21, K, L21, K, 1.f, A + (size_t)r0 * K + r0, K, s)) != WQ_OK) return st;
+    if ((st = chol_inverse(A, L, Li, K, r0, n2, tmp, s)) != WQ_OK) return st;
     // tmp = L21 . Li11 (n2 x h), then Li21 = -Li22 . tmp
-    if ((st = sgemm<false>(n2, h, h, 1.f, L + (size_t)(n0 + h) * K + n0, K, Li + (size_t)n0 * K + n0, K, 0.f, tmp, h,
-                           s)) != WQ_OK)
-        return st;
-    return sgemm<false>(n2, h, n2, -1.f, Li + (size_t)(n0 + h) * K + n0 + h, K, tmp, h, 0.f,
-                        Li + (size_t)(n0 + h) * K + n0, K, s);
+    if ((st = sgemm<false>(n2, h, h, 1.f, L21, K, Li11, K, 0.f, tmp, h, s)) != WQ_OK) return st;
+    return sgemm<false>(n2, h, n2, -1.f, Li + (size_t)r0 * K + r0, K, tmp, h, 0.f, Li + (size_t)r0 * K + n0, K, s);
 }
 
 // Columns [32 H, 32 H + 32) of a block (see gptq_block_kernel); a group can
@@ -343,7 +351,7 @@ template <int BITS, bool SYM, int BC>
 __global__ void __launch_bounds__(64) gptq_block_kernel(float* __restrict__ W32, const float* __restrict__ U, int N,
                                                         int K, int b0, int gs, uint8_t* __restrict__ codes,
                                                         uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros,
-                                                        float* __restrict__ Err) {
+                                                        float* __restrict__ Err, int ldE) {
     const int n = blockIdx.x * 64 + threadIdx.x;
     const bool live = n < N;
     const int nr = live ? n : N - 1;  // rows past N compute on a copy and store nothing
@@ -377,7 +385,7 @@ __global__ void __launch_bounds__(64) gptq_block_kernel(float* __restrict__ W32,
 #pragma unroll
         for (int v = 0; v < BC / 16; ++v)
             *reinterpret_cast<u4*>(crow + 16 * v) = u4{cw[4 * v], cw[4 * v + 1], cw[4 * v + 2], cw[4 * v + 3]};
-        float* erow = Err + (size_t)n * kGptqB;
+        float* erow = Err + (size_t)n * ldE;
 #pragma unroll
         for (int v = 0; v < BC / 4; ++v)
             *reinterpret_cast<f4*>(erow + 4 * v) = f4{e[4 * v], e[4 * v + 1], e[4 * v + 2], e[4 * v + 3]};
@@ -405,7 +413,7 @@ GptqLayout gptq_layout(int M, int N, int K) {
     Ly.Li = take(KK);
     Ly.U = take(KK);
     Ly.W32 = take(size_t(N) * K * 4);
-    Ly.Err = take(size_t(N) * kGptqB * 4);
+    Ly.Err = take(size_t(N) * kGptqOuter * 4);
     Ly.dead = take(size_t(K));
     Ly.total = off;
     return Ly;
@@ -422,26 +430,42 @@ bool gptq_args_ok(int M, int N, int K, int bits, int group_size, int* gs_out) {
     return true;
 }
 
+// Outer block width: 256 columns when no group can start inside an outer
+// block and reach past it (the group size divides 256 or is a multiple of
+// it), else 64 (one level).
+int gptq_outer(int gs) { return (kGptqOuter % gs == 0 || gs % kGptqOuter == 0) ? kGptqOuter : kGptqB; }
+
+// The column walk in two levels: inside an outer block, each 64-column
+// launch is followed by the update of the outer block's later columns; after
+// the outer block, one product carries all of its errors to the columns
+// after it.  Err holds the outer block's errors, [N][outer].
 template <int BITS, bool SYM>
 wq_status gptq_blocks(float* W32, const float* U, int N, int K, int gs, uint8_t* codes, uint16_t* scales,
                       uint8_t* zeros, float* Err, hipStream_t s) {
-    for (int b0 = 0; b0 < K; b0 += kGptqB) {
-        const int bc = min(kGptqB, K - b0);  // 64, or 32 for the last block
-        if (bc == kGptqB)
-            hipLaunchKernelGGL((gptq_block_kernel<BITS, SYM, kGptqB>), dim3((N + 63) / 64), dim3(64), 0, s, W32, U,
-                               N, K, b0, gs, codes, scales, zeros, Err);
-        else
-            hipLaunchKernelGGL((gptq_block_kernel<BITS, SYM, 32>), dim3((N + 63) / 64), dim3(64), 0, s, W32, U, N,
-                               K, b0, gs, codes, scales, zeros, Err);
-        wq_status st = wqh::launch_status();
-        if (st != WQ_OK) return st;
-        const int rest = K - b0 - bc;
-        if (rest > 0) {
-            // W[:, after] -= Err . U[block, after]
-            st = sgemm<false>(N, rest, bc, -1.f, Err, kGptqB, U + (size_t)b0 * K + b0 + bc, K, 1.f,
-                                        W32 + b0 + bc, K, s);
-            if (st != WQ_OK) return st;
+    const int outer = gptq_outer(gs);
+    wq_status st;
+    for (int ob0 = 0; ob0 < K; ob0 += outer) {
+        const int oe = min(ob0 + outer, K);
+        for (int b0 = ob0; b0 < oe; b0 += kGptqB) {
+            const int bc = min(kGptqB, oe - b0);  // 64, or 32 at the end
+            float* eb = Err + (b0 - ob0);
+            if (bc == kGptqB)
+                hipLaunchKernelGGL((gptq_block_kernel<BITS, SYM, kGptqB>), dim3((N + 63) / 64), dim3(64), 0, s, W32,
+                                   U, N, K, b0, gs, codes, scales, zeros, eb, outer);
+            else
+                hipLaunchKernelGGL((gptq_block_kernel<BITS, SYM, 32>), dim3((N + 63) / 64), dim3(64), 0, s, W32, U,
+                                   N, K, b0, gs, codes, scales, zeros, eb, outer);
+            if ((st = wqh::launch_status()) != WQ_OK) return st;
+            const int rest_in = oe - b0 - bc;
+            if (rest_in > 0 &&
+                (st = sgemm<false>(N, rest_in, bc, -1.f, eb, outer, U + (size_t)b0 * K + b0 + bc, K, 1.f,
+                                   W32 + b0 + bc, K, s)) != WQ_OK)
+                return st;
         }
+        const int rest = K - oe;
+        if (rest > 0 && (st = sgemm<false>(N, rest, oe - ob0, -1.f, Err, outer, U + (size_t)ob0 * K + oe, K, 1.f,
+                                           W32 + oe, K, s)) != WQ_OK)
+            return st;
     }
     return WQ_OK;
 }
@@ -489,28 +513,13 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, s, H, K, float(damp), dead);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
 
-    // L L^T = P H P (blocked Cholesky, lower, in A), Li = L^-1 (recursive
-    // halving), U = P Li P
+    // L L^T = P H P and Li = L^-1 (recursive halving), U = P Li P
     hipLaunchKernelGGL(reverse_kernel, grid_for(KK), dim3(256), 0, s, H, K, A);
     hipLaunchKernelGGL(fill_kernel, grid_for(KK), dim3(256), 0, s, L, KK, 0.f);
     hipLaunchKernelGGL(fill_kernel, grid_for(KK), dim3(256), 0, s, Li, KK, 0.f);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
-    for (int j0 = 0; j0 < K; j0 += kCholB) {
-        const int nb = std::min(kCholB, K - j0), r0 = j0 + nb, rest = K - r0;
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, A, K, j0, nb, L, Li);
-        if ((st = wqh::launch_status()) != WQ_OK) return st;
-        if (rest > 0) {
-            // L21 = A21 . L11^-T;  A22 -= L21 . L21^T
-            if ((st = sgemm<true>(rest, nb, nb, 1.f, A + (size_t)r0 * K + j0, K, Li + (size_t)j0 * K + j0,
-                                            K, 0.f, L + (size_t)r0 * K + j0, K, s)) != WQ_OK)
-                return st;
-            if ((st = sgemm<true>(rest, rest, nb, -1.f, L + (size_t)r0 * K + j0, K,
-                                            L + (size_t)r0 * K + j0, K, 1.f, A + (size_t)r0 * K + r0, K, s)) != WQ_OK)
-                return st;
-        }
-    }
-    // A is free after the factorization: scratch for the inverse's products
-    if ((st = tri_inverse(L, Li, K, 0, K, A, s)) != WQ_OK) return st;
+    // H is free once reversed into A: scratch for the inverse's products
+    if ((st = chol_inverse(A, L, Li, K, 0, K, H, s)) != WQ_OK) return st;
     hipLaunchKernelGGL(reverse_kernel, grid_for(KK), dim3(256), 0, s, Li, K, U);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
 
