@@ -19,6 +19,8 @@ from .wq_oracle import (  # noqa: F401
     awq_fold_weight,
     awq_scale_act,
     awq_search,
+    awq_clip_ratios,
+    awq_clip_search,
     gptq_quantize,
     linear_ref,
     silu_mul_ref,

@@ -356,6 +356,66 @@ def awq_search(x, w, bits: int, group_size: int, n_grid: int = 20, symmetric: bo
     return alphas, losses, int(np.argmin(losses))
 
 
+def awq_clip_ratios(n_grid: int = 20, n_ratios: int = 10) -> np.ndarray:
+    """Shrink ratios of AWQ's clipping search: r_i = fp32(1 - i / n_grid),
+    i = 0 .. n_ratios - 1 (1.0, 0.95, ..., 0.55 by default).  The pages say
+    AWQ computes clipping thresholds from the calibration data and clips
+    symmetrically; the grid (the published method's: shrink the group's
+    largest magnitude by up to one half in steps of 1/20) is the plain
+    reading taken."""
+    if n_grid < 1 or not 1 <= n_ratios <= n_grid:
+        raise ValueError("need 1 <= n_ratios <= n_grid")
+    return np.array([1.0 - i / n_grid for i in range(n_ratios)], dtype=F32)
+
+
+def awq_clip_search(x, w, bits: int, group_size: int, n_grid: int = 20, n_ratios: int = 10,
+                    symmetric: bool = False):
+    """AWQ's clipping-threshold search ("AutoAWQ vs The Stack v2", the
+    paragraph on per-channel scaling factors and clipping thresholds: a
+    threshold per weight group from the calibration activations, symmetric
+    clipping).  For every output row n, group g and ratio r_i:
+        t = fp16(fp32(r_i) * max over the group of |w|)   (fp32 multiply)
+        w_c = clip(w, -t, t)                               (exact in fp16)
+        w_hat = RTN-dequantized w_c (the group as one RTN group)
+        loss[n][g][i] = sum over m of (sum over k in g of x[m][k] (w - w_hat)[n][k])^2
+    in float64 from the fp16 values; best[n][g] = the first index of the
+    smallest loss; w_clip = w clipped at the best threshold (fp16).
+    The objective, the group's own output error on the calibration
+    activations, is the reading taken where the pages name none.
+    Returns dict(ratios, losses float64 [N][G][R], best int [N][G], w_clip)."""
+    x = np.asarray(x, dtype=F16)
+    w = np.asarray(w, dtype=F16)
+    N, K = w.shape
+    gs = K if group_size == -1 else int(group_size)
+    if gs <= 0 or K % gs:
+        raise ValueError("group_size must divide K")
+    G = K // gs
+    ratios = awq_clip_ratios(n_grid, n_ratios)
+    X = x.astype(F64)
+    losses = np.zeros((N, G, len(ratios)), dtype=F64)
+    thresholds = np.zeros((N, G, len(ratios)), dtype=F16)
+    for g in range(G):
+        cols = slice(g * gs, (g + 1) * gs)
+        wg = w[:, cols]
+        amax = np.max(np.abs(wg.astype(F32)), axis=1)
+        for i, r in enumerate(ratios):
+            t = (r * amax).astype(F16)
+            thresholds[:, g, i] = t
+            tf = t.astype(F32)[:, None]
+            wc = np.clip(wg.astype(F32), -tf, tf).astype(F16)
+            codes, scales, zeros = rtn_quantize(wc, bits, -1, symmetric=symmetric)
+            w_hat = dequant(codes, scales, zeros, bits, -1)
+            p = X[:, cols] @ (wg.astype(F64) - w_hat.astype(F64)).T       # [M][N]
+            losses[:, g, i] = np.sum(p * p, axis=0)
+    best = np.argmin(losses, axis=2)
+    w_clip = w.copy()
+    for g in range(G):
+        cols = slice(g * gs, (g + 1) * gs)
+        t = thresholds[np.arange(N), g, best[:, g]].astype(F32)[:, None]
+        w_clip[:, cols] = np.clip(w[:, cols].astype(F32), -t, t).astype(F16)
+    return dict(ratios=ratios, losses=losses, best=best, w_clip=w_clip)
+
+
 def _group_params_f32(wg, bits: int, symmetric: bool):
     """The RTN rule of rtn_quantize for one group per row, on float32 values
     wg [N][n]: returns (s_h fp16 [N], z float32 [N])."""

@@ -583,3 +583,103 @@ def test_act_order_permutation_invariance():
     assert np.array_equal(back, q["codes"])
     # groups are contiguous in packed order
     assert np.array_equal(g_idx[q["perm"]], np.arange(K) // gs)
+
+
+# ------------------------------------------------------- AWQ clip search --
+
+def test_awq_clip_ratio_grid_closed_form():
+    r = O.awq_clip_ratios(20, 10)
+    assert r.dtype == np.float32
+    assert np.array_equal(r, np.array([1.0, 0.95, 0.9, 0.85, 0.8, 0.75, 0.7, 0.65, 0.6, 0.55], dtype=np.float32))
+    with pytest.raises(ValueError):
+        O.awq_clip_ratios(20, 21)
+
+
+def test_awq_clip_on_grid_weights_keep_full_range():
+    # Weights on the RTN grid of their own range (asymmetric, 4 bits:
+    # values -1 .. 0.875 in steps of 0.125) quantize exactly at ratio 1,
+    # so the loss there is exactly 0 and any clipping can only add error.
+    vals = (np.arange(16) - 8) * 0.125
+    w = np.tile(vals, 4).reshape(2, 32).astype(np.float16)
+    w[1] = w[1][::-1]
+    x = I.activations((60,), 8, 32)
+    r = O.awq_clip_search(x, w, 4, 32)
+    assert np.all(r["losses"][:, :, 0] == 0.0)
+    assert np.all(r["losses"][:, :, 1:] > 0.0)
+    assert np.all(r["best"] == 0)
+    assert np.array_equal(r["w_clip"].view(np.uint16), w.view(np.uint16))
+
+
+def test_awq_clip_zero_activations_pick_first_ratio():
+    w = I.weights((61,), 3, 64, 0.02)
+    x = np.zeros((4, 64), dtype=np.float16)
+    r = O.awq_clip_search(x, w, 3, 32, symmetric=True)
+    assert np.all(r["losses"] == 0.0) and np.all(r["best"] == 0)
+
+
+def test_awq_clip_outlier_prefers_a_threshold():
+    # One weight far out in a group of small ones, on an input channel whose
+    # activations are tiny: at ratio 1 the step is set by the outlier and
+    # every other weight rounds coarsely; clipping costs little on that
+    # channel and gives all others a finer step.
+    g = np.random.default_rng([62])
+    w = (0.01 * g.standard_normal((4, 128))).astype(np.float16)
+    w[:, 17] = np.float16(0.3)
+    x = I.activations((62,), 64, 128)
+    x[:, 17] = (x[:, 17].astype(np.float32) * 0.01).astype(np.float16)
+    r = O.awq_clip_search(x, w, 3, 128)
+    assert np.all(r["best"] > 0)
+    L = r["losses"][:, 0, :]
+    assert np.all(L[np.arange(4), r["best"][:, 0]] < 0.8 * L[:, 0])
+    t = np.abs(r["w_clip"].astype(np.float32)).max(axis=1)
+    assert np.all(t < 0.3)
+
+
+def _clip_loss_brute(x, w, bits, gs, ratio_idx, n_grid, symmetric):
+    # scalar loops, the RTN rule written out for one group at a time
+    qmax = (1 << bits) - 1
+    M, K = x.shape
+    N = w.shape[0]
+    out = np.zeros((N, K // gs))
+    r = np.float32(1.0 - ratio_idx / n_grid)
+    for n in range(N):
+        for g in range(K // gs):
+            ks = range(g * gs, (g + 1) * gs)
+            amax = max(abs(float(w[n, k])) for k in ks)
+            t = float(np.float16(np.float32(r) * np.float32(amax)))
+            wc = [min(max(float(w[n, k]), -t), t) for k in ks]
+            if symmetric:
+                s = float(np.float16(np.float32(2.0) * np.float32(max(abs(v) for v in wc)) / np.float32(qmax)))
+                z = float(1 << (bits - 1))
+            else:
+                lo, hi = min(wc), max(wc)
+                s = float(np.float16((np.float32(hi) - np.float32(lo)) / np.float32(qmax)))
+            if s == 0.0:
+                s = 2.0 ** -14
+            if not symmetric:
+                z = min(max(float(np.rint(np.float32(-lo) / np.float32(s))), 0.0), float(qmax))
+            d = []
+            for k, v in zip(ks, wc):
+                q = min(max(float(np.rint(np.float32(v) / np.float32(s))) + z, 0.0), float(qmax))
+                wh = float(np.float16(np.float32(q - z) * np.float32(s)))
+                d.append(float(w[n, k]) - wh)
+            tot = 0.0
+            for m in range(M):
+                acc = 0.0
+                for j, k in enumerate(ks):
+                    acc += float(x[m, k]) * d[j]
+                tot += acc * acc
+            out[n, g] = tot
+    return out
+
+
+@pytest.mark.parametrize("bits,sym", [(4, False), (3, True), (2, False)])
+def test_awq_clip_losses_match_brute_force(bits, sym):
+    seed = (63, bits)
+    x = I.activations(seed, 3, 64)
+    w = I.weights(seed, 2, 64, 0.02)
+    w[0, 5] = np.float16(0.12)
+    r = O.awq_clip_search(x, w, bits, 32, n_grid=20, n_ratios=10, symmetric=sym)
+    for i in (0, 3, 9):
+        b = _clip_loss_brute(x, w, bits, 32, i, 20, sym)
+        assert np.allclose(r["losses"][:, :, i], b, rtol=1e-12, atol=1e-18)
