@@ -385,6 +385,19 @@ def awq_leg(wq, torch, repeats, cpu):
                gpu_ms_per_search=round(gpu_s * 1e3, 2), gpu_ms_per_alpha=round(gpu_s * 1e3 / len(alphas), 3),
                gpu_columns_per_s=round(N / gpu_s, 1), best_alpha=round(alphas[best], 4),
                loss_best_over_rtn=round(losses[best] / losses[0], 4))
+    # clipping search on the rescaled layer, 512 calibration rows, 10 ratios
+    s_h = wq.awq_scales(x, alphas[best])
+    w_f = wq.awq_fold(w, s_h)
+    x_c = wq.scale_act(x[:512].contiguous(), s_h)
+    w_c, best_c, _ = wq.awq_clip(x_c, w_f, BITS, GROUP)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        w_c, best_c, _ = wq.awq_clip(x_c, w_f, BITS, GROUP)
+    torch.cuda.synchronize()
+    clip_s = (time.perf_counter() - t0) / repeats
+    out["clip"] = dict(workload="clip search after the chosen alpha: M=512 K=4096 N=11008, 10 ratios",
+                       gpu_ms=round(clip_s * 1e3, 3), frac_groups_clipped=round(float((best_c > 0).float().mean()), 4))
     if cpu:
         import oracle as O
         cols = 32
@@ -394,6 +407,14 @@ def awq_leg(wq, torch, repeats, cpu):
         out["cpu_baseline"] = dict(kind="oracle", sample=f"{cols} output columns of the same layer, full M and K, "
                                                           f"20 alphas", seconds=round(cpu_s, 2),
                                    columns_per_s=round(cols / cpu_s, 2), best_alpha=round(float(a_o[b_o]), 4))
+        rows = 64
+        xc_np, wf_np = x_c.cpu().numpy(), w_f.cpu().numpy()
+        t0 = time.perf_counter()
+        O.awq_clip_search(xc_np, wf_np[:rows], BITS, GROUP)
+        cpu_c = time.perf_counter() - t0
+        out["clip"]["cpu_baseline"] = dict(kind="oracle", sample=f"{rows} weight rows, same M, K and ratios",
+                                           seconds=round(cpu_c, 2), rows_per_s=round(rows / cpu_c, 2),
+                                           gpu_rows_per_s=round(N / clip_s, 1))
     return out
 
 

@@ -129,6 +129,30 @@ wq_status wq_awq_search(const uint16_t* x, const uint16_t* w, int32_t M, int32_t
 size_t wq_awq_search_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits,
                                     int32_t group_size, int32_t n_grid);
 
+/* AWQ's clipping-threshold search ("AutoAWQ vs The Stack v2", paragraph on
+ * per-channel scaling factors and clipping thresholds: a threshold per group
+ * computed from the calibration activations, symmetric clipping).  For every
+ * output row n, group g and ratio r_i = fp32(1 - i / n_grid), i = 0 ..
+ * n_ratios - 1 (AWQ: n_grid = 20, n_ratios = 10, r = 1 .. 0.55):
+ *   t = fp16(r_i * max over the group of |w[n][k]|)  (fp32 multiply),
+ *   w_c = clip(w, -t, t), w_hat = w_c RTN-quantized and dequantized with
+ *   wq_quantize_rtn's rule (bits, symmetric; the group as one RTN group),
+ *   loss[n][g][i] = sum over m of (sum over k in g of x[m][k] (w - w_hat)[n][k])^2,
+ * with w - w_hat rounded to fp16 and the products accumulated in fp32 by
+ * the matrix cores; best[n][g] = the first index of the smallest loss, and
+ * w_out = w clipped at each group's best threshold (fp16).
+ * x fp16 [M][K] (calibration activations, M >= 1), w fp16 [N][K], w_out
+ * fp16 [N][K] (may equal w); best int32 [N][G] and losses fp32
+ * [N][G][n_ratios] are optional outputs (NULL to skip).  group_size: 32,
+ * 64, 128 or 256 (or -1 with K one of these); 1 <= n_ratios <= n_grid,
+ * n_ratios <= 1024.  x, w and w_out 16-byte aligned.  Asynchronous on
+ * `stream`.  Returns WQ_ERR_ARG for null/misaligned pointers or bad sizes,
+ * WQ_ERR_UNSUPPORTED for other bit widths or group sizes. */
+wq_status wq_awq_clip(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N, int32_t K,
+                      int32_t bits, int32_t group_size, int32_t symmetric, int32_t n_grid,
+                      int32_t n_ratios, uint16_t* w_out, int32_t* best, float* losses,
+                      void* stream);
+
 /* GPTQ ("GPTQ, AWQ and the rules of post-training quantization", section
  * "GPTQ: pay for the error with the other weights"): quantize w fp16 [N][K]
  * one input column at a time in index order, compensating each column's

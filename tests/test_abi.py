@@ -19,7 +19,7 @@ def test_library_exports_every_declared_symbol():
                 "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
                 "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m",
                 "wq_awq_search", "wq_awq_search_workspace_size", "wq_gemv_silu_mul",
-                "wq_gptq_quantize", "wq_gptq_workspace_size"}
+                "wq_gptq_quantize", "wq_gptq_workspace_size", "wq_awq_clip"}
     assert set(names) == expected
     handle = wq.lib()
     for name in names:
@@ -164,3 +164,22 @@ def test_gptq_argument_checks():
     assert call(damp=1.0) == WQ_ERR_ARG
     assert call(x=FAKE_MIS) == WQ_ERR_ARG
     assert call(wsb=size(64, 32, 256) - 1) == WQ_ERR_ARG
+
+
+def test_awq_clip_argument_checks():
+    f = wq.lib().wq_awq_clip
+
+    def call(x=FAKE, w=FAKE, M=64, N=32, K=256, bits=4, gs=128, sym=0, n_grid=20, n_ratios=10, out=FAKE):
+        return f(x, w, M, N, K, bits, gs, sym, n_grid, n_ratios, out, None, None, None)
+
+    assert call(x=None) == WQ_ERR_ARG
+    assert call(out=None) == WQ_ERR_ARG
+    assert call(M=0) == WQ_ERR_ARG
+    assert call(K=250) == WQ_ERR_ARG
+    assert call(gs=96, K=192) == WQ_ERR_UNSUPPORTED     # only 32, 64, 128, 256
+    assert call(gs=-1, K=512) == WQ_ERR_UNSUPPORTED
+    assert call(gs=100) == WQ_ERR_ARG
+    assert call(bits=5) == WQ_ERR_UNSUPPORTED
+    assert call(n_ratios=0) == WQ_ERR_ARG
+    assert call(n_ratios=21) == WQ_ERR_ARG              # more ratios than grid steps
+    assert call(out=FAKE_MIS) == WQ_ERR_ARG

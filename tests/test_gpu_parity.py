@@ -476,3 +476,73 @@ def test_gptq_llama_layer_sampled_rows():
     print(f"codes {agree:.5f} err gpu/ref {e_gpu / e_ref:.5f}")
     assert agree >= 0.997, agree
     assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)
+
+
+# ---------------------------------------------------- AWQ clip search ----
+#
+# The GPU sums fp16 matrix-core products of x and fp16(w - w_hat); the
+# oracle sums exact float64 products.  Losses agree to a relative 5e-3; the
+# chosen ratio is a minimum of the oracle's losses within that tolerance,
+# and the clipped weights are bit-exact for the chosen ratio.
+
+def _clip_inputs(seed, M, N, K):
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K, 0.05))
+    w = I.weights(seed, N, K, 0.02)
+    g = np.random.default_rng(list(seed) + [7])
+    rows, cols = g.integers(0, N, size=N // 2 + 1), g.integers(0, K, size=N // 2 + 1)
+    w[rows, cols] = (w[rows, cols].astype(np.float32) * 8).astype(np.float16)   # heavy-tailed weights
+    return x, w
+
+
+def _check_clip(x, w, bits, gs, sym, ref, w_clip, best, losses, n_grid=20):
+    L = ref["losses"]
+    lg = host(losses).astype(np.float64)
+    scale = np.max(L)
+    assert np.all(np.abs(lg - L) <= 5e-3 * L + 1e-9 * scale), float(np.max(np.abs(lg - L) / (L + 1e-30)))
+    b = host(best)
+    Lmin = L.min(axis=2)
+    Lb = np.take_along_axis(L, b[:, :, None], axis=2)[:, :, 0]
+    assert np.all(Lb <= Lmin * (1 + 1e-2) + 1e-9 * scale)
+    agree = np.mean(b == ref["best"])
+    assert agree >= 0.9, agree
+    # clipped weights: bit-exact against the clip at the chosen ratio
+    N, K = w.shape
+    gsz = K if gs == -1 else gs
+    wg = w.astype(np.float32).reshape(N, K // gsz, gsz)
+    amax = np.abs(wg).max(axis=2)
+    r = ref["ratios"][b]
+    t = (r * amax).astype(np.float16).astype(np.float32)[:, :, None]
+    want = np.clip(wg, -t, t).astype(np.float16).reshape(N, K)
+    got = host(w_clip)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    same = (b == ref["best"])
+    mask = np.repeat(same, gsz, axis=1)
+    assert np.array_equal(got.view(np.uint16)[mask], ref["w_clip"].view(np.uint16)[mask])
+    return agree
+
+
+@pytest.mark.parametrize("M,N,K,bits,gs,sym", [(96, 70, 256, 4, 128, False), (64, 64, 256, 3, 32, True),
+                                               (200, 40, 512, 2, 64, False), (128, 33, 512, 8, 256, True),
+                                               (64, 64, 128, 4, -1, False)])
+def test_awq_clip_matches_oracle(M, N, K, bits, gs, sym):
+    seed = (130, M, N, K, bits)
+    x, w = _clip_inputs(seed, M, N, K)
+    ref = O.awq_clip_search(x, w, bits, gs, symmetric=sym)
+    w_clip, best, losses = wq.awq_clip(dev(x), dev(w), bits, gs, symmetric=sym, with_losses=True)
+    agree = _check_clip(x, w, bits, gs, sym, ref, w_clip, best, losses)
+    print(f"best agreement {agree:.4f}")
+
+
+def test_awq_clip_in_place_and_llama_rows_sampled():
+    # prefill layer (K = 4096, N = 11008) on a 512-token calibration sample,
+    # clipped in place; the oracle checks sampled weight rows
+    M, N, K = 512, 11008, 4096
+    seed = (131,)
+    x, w = _clip_inputs(seed, M, N, K)
+    wd = dev(w)
+    _, best, losses = wq.awq_clip(dev(x), wd, 4, 128, out=wd, with_losses=True)
+    rows = np.array([0, 1, 5000, N - 1])
+    ref = O.awq_clip_search(x, w[rows], 4, 128)
+    sel = (torch.from_numpy(rows).cuda(),)
+    agree = _check_clip(x, w[rows], 4, 128, False, ref, wd[sel], best[sel], losses[sel])
+    print(f"best agreement {agree:.4f}")

@@ -16,7 +16,7 @@ import re
 
 __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
-    "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "gptq_quantize", "act_order_perm", "pack", "unpack",
+    "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "awq_clip", "gptq_quantize", "act_order_perm", "pack", "unpack",
     "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_max_m",
     "status_str", "version", "QuantizedLinear",
 ]
@@ -48,6 +48,7 @@ _SIG = {
     "wq_gptq_quantize": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _VP, _VP,
                                         _VP, _VP, ctypes.c_size_t, _VP]),
     "wq_gptq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "wq_awq_clip": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
 }
 _SIG["wq_gemv_silu_mul"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
@@ -201,6 +202,26 @@ def awq_search(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, sym
                                _stream(x.device)), "wq_awq_search")
     alphas = [i / (n_grid - 1) for i in range(n_grid)]
     return alphas, list(losses), int(best.value)
+
+
+def awq_clip(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, n_ratios: int = 10,
+             symmetric: bool = False, out=None, with_losses: bool = False):
+    """AWQ's clipping-threshold search on calibration activations x fp16
+    [M][K] for weights w fp16 [N][K] -> (w_clip fp16 [N][K], best int32
+    [N][G], losses fp32 [N][G][n_ratios] or None).  out may be w (in place)."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    w = _dev(w, torch.float16, "w", 2)
+    N, K = w.shape
+    if x.shape[1] != K:
+        raise ValueError("x must be [M][K] with the K of w")
+    G = _groups(K, group_size)
+    out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2)
+    best = torch.empty((N, G), dtype=torch.int32, device=w.device)
+    losses = torch.empty((N, G, n_ratios), dtype=torch.float32, device=w.device) if with_losses else None
+    _check(lib().wq_awq_clip(_ptr(x), _ptr(w), x.shape[0], N, K, bits, group_size, int(bool(symmetric)), n_grid,
+                             n_ratios, _ptr(out), _ptr(best), _ptr(losses), _stream(w.device)), "wq_awq_clip")
+    return out, best, losses
 
 
 def gptq_quantize(w, x, bits: int = 4, group_size: int = 128, symmetric: bool = False, damp: float = 0.01):

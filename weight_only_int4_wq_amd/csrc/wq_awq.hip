@@ -138,6 +138,184 @@ bool search_args_ok(int M, int N, int K, int bits, int group_size, int n_grid, i
     return true;
 }
 
+
+// ------------------------------------------------ clipping threshold search
+
+__device__ __forceinline__ float clip_h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+__device__ __forceinline__ uint16_t clip_f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// t = fp16(fp32(r * amax)): the product is rounded to fp32 first.  Left to
+// itself the compiler fuses the multiply and the conversion into one
+// mixed-precision instruction that rounds only once, which picks the other
+// fp16 neighbour when the fp32 product is an fp16 tie; the empty asm (no
+// instruction) keeps the fp32 product in a register between the two.
+__device__ __forceinline__ float clip_threshold(float r, float amax) {
+    float p = r * amax;
+    asm("" : "+v"(p));
+    return clip_h2f(clip_f2h(p));
+}
+
+// AWQ's clipping-threshold search ("AutoAWQ vs The Stack v2", paragraph on
+// scaling factors and clipping thresholds): one block per (64 output rows,
+// group of GS input channels).  For each ratio r_i = fp32(1 - i / n_grid):
+// t = fp16(r_i * max|w|) per row, the group clipped to [-t, t] and RTN-
+// quantized (wq_quantize_rtn's rule, the group as one RTN group) in
+// registers, d = w - w_hat staged in LDS as fp16, and
+//   loss[n] = sum over m of (sum over k in the group of x[m][k] d[n][k])^2
+// from fp16 matrix-core products (fp32 accumulation) over the calibration
+// rows, 64 at a time.  Thread t holds row t / 4, quarter t % 4 of the group.
+template <int BITS, bool SYM, int GS>
+__global__ void __launch_bounds__(256) awq_clip_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                       int M, int N, int K, int n_grid, int n_ratios,
+                                                       uint16_t* __restrict__ w_out, int32_t* __restrict__ best_out,
+                                                       float* __restrict__ losses) {
+    constexpr float qmax = float((1 << BITS) - 1);
+    constexpr int Q = GS / 4;      // values per thread
+    constexpr int LDD = GS + 8;    // LDS row stride (fp16)
+    __shared__ uint16_t Ds[64 * LDD];
+    __shared__ float red[2][64];
+    const int tid = threadIdx.x, rr = tid >> 2, qq = tid & 3;
+    const int n0 = blockIdx.x * 64, g = blockIdx.y, c0 = g * GS;
+    const int G = K / GS;
+    const int n = n0 + rr;
+    const bool live = n < N;
+    const uint16_t* wrow = w + (size_t)(live ? n : N - 1) * K + c0 + qq * Q;
+    float wv[Q];
+#pragma unroll
+    for (int v = 0; v < Q / 8; ++v) {
+        const u4 t = *reinterpret_cast<const u4*>(wrow + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wv[8 * v + 2 * e] = clip_h2f(uint16_t(t[e] & 0xFFFFu));
+            wv[8 * v + 2 * e + 1] = clip_h2f(uint16_t(t[e] >> 16));
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) amax = fmaxf(amax, fabsf(wv[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int wmi = wave >> 1, wn = (wave & 1) * 32;
+    float best_err = INFINITY;
+    int best_i = 0;
+    for (int i = 0; i < n_ratios; ++i) {
+        const float r = float(1.0 - double(i) / double(n_grid));
+        const float t = clip_threshold(r, amax);
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const float c = fminf(fmaxf(wv[j], -t), t);
+            mn = fminf(mn, c);
+            mx = fmaxf(mx, c);
+        }
+        mn = fminf(mn, __shfl_xor(mn, 1));
+        mn = fminf(mn, __shfl_xor(mn, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        const float s32 = SYM ? __fdiv_rn(2.0f * fmaxf(fabsf(mn), fabsf(mx)), qmax) : __fdiv_rn(mx - mn, qmax);
+        uint16_t sh = clip_f2h(s32);
+        if ((sh & 0x7FFFu) == 0) sh = 0x0400u;  // 2^-14
+        const float sc = clip_h2f(sh);
+        const float z = SYM ? float(1 << (BITS - 1)) : fminf(fmaxf(rintf(__fdiv_rn(-mn, sc)), 0.f), qmax);
+        uint16_t* drow = Ds + rr * LDD + qq * Q;
+#pragma unroll
+        for (int j = 0; j < Q; j += 2) {
+            float dd[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float c = fminf(fmaxf(wv[j + e], -t), t);
+                const float q = fminf(fmaxf(rintf(__fdiv_rn(c, sc)) + z, 0.f), qmax);
+                dd[e] = wv[j + e] - clip_h2f(clip_f2h((q - z) * sc));
+            }
+            *reinterpret_cast<uint32_t*>(drow + j) = uint32_t(clip_f2h(dd[0])) | (uint32_t(clip_f2h(dd[1])) << 16);
+        }
+        __syncthreads();
+        // squared group outputs: each wavefront a 32 (m) x 32 (n) quarter of
+        // every 64 x 64 tile of x . d^T
+        float sums[2] = {0.f, 0.f};
+        for (int m0 = 0; m0 < M; m0 += 64) {
+            f4 acc[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < GS; k0 += 32) {
+                h8 av[2], bv[2];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int m = m0 + wmi * 32 + 16 * tt + li;
+                    const h8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+                    av[tt] = m < M ? *reinterpret_cast<const h8*>(x + (size_t)m * K + c0 + k0 + 8 * lg) : zero8;
+                    bv[tt] = *reinterpret_cast<const h8*>(Ds + (wn + 16 * tt + li) * LDD + k0 + 8 * lg);
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[a], bv[b], acc[a][b], 0, 0, 0);
+            }
+            // lane holds rows 4 * lg + e of column li of each 16 x 16 block
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sums[b] = fmaf(acc[a][b][e], acc[a][b][e], sums[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            sums[b] += __shfl_xor(sums[b], 16);
+            sums[b] += __shfl_xor(sums[b], 32);
+        }
+        if (lg == 0) {
+            red[wmi][wn + li] = sums[0];
+            red[wmi][wn + 16 + li] = sums[1];
+        }
+        __syncthreads();
+        const float err = red[0][rr] + red[1][rr];
+        if (err < best_err) {
+            best_err = err;
+            best_i = i;
+        }
+        if (losses && live && qq == 0) losses[((size_t)n * G + g) * n_ratios + i] = err;
+        __syncthreads();  // Ds and red are rewritten by the next ratio
+    }
+    if (live) {
+        const float r = float(1.0 - double(best_i) / double(n_grid));
+        const float t = clip_threshold(r, amax);
+        uint16_t* orow = w_out + (size_t)n * K + c0 + qq * Q;
+#pragma unroll
+        for (int v = 0; v < Q / 8; ++v) {
+            u4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint16_t lo = clip_f2h(fminf(fmaxf(wv[8 * v + 2 * e], -t), t));
+                const uint16_t hi = clip_f2h(fminf(fmaxf(wv[8 * v + 2 * e + 1], -t), t));
+                o[e] = uint32_t(lo) | (uint32_t(hi) << 16);
+            }
+            *reinterpret_cast<u4*>(orow + 8 * v) = o;
+        }
+        if (best_out && qq == 0) best_out[(size_t)n * G + g] = best_i;
+    }
+}
+
+template <int BITS, bool SYM>
+wq_status launch_clip(int gs, const uint16_t* x, const uint16_t* w, int M, int N, int K, int n_grid, int n_ratios,
+                      uint16_t* w_out, int32_t* best, float* losses, hipStream_t s) {
+    const dim3 grid((N + 63) / 64, K / gs), block(256);
+    switch (gs) {
+        case 32: hipLaunchKernelGGL((awq_clip_kernel<BITS, SYM, 32>), grid, block, 0, s, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses); break;
+        case 64: hipLaunchKernelGGL((awq_clip_kernel<BITS, SYM, 64>), grid, block, 0, s, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses); break;
+        case 128: hipLaunchKernelGGL((awq_clip_kernel<BITS, SYM, 128>), grid, block, 0, s, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses); break;
+        default: hipLaunchKernelGGL((awq_clip_kernel<BITS, SYM, 256>), grid, block, 0, s, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses); break;
+    }
+    return wqh::launch_status();
+}
+
 }  // namespace
 
 wq_status wqh::dense_f32(const uint16_t* x, const uint16_t* w, float* y32, int M, int N, int K, hipStream_t s) {
@@ -208,4 +386,29 @@ extern "C" wq_status wq_awq_search(const uint16_t* x, const uint16_t* w, int32_t
         *best = b;
     }
     return WQ_OK;
+}
+
+extern "C" wq_status wq_awq_clip(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N, int32_t K, int32_t bits,
+                                 int32_t group_size, int32_t symmetric, int32_t n_grid, int32_t n_ratios,
+                                 uint16_t* w_out, int32_t* best, float* losses, void* stream) {
+    if (!x || !w || !w_out) return WQ_ERR_ARG;
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return WQ_ERR_UNSUPPORTED;
+    if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return WQ_ERR_ARG;
+    const int gs = group_size == -1 ? K : group_size;
+    if (gs <= 0 || gs % 32 != 0 || K % gs != 0) return WQ_ERR_ARG;
+    if (gs != 32 && gs != 64 && gs != 128 && gs != 256) return WQ_ERR_UNSUPPORTED;
+    if (n_grid < 1 || n_ratios < 1 || n_ratios > n_grid || n_ratios > 1024) return WQ_ERR_ARG;
+    if (!wqh::aligned16(x) || !wqh::aligned16(w) || !wqh::aligned16(w_out)) return WQ_ERR_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool sym = symmetric != 0;
+    switch (bits) {
+        case 2: return sym ? launch_clip<2, true>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s)
+                           : launch_clip<2, false>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s);
+        case 3: return sym ? launch_clip<3, true>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s)
+                           : launch_clip<3, false>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s);
+        case 4: return sym ? launch_clip<4, true>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s)
+                           : launch_clip<4, false>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s);
+        default: return sym ? launch_clip<8, true>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s)
+                            : launch_clip<8, false>(gs, x, w, M, N, K, n_grid, n_ratios, w_out, best, losses, s);
+    }
 }
