@@ -52,7 +52,7 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq", "silu", "gptq"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq", "silu", "gptq", "fused"], default=None,
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
                         "copies of a known size, the reference for scaling HBM byte counters; "
                         "'configs' times every case of the five synthetic workloads; 'awq' times "
@@ -364,6 +364,51 @@ def silu_leg(wq, torch, steps):
     return dict(leg="gate_up_silu", workload="llama7b gate+up 4096x(2x11008), M=1, 4-bit g128", **res)
 
 
+def fused_leg(wq, torch, steps):
+    """AWQ decode with the activation scaling and a bias fused into the GEMV
+    (wq_gemv_ex) against wq_scale_act + wq_gemv + a torch bias add, on the
+    4096 x 4096 projection and the 4096 x 22016 gate/up projection (M = 1,
+    4-bit, group 128), over a rotating pool of weight copies in graph
+    replays."""
+    res = {}
+    K = 4096
+    x = torch.from_numpy(I.activations((5, K), 1, K)).cuda()
+    s_h = wq.awq_scales(torch.from_numpy(I.activations((5, K), 64, K)).cuda(), 0.5)
+    for name, N in (("o_proj_4096x4096", 4096), ("gate_up_4096x22016", 22016)):
+        w = torch.from_numpy(I.weights((5, K, N), N, K, 0.02)).cuda()
+        L = wq.QuantizedLinear.from_float(w, bits=BITS, group_size=GROUP)
+        del w
+        b = torch.from_numpy((np.random.default_rng([5, N]).standard_normal(N) * 0.1).astype(np.float16)).cuda()
+        per_copy = L.packed.numel() * 4 + L.scales.numel() * 3
+        copies = max(2, -(-POOL_BYTES // per_copy))
+        pool = [(L.packed, L.scales, L.zeros)] + [(L.packed.clone(), L.scales.clone(), L.zeros.clone())
+                                                  for _ in range(copies - 1)]
+        y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+        xs = torch.empty_like(x)
+
+        def fused(i):
+            p, sc, z = pool[i]
+            wq.gemv_ex(x, p, sc, z, BITS, GROUP, act_scale=s_h, bias=b, out=y)
+
+        def unfused(i):
+            p, sc, z = pool[i]
+            wq.scale_act(x, s_h, out=xs)
+            wq.gemv(xs, p, sc, z, BITS, GROUP, out=y)
+            y.add_(b)
+
+        def plain(i):
+            p, sc, z = pool[i]
+            wq.gemv(x, p, sc, z, BITS, GROUP, out=y)
+
+        r = {}
+        for key, fn in (("fused_us", fused), ("scale_gemv_bias_us", unfused), ("gemv_only_us", plain)):
+            r[key] = round(timed(torch, fn, copies, max(steps, copies), copies) * 1e3, 3)
+        res[name] = r
+        del pool, L
+    return dict(leg="fused_scale_bias", workload="llama7b decode projections, M=1, 4-bit g128, AWQ x/s + bias",
+                **res)
+
+
 def awq_leg(wq, torch, repeats, cpu):
     """AWQ's alpha search (20 grid points) on the prefill layer's calibration
     batch: M = 2048, K = 4096, N = 11008, 1% outlier channels x20, 4-bit,
@@ -535,6 +580,9 @@ def main():
         return
     if args.only == "awq":
         print(json.dumps(awq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)
+        return
+    if args.only == "fused":
+        print(json.dumps(fused_leg(wq, torch, max(args.steps, 200))), flush=True)
         return
     if args.only == "gptq":
         print(json.dumps(gptq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)

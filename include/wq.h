@@ -283,6 +283,23 @@ wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed, const uint
                            int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
                            void* stream);
 
+/* The decode GEMV with its neighbours fused (the pages: fusing a block's
+ * operations into single kernels saves launches and intermediate tensors,
+ * "AutoAWQ vs The Stack v2", paragraph on fused attention and transformer
+ * blocks).  act_scale (nullable, fp16 [K], 16-byte aligned): the AWQ
+ * activation scaling x' = fp16(fp32(x) / fp32(act_scale[k])), done while the
+ * activations are staged, bit-identical to wq_scale_act followed by
+ * wq_gemv.  bias (nullable, fp16 [N]): added to the fp32 sum of each output
+ * before its rounding.  silu = 0: y fp16 [M][N] = x' . dequant(Wq)^T + bias.
+ * silu = 1: the stacked gate/up layout of wq_gemv_silu_mul (N even), y fp16
+ * [M][N/2] = silu(g + bias[j]) * (u + bias[j + N/2]).  Other arguments as
+ * wq_gemv; 1 <= M <= 4 and fp16 x of K within the 64 KB staging budget
+ * (K <= 16384 at M = 1), else WQ_ERR_UNSUPPORTED. */
+wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                     const uint8_t* zeros, const int32_t* perm, const uint16_t* act_scale,
+                     const uint16_t* bias, uint16_t* y, int32_t M, int32_t N, int32_t K,
+                     int32_t bits, int32_t group_size, int32_t silu, void* stream);
+
 /* Largest M that wq_linear sends to wq_gemv. */
 int32_t wq_gemv_max_m(void);
 

@@ -259,20 +259,23 @@ def awq_scale_act(x, s_h) -> np.ndarray:
     return (x.astype(F32) / s[None, :]).astype(F16)
 
 
-def linear_ref(x, w_hat, chunk: int = 8192) -> np.ndarray:
-    """y[m][n] = sum_k x[m][k] * w_hat[n][k] in float64 (exact definition of
-    the layer output from the dequantized weights).  Chunked over n only to
-    bound memory."""
+def linear_ref(x, w_hat, chunk: int = 8192, bias=None) -> np.ndarray:
+    """y[m][n] = sum_k x[m][k] * w_hat[n][k] (+ bias[n]) in float64 (exact
+    definition of the layer output from the dequantized weights; the
+    optional fp16 bias of a fused epilogue is added to the exact sum).
+    Chunked over n only to bound memory."""
     x64 = np.asarray(x, dtype=F16).astype(F64)
     w = np.asarray(w_hat, dtype=F16)
     N = w.shape[0]
     y = np.empty((x64.shape[0], N), dtype=F64)
     for n0 in range(0, N, chunk):
         y[:, n0:n0 + chunk] = x64 @ w[n0:n0 + chunk].astype(F64).T
+    if bias is not None:
+        y += np.asarray(bias, dtype=F16).astype(F64)[None, :]
     return y
 
 
-def silu_mul_ref(x, w_hat) -> np.ndarray:
+def silu_mul_ref(x, w_hat, bias=None) -> np.ndarray:
     """Fused gate/up projection with its activation, in float64.
 
     w_hat holds the two projections stacked, 2I rows: rows [0, I) the gate,
@@ -282,9 +285,10 @@ def silu_mul_ref(x, w_hat) -> np.ndarray:
     cut launches and intermediate tensors ("AutoAWQ vs The Stack v2",
     paragraph on fused transformer blocks); which operations, and SiLU as
     the gate's activation, is the reading taken (the gated MLP of the
-    LLaMA-shaped layers the workloads use).
+    LLaMA-shaped layers the workloads use).  An optional bias [2I] is added
+    to g and u before the activation.
     """
-    y = linear_ref(x, w_hat)
+    y = linear_ref(x, w_hat, bias=bias)
     two_i = y.shape[1]
     if two_i % 2:
         raise ValueError("the stacked gate/up weight needs an even row count")

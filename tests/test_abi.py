@@ -19,7 +19,7 @@ def test_library_exports_every_declared_symbol():
                 "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
                 "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m",
                 "wq_awq_search", "wq_awq_search_workspace_size", "wq_gemv_silu_mul",
-                "wq_gptq_quantize", "wq_gptq_workspace_size", "wq_awq_clip"}
+                "wq_gptq_quantize", "wq_gptq_workspace_size", "wq_awq_clip", "wq_gemv_ex"}
     assert set(names) == expected
     handle = wq.lib()
     for name in names:
@@ -183,3 +183,17 @@ def test_awq_clip_argument_checks():
     assert call(n_ratios=0) == WQ_ERR_ARG
     assert call(n_ratios=21) == WQ_ERR_ARG              # more ratios than grid steps
     assert call(out=FAKE_MIS) == WQ_ERR_ARG
+
+
+def test_gemv_ex_argument_checks():
+    f = wq.lib().wq_gemv_ex
+
+    def call(x=FAKE, s=None, b=None, y=FAKE, M=1, N=64, K=128, bits=4, gs=128, silu=0):
+        return f(x, FAKE, FAKE, None, None, s, b, y, M, N, K, bits, gs, silu, None)
+
+    assert call(x=None) == WQ_ERR_ARG
+    assert call(s=FAKE_MIS) == WQ_ERR_ARG          # act_scale must be 16-byte aligned
+    assert call(silu=1, N=63) == WQ_ERR_ARG
+    assert call(M=5) == WQ_ERR_UNSUPPORTED
+    assert call(bits=5) == WQ_ERR_UNSUPPORTED
+    assert call(M=0) == WQ_OK

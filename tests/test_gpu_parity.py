@@ -546,3 +546,47 @@ def test_awq_clip_in_place_and_llama_rows_sampled():
     sel = (torch.from_numpy(rows).cuda(),)
     agree = _check_clip(x, w[rows], 4, 128, False, ref, wd[sel], best[sel], losses[sel])
     print(f"best agreement {agree:.4f}")
+
+
+# ------------------------------------ fused x/s and bias (wq_gemv_ex) ----
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits,gs,sym,act,N,K", [(4, 128, False, False, 300, 4096), (4, 128, False, True, 130, 1024),
+                                                 (3, 32, True, False, 96, 512), (8, -1, True, False, 70, 256)])
+def test_gemv_ex_act_scale_is_scale_then_gemv(M, bits, gs, sym, act, N, K):
+    # the fused division reproduces wq_scale_act bit for bit, so the output
+    # equals the unfused pair's exactly; with a bias, the oracle decides
+    seed = (140, M, bits, N, K)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    g_idx = I.act_order_gidx(seed, K, gs) if act else None
+    L = gpu_layer(w, bits, gs, g_idx=g_idx, sym=sym)
+    _, s_h = O.awq_channel_scales(x, 0.5)
+    sd, xd = dev(s_h), dev(x)
+    y_ref = wq.gemv(wq.scale_act(xd, sd), L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"])
+    y = wq.gemv_ex(xd, L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"], act_scale=sd)
+    assert np.array_equal(host(y).view(np.uint16), host(y_ref).view(np.uint16))
+    b = (np.random.default_rng(list(seed)).standard_normal(N) * 0.5).astype(np.float16)
+    y_b = wq.gemv_ex(xd, L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"], act_scale=sd, bias=dev(b))
+    codes, scales, zeros = O.rtn_quantize(w, bits, gs, g_idx=g_idx, symmetric=sym)
+    w_hat = O.dequant(codes, scales, zeros, bits, gs, g_idx)
+    check_y(y_b, O.linear_ref(O.awq_scale_act(x, s_h), w_hat, bias=b), f"M={M} bits={bits}")
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_gemv_ex_silu_with_scale_and_bias(M):
+    I_, K, bits, gs = 200, 2048, 4, 128
+    seed = (141, M)
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, 2 * I_, K, 0.02)
+    L = gpu_layer(w, bits, gs)
+    _, s_h = O.awq_channel_scales(x, 0.5)
+    b = (np.random.default_rng(list(seed)).standard_normal(2 * I_) * 0.5).astype(np.float16)
+    y = wq.gemv_ex(dev(x), L["packed"], L["scales"], L["zeros"], bits, gs, act_scale=dev(s_h), bias=dev(b), silu=True)
+    codes, scales, zeros = O.rtn_quantize(w, bits, gs)
+    w_hat = O.dequant(codes, scales, zeros, bits, gs)
+    check_y(y, O.silu_mul_ref(O.awq_scale_act(x, s_h), w_hat, bias=b), f"M={M}")
+    # without scale or bias it is gemv_silu_mul exactly
+    y0 = wq.gemv_ex(dev(x), L["packed"], L["scales"], L["zeros"], bits, gs, silu=True)
+    y1 = wq.gemv_silu_mul(dev(x), L["packed"], L["scales"], L["zeros"], bits, gs)
+    assert np.array_equal(host(y0).view(np.uint16), host(y1).view(np.uint16))

@@ -683,3 +683,15 @@ def test_awq_clip_losses_match_brute_force(bits, sym):
     for i in (0, 3, 9):
         b = _clip_loss_brute(x, w, bits, 32, i, 20, sym)
         assert np.allclose(r["losses"][:, :, i], b, rtol=1e-12, atol=1e-18)
+
+
+def test_bias_closed_forms():
+    # zero activations give the bias itself; a unit activation on channel j
+    # gives column j of w_hat plus the bias; silu(b_g) * b_u for x = 0
+    w_hat = np.array([[0.5, -1.0], [2.0, 0.25], [0.0, 1.5], [-0.75, 1.0]], dtype=np.float16)
+    b = np.array([0.125, -2.0, 1.0, 3.0], dtype=np.float16)
+    assert np.array_equal(O.linear_ref(np.zeros((1, 2), np.float16), w_hat, bias=b)[0], b.astype(np.float64))
+    y = O.linear_ref(np.array([[0.0, 1.0]], np.float16), w_hat, bias=b)[0]
+    assert np.array_equal(y, np.array([-1.0 + 0.125, 0.25 - 2.0, 1.5 + 1.0, 1.0 + 3.0]))
+    z = O.silu_mul_ref(np.zeros((1, 2), np.float16), w_hat, bias=b)[0]
+    assert np.allclose(z, [0.125 / (1 + np.exp(-0.125)) * 1.0, -2.0 / (1 + np.exp(2.0)) * 3.0], rtol=1e-15)

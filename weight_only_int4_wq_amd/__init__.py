@@ -17,7 +17,7 @@ import re
 __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
     "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "awq_clip", "gptq_quantize", "act_order_perm", "pack", "unpack",
-    "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_max_m",
+    "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_ex", "gemv_max_m",
     "status_str", "version", "QuantizedLinear",
 ]
 
@@ -51,6 +51,7 @@ _SIG = {
     "wq_awq_clip": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
 }
 _SIG["wq_gemv_silu_mul"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
+_SIG["wq_gemv_ex"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _VP])
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
     _SIG[_name] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                                   _VP, ctypes.c_size_t, _VP])
@@ -396,6 +397,36 @@ def gemv_silu_mul(x, packed, scales, zeros, bits: int, group_size: int, perm=Non
         _dev(out, torch.float16, "out", 2)
     _check(lib().wq_gemv_silu_mul(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(y), M, N, K,
                                   bits, group_size, _stream(x.device)), "wq_gemv_silu_mul")
+    return y
+
+
+def gemv_ex(x, packed, scales, zeros, bits: int, group_size: int, perm=None, act_scale=None, bias=None,
+            silu: bool = False, out=None):
+    """Decode GEMV (M <= 4) with the AWQ activation scaling x' = fp16(x / s)
+    done while the activations are staged (act_scale fp16 [K]) and a bias
+    (fp16 [N]) added before the output rounding; with silu the stacked
+    gate/up epilogue of gemv_silu_mul (bias on both halves first)."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    packed = _dev(packed, torch.int32, "packed", 2)
+    scales = _dev(scales, torch.float16, "scales", 2)
+    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    act_scale = _dev(act_scale, torch.float16, "act_scale", 1, allow_none=True)
+    bias = _dev(bias, torch.float16, "bias", 1, allow_none=True)
+    M, K = x.shape
+    N = packed.shape[0]
+    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
+    if act_scale is not None and act_scale.shape[0] != K:
+        raise ValueError("act_scale must have K entries")
+    if bias is not None and bias.shape[0] != N:
+        raise ValueError("bias must have N entries")
+    cols = N // 2 if silu else N
+    y = torch.empty((M, cols), dtype=torch.float16, device=x.device) if out is None else \
+        _dev(out, torch.float16, "out", 2)
+    _check(lib().wq_gemv_ex(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(act_scale),
+                            _ptr(bias), _ptr(y), M, N, K, bits, group_size, int(bool(silu)), _stream(x.device)),
+           "wq_gemv_ex")
     return y
 
 

@@ -338,14 +338,19 @@ struct WideSlot {
     bool ok[R];
 };
 
-template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER, bool SILU = false>
+template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER, bool SILU = false, bool EX = false>
 __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const uint16_t* __restrict__ x,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
                                                           const int32_t* __restrict__ perm,
                                                           uint16_t* __restrict__ y, int M, int N, int K,
-                                                          GroupDiv gd) {
+                                                          GroupDiv gd, const uint16_t* __restrict__ act_scale,
+                                                          const uint16_t* __restrict__ bias) {
+    // EX: act_scale (nullable, fp16 [K]) divides the activations while they
+    // are staged, x' = fp16(fp32(x) / fp32(s)) exactly as the separate
+    // scaling kernel does; bias (nullable, fp16 [N]) is added to the fp32
+    // sums before the output rounding (before the SiLU with SILU).
     // LDS: u4 xs[MT][4][CPL][CNP] (activation pairs), then float2 xsum[MT][CNP]
     // (per slot: sum of x over pairs 0 and 2 of every block, over pairs 1 and 3)
     extern __shared__ u4 xs[];
@@ -421,14 +426,45 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         }
         return v;  // rows m >= M are zeroed when staged
     };
-    auto stage_slot = [&](int m, int cp, const u4 (&v)[CPL][4]) {
+    // the 8 scales of block b of chunk c (act-order: through perm)
+    auto load_sblock = [&](int c, int b) -> u4 {
+        if constexpr (GATHER) {
+            uint32_t el[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) el[i] = act_scale[perm[32 * c + 8 * b + i]];
+            return u4{el[0] | (el[1] << 16), el[2] | (el[3] << 16), el[4] | (el[5] << 16), el[6] | (el[7] << 16)};
+        } else {
+            return *reinterpret_cast<const u4*>(act_scale + 32 * c + 8 * b);
+        }
+    };
+    // x' = fp16(x / s) for 8 activations
+    auto scale_block = [&](u4 v, u4 t) -> u4 {
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w}, sv[4] = {t.x, t.y, t.z, t.w};
+        uint32_t out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __fdiv_rn(float(__builtin_bit_cast(_Float16, uint16_t(in[i]))),
+                                       float(__builtin_bit_cast(_Float16, uint16_t(sv[i]))));
+            const float hi = __fdiv_rn(float(__builtin_bit_cast(_Float16, uint16_t(in[i] >> 16))),
+                                       float(__builtin_bit_cast(_Float16, uint16_t(sv[i] >> 16))));
+            out[i] = uint32_t(__builtin_bit_cast(uint16_t, (_Float16)lo)) |
+                     (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)hi)) << 16);
+        }
+        return u4{out[0], out[1], out[2], out[3]};
+    };
+    // sv: the slot's scales (EX with act_scale only)
+    auto stage_slot = [&](int m, int cp, const u4 (&v)[CPL][4], const u4 (&sv)[CPL][4]) {
         float se = 0.f, so = 0.f;
         const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int e = 0; e < CPL; ++e)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const u4 o = m < M ? stage_block(v[e][b]) : u4{0u, 0u, 0u, 0u};
+                u4 raw = v[e][b];
+                if constexpr (EX) {
+                    if (act_scale) raw = scale_block(raw, sv[e][b]);
+                }
+                const u4 o = m < M ? stage_block(raw) : u4{0u, 0u, 0u, 0u};
                 xs[((m * 4 + b) * CPL + e) * CNP + cp] = o;
                 se = __builtin_amdgcn_fdot2(as_h2(o.x), one, se, false);
                 so = __builtin_amdgcn_fdot2(as_h2(o.y), one, so, false);
@@ -445,11 +481,20 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     constexpr int NT = 64 * kStreamWaves;
     constexpr int PRE = (MT == 1 && !GATHER) ? 2 : 1;
     u4 xpre[PRE][MT][CPL][4];
+    u4 spre[PRE][CPL][4];  // scales, loaded with the activations (EX)
     auto load_pre = [&]() {
 #pragma unroll
         for (int p = 0; p < PRE; ++p) {
             if (p > 0 && p * NT >= CNP) break;  // wave-uniform
             const int cp = min(int(threadIdx.x) + p * NT, CNP - 1);
+            if constexpr (EX) {
+                if (act_scale) {
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) spre[p][e][b] = load_sblock(cp * CPL + e, b);
+                }
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -473,17 +518,22 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         if (p > 0 && p * NT >= CNP) break;
         const int cp = min(int(threadIdx.x) + p * NT, CNP - 1);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) stage_slot(m, cp, xpre[p][m]);
+        for (int m = 0; m < MT; ++m) stage_slot(m, cp, xpre[p][m], spre[p]);
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         for (int cp = threadIdx.x + PRE * NT; cp < CNP; cp += NT) {
-            u4 v[CPL][4];
+            u4 v[CPL][4], sv[CPL][4];
 #pragma unroll
             for (int e = 0; e < CPL; ++e)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) v[e][b] = load_block(m, cp * CPL + e, b);
-            stage_slot(m, cp, v);
+                for (int b = 0; b < 4; ++b) {
+                    v[e][b] = load_block(m, cp * CPL + e, b);
+                    if constexpr (EX) {
+                        if (act_scale) sv[e][b] = load_sblock(cp * CPL + e, b);
+                    }
+                }
+            stage_slot(m, cp, v, sv);
         }
     }
 
@@ -550,11 +600,17 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                 if constexpr (SILU) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        const float g = wave_sum_last(acc[0][m]);
-                        const float u = wave_sum_last(acc[1][m]);
+                        float g = wave_sum_last(acc[0][m]);
+                        float u = wave_sum_last(acc[1][m]);
                         acc[0][m] = 0.f;
                         acc[1][m] = 0.f;
                         if (lane == 63 && m < M) {
+                            if constexpr (EX) {
+                                if (bias) {
+                                    g += float(__builtin_bit_cast(_Float16, bias[c_rg]));
+                                    u += float(__builtin_bit_cast(_Float16, bias[c_rg + half]));
+                                }
+                            }
                             const float v = g / (1.0f + expf(-g)) * u;
                             y[(size_t)m * half + c_rg] = __builtin_bit_cast(uint16_t, (_Float16)v);
                         }
@@ -565,8 +621,11 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                         const int n = c_rg * R + r;
 #pragma unroll
                         for (int m = 0; m < MT; ++m) {
-                            const float v = wave_sum_last(acc[r][m]);
+                            float v = wave_sum_last(acc[r][m]);
                             acc[r][m] = 0.f;
+                            if constexpr (EX) {
+                                if (bias && lane == 63 && n < N) v += float(__builtin_bit_cast(_Float16, bias[n]));
+                            }
                             if (lane == 63 && n < N && m < M)
                                 y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
                         }
@@ -632,9 +691,10 @@ inline size_t stream_lds_bytes(int MT, int K, int cpl) {
 #endif
 constexpr int kStreamBlocksPerCU = WQ_GEMV_BPC;
 
-template <int BITS, int MT, int R, int D, int CPL, bool SILU = false>
+template <int BITS, int MT, int R, int D, int CPL, bool SILU = false, bool EX = false>
 wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                        const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
+                        const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s,
+                        const uint16_t* act_scale = nullptr, const uint16_t* bias = nullptr) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
@@ -646,17 +706,17 @@ wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_
     const size_t lds = stream_lds_bytes(MT, K, CPL);
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros && perm)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
-                           packed, scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
+                           packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     else if (zeros)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
-                           x, packed, scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+                           x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     else if (perm)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
-                           x, packed, scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+                           x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false, SILU>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
-                           x, packed, scales, zeros, perm, y, M, N, K, gd);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
+                           x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     return wqh::launch_status();
 }
 
@@ -713,6 +773,25 @@ wq_status launch_silu(const uint16_t* x, const uint32_t* packed, const uint16_t*
     return launch_stream<BITS, 4, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
 }
 
+// The streaming kernel with the activation scaling and bias epilogue (M <= 4,
+// activations within the LDS budget).
+template <int BITS>
+wq_status launch_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                    const int32_t* perm, const uint16_t* act_scale, const uint16_t* bias, uint16_t* y, int M, int N,
+                    int K, int gs, bool silu, hipStream_t s) {
+    const int MT = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+    if (stream_lds_bytes(MT, K, 1) > kLdsBudget) return WQ_ERR_UNSUPPORTED;
+    if (silu) {
+        if (M <= 1) return launch_stream<BITS, 1, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
+        if (M <= 2) return launch_stream<BITS, 2, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
+        return launch_stream<BITS, 4, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
+    }
+    constexpr int R = WQ_GEMV_NARROW_R, D = WQ_GEMV_NARROW_D;
+    if (M <= 1) return launch_stream<BITS, 1, R, D, 1, false, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
+    if (M <= 2) return launch_stream<BITS, 2, R, D, 1, false, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
+    return launch_stream<BITS, 4, R, D, 1, false, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
+}
+
 }  // namespace
 
 namespace wqh {
@@ -754,5 +833,26 @@ extern "C" wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed,
         case 3: return launch_silu<3>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         case 4: return launch_silu<4>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         default: return launch_silu<8>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
+    }
+}
+
+extern "C" wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                                const uint8_t* zeros, const int32_t* perm, const uint16_t* act_scale,
+                                const uint16_t* bias, uint16_t* y, int32_t M, int32_t N, int32_t K, int32_t bits,
+                                int32_t group_size, int32_t silu, void* stream) {
+    int gs = 0;
+    const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
+    if (st != WQ_OK) return st;
+    if (silu && N % 2) return WQ_ERR_ARG;
+    if (act_scale && !wqh::aligned16(act_scale)) return WQ_ERR_ARG;
+    if (M > 4) return WQ_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return WQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool sl = silu != 0;
+    switch (bits) {
+        case 2: return launch_ex<2>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);
+        case 3: return launch_ex<3>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);
+        case 4: return launch_ex<4>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);
+        default: return launch_ex<8>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);
     }
 }
