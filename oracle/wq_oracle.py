@@ -438,7 +438,8 @@ def _group_params_f32(wg, bits: int, symmetric: bool):
     return s_h, z
 
 
-def gptq_quantize(w, x, bits: int, group_size: int, symmetric: bool = False, damp: float = 0.01):
+def gptq_quantize(w, x, bits: int, group_size: int, symmetric: bool = False, damp: float = 0.01,
+                  act_order: bool = False):
     """GPTQ ("GPTQ, AWQ and the rules of post-training quantization",
     section "GPTQ: pay for the error with the other weights"): columns are
     quantized one at a time in a fixed order (index order), and each
@@ -459,8 +460,15 @@ def gptq_quantize(w, x, bits: int, group_size: int, symmetric: bool = False, dam
     of the mean diagonal), the dead-channel rule and groups taken from the
     running weights at their first column are the published method's
     choices, read as the plain ones.
-    Returns a dict like quantize_linear_layer's (codes, scales, zeros,
-    w_hat; no act-order).
+    act_order (the pages' desc_act option for GPTQ, "AutoGPTQ vs The Stack
+    v2", first capability paragraph): the columns are processed in
+    descending order of diag(H) after the dead-channel rule (stable for
+    ties), groups are formed in that processing order, and g_idx[k] = (the
+    position of channel k in that order) // group_size maps each channel to
+    its group; the reading taken is the published method's.
+    Returns a dict like quantize_linear_layer's (codes in original channel
+    order, scales and zeros [N][G] by group, w_hat), plus g_idx int32 [K]
+    (act_order only, else None).
     """
     qmax = _check_bits(bits)
     W = np.asarray(w, dtype=F16).astype(F64).copy()
@@ -473,6 +481,11 @@ def gptq_quantize(w, x, bits: int, group_size: int, symmetric: bool = False, dam
     dead = np.diag(H) == 0
     H[dead, dead] = 1.0
     W[:, dead] = 0.0
+    perm = np.arange(K)
+    if act_order:
+        perm = np.argsort(-np.diag(H), kind="stable")
+        W = W[:, perm]
+        H = H[np.ix_(perm, perm)]
     H[np.diag_indices(K)] += damp * np.mean(np.diag(H))
     U = np.linalg.cholesky(np.linalg.inv(H)).T
     G = K // gs
@@ -495,7 +508,16 @@ def gptq_quantize(w, x, bits: int, group_size: int, symmetric: bool = False, dam
         w_hat[:, i] = wq
         err = (W[:, i] - wq.astype(F64)) / U[i, i]
         W[:, i + 1:] -= np.outer(err, U[i, i + 1:])
-    return dict(codes=codes, scales=scales, zeros=zeros, w_hat=w_hat)
+    if not act_order:
+        return dict(codes=codes, scales=scales, zeros=zeros, w_hat=w_hat, g_idx=None)
+    # back to the original channel order
+    codes_o = np.empty_like(codes)
+    w_hat_o = np.empty_like(w_hat)
+    codes_o[:, perm] = codes
+    w_hat_o[:, perm] = w_hat
+    g_idx = np.empty(K, dtype=np.int32)
+    g_idx[perm] = np.arange(K) // gs
+    return dict(codes=codes_o, scales=scales, zeros=zeros, w_hat=w_hat_o, g_idx=g_idx)
 
 
 def f64_to_f16_nearest(v: float) -> np.float16:

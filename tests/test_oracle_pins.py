@@ -695,3 +695,41 @@ def test_bias_closed_forms():
     assert np.array_equal(y, np.array([-1.0 + 0.125, 0.25 - 2.0, 1.5 + 1.0, 1.0 + 3.0]))
     z = O.silu_mul_ref(np.zeros((1, 2), np.float16), w_hat, bias=b)[0]
     assert np.allclose(z, [0.125 / (1 + np.exp(-0.125)) * 1.0, -2.0 / (1 + np.exp(2.0)) * 3.0], rtol=1e-15)
+
+
+def test_gptq_act_order_with_diagonal_hessian_is_rtn_in_rank_groups():
+    # x = diag(c) with distinct c: H is diagonal, nothing is carried, the
+    # processing order is c descending, and the result is plain RTN with the
+    # groups given by that order
+    K, N, gs = 128, 24, 32
+    seed = (51,)
+    w = I.weights(seed, N, K, 0.02)
+    c = 1.0 + np.random.default_rng([51]).permutation(K) / 16.0      # distinct, exact in fp16
+    x = np.diag(c).astype(np.float16)
+    r = O.gptq_quantize(w, x, 4, gs, act_order=True)
+    order = np.argsort(-c, kind="stable")
+    want_g = np.empty(K, dtype=np.int32)
+    want_g[order] = np.arange(K) // gs
+    assert np.array_equal(r["g_idx"], want_g)
+    rc, rs, rz = O.rtn_quantize(w, 4, gs, g_idx=want_g)
+    assert np.array_equal(r["codes"], rc)
+    assert np.array_equal(r["scales"].view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(r["zeros"], rz)
+
+
+def test_gptq_act_order_is_fixed_order_on_the_permuted_problem():
+    # act-order GPTQ equals fixed-order GPTQ run on the inputs permuted into
+    # descending diag(H), mapped back to the original channels
+    K, N, M, gs = 96, 16, 256, 32
+    seed = (52,)
+    g = np.random.default_rng([52])
+    x = (I.correlated_activations(seed, M, K).astype(np.float32) * (0.5 + g.random(K))).astype(np.float16)
+    w = I.weights(seed, N, K, 0.02)
+    r = O.gptq_quantize(w, x, 3, gs, act_order=True)
+    d = np.sum(x.astype(np.float64) ** 2, axis=0)
+    order = np.argsort(-d, kind="stable")
+    f = O.gptq_quantize(w[:, order], x[:, order], 3, gs)
+    assert np.array_equal(r["codes"][:, order], f["codes"])
+    assert np.array_equal(r["scales"].view(np.uint16), f["scales"].view(np.uint16))
+    assert np.array_equal(r["g_idx"][order], np.arange(K) // gs)
+    assert not np.array_equal(order, np.arange(K))
