@@ -475,11 +475,11 @@ def gptq_leg(wq, torch, repeats, cpu):
     x_np = I.correlated_activations(seed, M, K)
     w_np = I.weights(seed, N, K, 0.02)
     x, w = torch.from_numpy(x_np).cuda(), torch.from_numpy(w_np).cuda()
-    codes, scales, zeros = wq.gptq_quantize(w, x, BITS, GROUP)  # warm-up
+    codes, scales, zeros, _ = wq.gptq_quantize(w, x, BITS, GROUP)  # warm-up
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(repeats):
-        codes, scales, zeros = wq.gptq_quantize(w, x, BITS, GROUP)
+        codes, scales, zeros, _ = wq.gptq_quantize(w, x, BITS, GROUP)
     torch.cuda.synchronize()
     gpu_s = (time.perf_counter() - t0) / repeats
 

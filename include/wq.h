@@ -167,18 +167,24 @@ wq_status wq_awq_clip(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N
  * x fp16 [M][K] (calibration activations, M a multiple of 32); outputs as
  * wq_quantize_rtn's: codes uint8 [N][K], scales fp16 [N][G], zeros uint8
  * [N][G] (NULL when symmetric, required otherwise), ready for wq_pack.
+ * act_order (desc_act, "AutoGPTQ vs The Stack v2", first capability
+ * paragraph): the columns are processed in descending order of the Hessian
+ * diagonal (after the dead-channel rule, before damping; ties by channel
+ * index), groups are formed in that order, and g_idx int32 [K] (required
+ * with act_order, ignored otherwise) receives each channel's group, the
+ * group map wq_act_order_perm and wq_pack take; codes stay in channel order.
  * group_size: -1 (one group per row) or a multiple of 32 dividing K that
  * divides 64 or is a multiple of 64.  0 <= damp < 1 (0.01 is usual).
  * workspace: device memory of at least wq_gptq_workspace_size(M, N, K)
- * bytes, 16-byte aligned (about 5 K^2 floats plus N*K floats); codes 16-byte
+ * bytes, 16-byte aligned (about 5 K^2 floats plus 5 N*K bytes); codes 16-byte
  * aligned.
  * Asynchronous on `stream`.  Returns WQ_ERR_ARG for null/misaligned
  * pointers, bad sizes or a short workspace, WQ_ERR_UNSUPPORTED for other
  * bit widths. */
 wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N, int32_t K,
                            int32_t bits, int32_t group_size, int32_t symmetric, double damp,
-                           uint8_t* codes, uint16_t* scales, uint8_t* zeros, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           int32_t act_order, uint8_t* codes, uint16_t* scales, uint8_t* zeros,
+                           int32_t* g_idx, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace wq_gptq_quantize needs (0 for invalid sizes). */
 size_t wq_gptq_workspace_size(int32_t M, int32_t N, int32_t K);

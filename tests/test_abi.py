@@ -149,8 +149,8 @@ def test_gptq_argument_checks():
     assert size(0, 32, 256) == 0
 
     def call(x=FAKE, w=FAKE, M=64, N=32, K=256, bits=4, gs=128, sym=0, damp=0.01, zeros=FAKE, ws=FAKE,
-             wsb=1 << 30):
-        return L.wq_gptq_quantize(x, w, M, N, K, bits, gs, sym, damp, FAKE, FAKE, zeros, ws, wsb, None)
+             wsb=1 << 30, act=0, g_idx=None):
+        return L.wq_gptq_quantize(x, w, M, N, K, bits, gs, sym, damp, act, FAKE, FAKE, zeros, g_idx, ws, wsb, None)
 
     assert call(x=None) == WQ_ERR_ARG
     assert call(ws=None) == WQ_ERR_ARG
@@ -164,6 +164,7 @@ def test_gptq_argument_checks():
     assert call(damp=1.0) == WQ_ERR_ARG
     assert call(x=FAKE_MIS) == WQ_ERR_ARG
     assert call(wsb=size(64, 32, 256) - 1) == WQ_ERR_ARG
+    assert call(act=1) == WQ_ERR_ARG               # act-order needs the g_idx output
 
 
 def test_awq_clip_argument_checks():

@@ -45,8 +45,8 @@ _SIG = {
     "wq_awq_search": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP,
                                      ctypes.c_size_t, _VP]),
     "wq_awq_search_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32, _I32]),
-    "wq_gptq_quantize": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _VP, _VP,
-                                        _VP, _VP, ctypes.c_size_t, _VP]),
+    "wq_gptq_quantize": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_double, _I32, _VP,
+                                        _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     "wq_gptq_workspace_size": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "wq_awq_clip": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
 }
@@ -225,10 +225,12 @@ def awq_clip(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, n_rat
     return out, best, losses
 
 
-def gptq_quantize(w, x, bits: int = 4, group_size: int = 128, symmetric: bool = False, damp: float = 0.01):
+def gptq_quantize(w, x, bits: int = 4, group_size: int = 128, symmetric: bool = False, damp: float = 0.01,
+                  act_order: bool = False):
     """GPTQ of fp16 w [N][K] on calibration activations x fp16 [M][K] ->
-    (codes u8 [N][K], scales fp16 [N][G], zeros u8 [N][G] or None), the
-    layout quantize_rtn returns."""
+    (codes u8 [N][K], scales fp16 [N][G], zeros u8 [N][G] or None, g_idx
+    int32 [K] or None), the layout quantize_rtn returns plus the act-order
+    group map."""
     torch = _torch()
     w = _dev(w, torch.float16, "w", 2)
     x = _dev(x, torch.float16, "x", 2)
@@ -244,10 +246,11 @@ def gptq_quantize(w, x, bits: int = 4, group_size: int = 128, symmetric: bool = 
     codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     scales = torch.empty((N, G), dtype=torch.float16, device=w.device)
     zeros = None if symmetric else torch.empty((N, G), dtype=torch.uint8, device=w.device)
+    g_idx = torch.empty((K,), dtype=torch.int32, device=w.device) if act_order else None
     _check(lib().wq_gptq_quantize(_ptr(x), _ptr(w), M, N, K, bits, group_size, int(bool(symmetric)), float(damp),
-                                  _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(ws), need, _stream(w.device)),
-           "wq_gptq_quantize")
-    return codes, scales, zeros
+                                  int(bool(act_order)), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(ws),
+                                  need, _stream(w.device)), "wq_gptq_quantize")
+    return codes, scales, zeros, g_idx
 
 
 def act_order_perm(g_idx, group_size: int):

@@ -56,9 +56,10 @@ __global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* __restri
 }
 
 // Dead channels and damping, one block, fixed order: dead[k] = (H[k][k] == 0),
-// those diagonals become 1, then every diagonal gains damp * mean(diag).
+// those diagonals become 1 (copied to diag, the act-order key), then every
+// diagonal gains damp * mean(diag).
 __global__ void __launch_bounds__(1024) damp_kernel(float* __restrict__ H, int K, float damp,
-                                                    uint8_t* __restrict__ dead) {
+                                                    uint8_t* __restrict__ dead, float* __restrict__ diag) {
     __shared__ float part[1024];
     float acc = 0.f;
     for (int k = threadIdx.x; k < K; k += 1024) {
@@ -67,6 +68,7 @@ __global__ void __launch_bounds__(1024) damp_kernel(float* __restrict__ H, int K
         dead[k] = z ? 1 : 0;
         if (z) d = 1.f;
         H[(size_t)k * K + k] = d;
+        diag[k] = d;
         acc += d;
     }
     part[threadIdx.x] = acc;
@@ -92,12 +94,59 @@ __global__ void __launch_bounds__(256) fill_kernel(float* __restrict__ p, long l
     for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < n; t += (long long)gridDim.x * 256) p[t] = v;
 }
 
-// W32[n][k] = fp32(w[n][k]), 0 on dead channels.
-__global__ void __launch_bounds__(256) init_w_kernel(const uint16_t* __restrict__ w, const uint8_t* __restrict__ dead,
-                                                     long long total, int K, float* __restrict__ W32) {
+// Processing order: perm[i] = the channel of rank i.  With act-order the
+// rank is the position in descending diag order, ties by channel index (a
+// stable sort); otherwise the identity.
+__global__ void __launch_bounds__(256) rank_kernel(const float* __restrict__ diag, int K, int act_order,
+                                                   int32_t* __restrict__ perm) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= K) return;
+    if (!act_order) {
+        perm[k] = k;
+        return;
+    }
+    const float d = diag[k];
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+        const float e = diag[j];
+        rank += (e > d || (e == d && j < k)) ? 1 : 0;
+    }
+    perm[rank] = k;
+}
+
+// dst[i][j] = H[perm[K-1-i]][perm[K-1-j]]: the Hessian in processing order,
+// index-reversed.
+__global__ void __launch_bounds__(256) permute_reverse_kernel(const float* __restrict__ H,
+                                                              const int32_t* __restrict__ perm, int K,
+                                                              float* __restrict__ dst) {
+    const long long total = (long long)K * K;
     for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
-        const int k = int(t % K);
-        W32[t] = dead[k] ? 0.f : h2f(w[t]);
+        const int i = int(t / K), j = int(t % K);
+        dst[t] = H[(size_t)perm[K - 1 - i] * K + perm[K - 1 - j]];
+    }
+}
+
+// W32[n][i] = fp32(w[n][perm[i]]), 0 on dead channels (columns in
+// processing order).
+__global__ void __launch_bounds__(256) init_w_kernel(const uint16_t* __restrict__ w, const uint8_t* __restrict__ dead,
+                                                     const int32_t* __restrict__ perm, long long total, int K,
+                                                     float* __restrict__ W32) {
+    for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
+        const long long n = t / K;
+        const int k = perm[int(t % K)];
+        W32[t] = dead[k] ? 0.f : h2f(w[n * K + k]);
+    }
+}
+
+// codes[n][perm[i]] = cp[n][i] and g_idx[perm[i]] = i / gs (act-order).
+__global__ void __launch_bounds__(256) unpermute_kernel(const uint8_t* __restrict__ cp, const int32_t* __restrict__ perm,
+                                                        long long total, int K, int gs, uint8_t* __restrict__ codes,
+                                                        int32_t* __restrict__ g_idx) {
+    for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
+        const long long n = t / K;
+        const int i = int(t % K);
+        codes[n * K + perm[i]] = cp[t];
+        if (n == 0) g_idx[perm[i]] = i / gs;
     }
 }
 
@@ -394,7 +443,7 @@ __global__ void __launch_bounds__(64) gptq_block_kernel(float* __restrict__ W32,
 
 // Workspace regions (256-byte aligned).
 struct GptqLayout {
-    size_t xt, H, A, L, Li, U, W32, Err, dead, total;
+    size_t xt, H, A, L, Li, U, W32, Err, dead, diag, perm, cperm, total;
 };
 
 GptqLayout gptq_layout(int M, int N, int K) {
@@ -415,6 +464,9 @@ GptqLayout gptq_layout(int M, int N, int K) {
     Ly.W32 = take(size_t(N) * K * 4);
     Ly.Err = take(size_t(N) * kGptqOuter * 4);
     Ly.dead = take(size_t(K));
+    Ly.diag = take(size_t(K) * 4);
+    Ly.perm = take(size_t(K) * 4);
+    Ly.cperm = take(size_t(N) * K);
     Ly.total = off;
     return Ly;
 }
@@ -479,9 +531,10 @@ extern "C" size_t wq_gptq_workspace_size(int32_t M, int32_t N, int32_t K) {
 
 extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N, int32_t K,
                                       int32_t bits, int32_t group_size, int32_t symmetric, double damp,
-                                      uint8_t* codes, uint16_t* scales, uint8_t* zeros, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      int32_t act_order, uint8_t* codes, uint16_t* scales, uint8_t* zeros,
+                                      int32_t* g_idx, void* workspace, size_t workspace_bytes, void* stream) {
     if (!x || !w || !codes || !scales || !workspace) return WQ_ERR_ARG;
+    if (act_order && !g_idx) return WQ_ERR_ARG;
     if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return WQ_ERR_UNSUPPORTED;
     int gs = 0;
     if (!gptq_args_ok(M, N, K, bits, group_size, &gs)) return WQ_ERR_ARG;
@@ -502,6 +555,9 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     float* W32 = reinterpret_cast<float*>(ws + Ly.W32);
     float* Err = reinterpret_cast<float*>(ws + Ly.Err);
     uint8_t* dead = reinterpret_cast<uint8_t*>(ws + Ly.dead);
+    float* diag = reinterpret_cast<float*>(ws + Ly.diag);
+    int32_t* perm = reinterpret_cast<int32_t*>(ws + Ly.perm);
+    uint8_t* cdst = act_order ? reinterpret_cast<uint8_t*>(ws + Ly.cperm) : codes;
     const long long KK = (long long)K * K;
     auto grid_for = [](long long n) { return dim3(unsigned(std::min<long long>((n + 255) / 256, 65536))); };
     wq_status st;
@@ -510,11 +566,13 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     hipLaunchKernelGGL(transpose_kernel, dim3((K + 31) / 32, (M + 31) / 32), dim3(256), 0, s, x, M, K, xt);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
     if ((st = wqh::dense_f32(xt, xt, H, K, K, M, s)) != WQ_OK) return st;
-    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, s, H, K, float(damp), dead);
+    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, s, H, K, float(damp), dead, diag);
+    hipLaunchKernelGGL(rank_kernel, dim3((K + 255) / 256), dim3(256), 0, s, diag, K, act_order ? 1 : 0, perm);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
 
-    // L L^T = P H P and Li = L^-1 (recursive halving), U = P Li P
-    hipLaunchKernelGGL(reverse_kernel, grid_for(KK), dim3(256), 0, s, H, K, A);
+    // L L^T = P H' P and Li = L^-1 (recursive halving), U = P Li P, with H'
+    // the Hessian in processing order
+    hipLaunchKernelGGL(permute_reverse_kernel, grid_for(KK), dim3(256), 0, s, H, perm, K, A);
     hipLaunchKernelGGL(fill_kernel, grid_for(KK), dim3(256), 0, s, L, KK, 0.f);
     hipLaunchKernelGGL(fill_kernel, grid_for(KK), dim3(256), 0, s, Li, KK, 0.f);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
@@ -525,17 +583,21 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
 
     // the column walk with lazy block updates
     const long long NK = (long long)N * K;
-    hipLaunchKernelGGL(init_w_kernel, grid_for(NK), dim3(256), 0, s, w, dead, NK, K, W32);
+    hipLaunchKernelGGL(init_w_kernel, grid_for(NK), dim3(256), 0, s, w, dead, perm, NK, K, W32);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
     const bool sym = symmetric != 0;
     switch (bits) {
-        case 2: return sym ? gptq_blocks<2, true>(W32, U, N, K, gs, codes, scales, zeros, Err, s)
-                           : gptq_blocks<2, false>(W32, U, N, K, gs, codes, scales, zeros, Err, s);
-        case 3: return sym ? gptq_blocks<3, true>(W32, U, N, K, gs, codes, scales, zeros, Err, s)
-                           : gptq_blocks<3, false>(W32, U, N, K, gs, codes, scales, zeros, Err, s);
-        case 4: return sym ? gptq_blocks<4, true>(W32, U, N, K, gs, codes, scales, zeros, Err, s)
-                           : gptq_blocks<4, false>(W32, U, N, K, gs, codes, scales, zeros, Err, s);
-        default: return sym ? gptq_blocks<8, true>(W32, U, N, K, gs, codes, scales, zeros, Err, s)
-                            : gptq_blocks<8, false>(W32, U, N, K, gs, codes, scales, zeros, Err, s);
+        case 2: st = sym ? gptq_blocks<2, true>(W32, U, N, K, gs, cdst, scales, zeros, Err, s)
+                         : gptq_blocks<2, false>(W32, U, N, K, gs, cdst, scales, zeros, Err, s); break;
+        case 3: st = sym ? gptq_blocks<3, true>(W32, U, N, K, gs, cdst, scales, zeros, Err, s)
+                         : gptq_blocks<3, false>(W32, U, N, K, gs, cdst, scales, zeros, Err, s); break;
+        case 4: st = sym ? gptq_blocks<4, true>(W32, U, N, K, gs, cdst, scales, zeros, Err, s)
+                         : gptq_blocks<4, false>(W32, U, N, K, gs, cdst, scales, zeros, Err, s); break;
+        default: st = sym ? gptq_blocks<8, true>(W32, U, N, K, gs, cdst, scales, zeros, Err, s)
+                          : gptq_blocks<8, false>(W32, U, N, K, gs, cdst, scales, zeros, Err, s); break;
     }
+    if (st != WQ_OK || !act_order) return st;
+    // back to the original channel order, and the group map
+    hipLaunchKernelGGL(unpermute_kernel, grid_for(NK), dim3(256), 0, s, cdst, perm, NK, K, gs, codes, g_idx);
+    return wqh::launch_status();
 }
