@@ -71,8 +71,8 @@ def layer_bytes(M, K, N, bits=BITS, group=GROUP):
 # Device sources each timed kernel is built from (kernel file + shared headers).
 GEMV_SOURCES = ("wq_gemv.hip", "wq_common.h")
 GEMM_SOURCES = ("wq_gemm_large.hip", "wq_gemm_common.h", "wq_common.h")
-GEMV_KERNEL = "gemv_stream_kernel<4,1,2,2,1,true,false>"
-GEMM_KERNEL = "gemm_large_kernel<4,true,true>"
+GEMV_KERNEL = "gemv_stream_kernel<4,1,2,2,1,true,false,false,false>"
+GEMM_KERNEL = "gemm_large_kernel<4,true,true,false>"
 
 
 def src_sha(parts):

@@ -31,7 +31,7 @@ namespace {
 
 using namespace wq;
 
-template <int BITS, int BM, int BN, int WAVES_M, int NST, bool HAS_Z>
+template <int BITS, int BM, int BN, int WAVES_M, int NST, bool HAS_Z, bool PART>
 __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ x,
                                                    const uint32_t* __restrict__ packed,
                                                    const uint16_t* __restrict__ scales,
@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
 
     // ---- epilogue: lane holds rows 4*lg + r of column li of each 16x16
     // tile; fp16 y, or this range's fp32 partial
-    float* pr = part ? part + (size_t)blockIdx.y * M * N : nullptr;
+    float* pr = PART ? part + (size_t)blockIdx.y * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + wm * WM + i * 16 + 4 * lg + r;
                 if (row < M && col < N) {
-                    if (pr)
+                    if constexpr (PART)
                         pr[(size_t)row * N + col] = acc[i][j][r];
                     else
                         y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
@@ -277,11 +277,18 @@ wq_status launch_tile(const uint16_t* x, const uint32_t* packed, const uint16_t*
     const bool split = plan.splits > 1;
     const dim3 grid(tiles, plan.splits);
     float* pp = out32 ? out32 : (split ? part : nullptr);
-    if (zeros)
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true>), grid, dim3(256), 0, s, x, packed, scales,
-                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    // PART is a template flag: the plain fp16 epilogue carries no branch
+    if (zeros && pp)
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true, true>), grid, dim3(256), 0, s, x, packed,
+                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    else if (zeros)
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, true, false>), grid, dim3(256), 0, s, x, packed,
+                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    else if (pp)
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false, true>), grid, dim3(256), 0, s, x, packed,
+                           scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else
-        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false>), grid, dim3(256), 0, s, x, packed,
+        hipLaunchKernelGGL((gemm_kernel<BITS, BM, BN, WAVES_M, NST, false, false>), grid, dim3(256), 0, s, x, packed,
                            scales, zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     const wq_status st = wqh::launch_status();
     if (st != WQ_OK || !split) return st;

@@ -64,7 +64,7 @@ __device__ __forceinline__ uint32_t zero_pair_nat(uint32_t z) {
         return zero_pair(z);
 }
 
-template <int BITS, bool HAS_Z, bool FAST>
+template <int BITS, bool HAS_Z, bool FAST, bool PART>
 __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
@@ -322,7 +322,7 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
 
     // ---- epilogue: acc[i][j][r] is row 32i + 8(r/4) + 4h + r%4, column
     // 32j + c of the wavefront's tile; fp16 y, or this range's fp32 partial
-    float* pr = part ? part + (size_t)blockIdx.y * M * N : nullptr;
+    float* pr = PART ? part + (size_t)blockIdx.y * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -332,7 +332,7 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
                 if (row < M && col < N) {
-                    if (pr)
+                    if constexpr (PART)
                         pr[(size_t)row * N + col] = acc[i][j][r];
                     else
                         y[(size_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][r]);
@@ -354,12 +354,20 @@ wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* sc
     const bool split = plan.splits > 1;
     const dim3 grid(tiles, plan.splits);
     float* pp = out32 ? out32 : (split ? part : nullptr);
-    if (fast)
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true>), grid, dim3(256), 0, s, x, packed, scales, zeros, y,
-                           M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    // PART (fp32 partials or the fp32 output) is a template flag so that the
+    // plain fp16 epilogue carries no per-element branch
+    if (fast && pp)
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true, true>), grid, dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    else if (fast)
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true, false>), grid, dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+    else if (pp)
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false, true>), grid, dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false>), grid, dim3(256), 0, s, x, packed, scales, zeros,
-                           y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false, false>), grid, dim3(256), 0, s, x, packed, scales,
+                           zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     const wq_status st = wqh::launch_status();
     if (st != WQ_OK || !split) return st;
     return wqh::splitk_reduce(part, plan.splits, M, N, y, s);
