@@ -621,3 +621,22 @@ def test_gptq_act_order_matches_oracle(M, N, K, bits, gs, sym):
     packed, perm = wq.pack(codes, bits, gs, g_idx=g_idx)
     y = wq.gemv(dev(x[:2]), packed, scales, zeros, bits, gs, perm=perm)
     check_y(y, O.linear_ref(x[:2], w_hat), "act-order GPTQ layer")
+
+
+@pytest.mark.parametrize("M", [1, 3, 64])
+@pytest.mark.parametrize("act", [False, True])
+def test_quantized_linear_awq_layer(M, act):
+    # the convenience class: AWQ fold + RTN (+ act-order) at set-up; at call
+    # time x/s fused into the GEMV for M <= 4, a separate pass before the GEMM
+    K, N, bits, gs = 1024, 300, 4, 128
+    seed = (150, M, int(act))
+    x = I.with_outliers(I.activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    g_idx = I.act_order_gidx(seed, K, gs) if act else None
+    _, s_h = O.awq_channel_scales(x, 0.5)
+    layer = wq.QuantizedLinear.from_float(dev(w), bits=bits, group_size=gs, g_idx=None if g_idx is None else dev(g_idx),
+                                          act_scale=dev(s_h))
+    ws = torch.empty((max(1, wq.workspace_size(M, N, K, bits, act)),), dtype=torch.uint8, device="cuda")
+    y = layer(dev(x), workspace=ws)
+    ref = O.quantize_linear_layer(O.awq_fold_weight(w, s_h), bits, gs, g_idx=g_idx)
+    check_y(y, O.linear_ref(O.awq_scale_act(x, s_h), ref["w_hat"]), f"M={M} act={act}")

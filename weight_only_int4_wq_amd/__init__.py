@@ -462,6 +462,13 @@ class QuantizedLinear:
 
     def __call__(self, x, out=None, workspace=None, kernel: str = "linear"):
         if self.act_scale is not None:
+            M = x.shape[0]
+            mt = 1 if M <= 1 else 2 if M <= 2 else 4
+            fits = 1 <= M <= 4 and mt * (2 * self.K + (self.K // 32) * 8) <= 64 * 1024
+            if kernel in ("linear", "gemv") and fits:
+                # decode: the division happens while the GEMV stages x
+                return gemv_ex(x, self.packed, self.scales, self.zeros, self.bits, self.group_size, perm=self.perm,
+                               act_scale=self.act_scale, out=out)
             x = scale_act(x, self.act_scale)
         fn = {"linear": linear, "gemv": gemv, "gemm": gemm}[kernel]
         return fn(x, self.packed, self.scales, self.zeros, self.bits, self.group_size, self.perm, out, workspace)
