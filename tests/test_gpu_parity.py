@@ -640,3 +640,35 @@ def test_quantized_linear_awq_layer(M, act):
     y = layer(dev(x), workspace=ws)
     ref = O.quantize_linear_layer(O.awq_fold_weight(w, s_h), bits, gs, g_idx=g_idx)
     check_y(y, O.linear_ref(O.awq_scale_act(x, s_h), ref["w_hat"]), f"M={M} act={act}")
+
+
+def test_awq_then_gptq_composition():
+    # AWQ's rescaling (alpha from the search) followed by GPTQ on the
+    # rescaled layer: the same codes as the oracle's composition, and a
+    # lower output error than either AWQ + RTN or GPTQ alone
+    M, N, K, bits, gs = 256, 96, 512, 3, 128
+    seed = (124,)
+    x = I.with_outliers(I.correlated_activations(seed, M, K), I.outlier_channels(seed, K))
+    w = I.weights(seed, N, K, 0.02)
+    xd, wd = dev(x), dev(w)
+    alphas, _, best = wq.awq_search(xd, wd, bits, gs)
+    s_d = wq.awq_scales(xd, alphas[best])
+    wf, xf = wq.awq_fold(wd, s_d), wq.scale_act(xd, s_d)
+    codes, scales, zeros, _ = wq.gptq_quantize(wf, xf, bits, gs)
+    _, s_h = O.awq_channel_scales(x, alphas[best])
+    wf_o, xf_o = O.awq_fold_weight(w, s_h), O.awq_scale_act(x, s_h)
+    assert np.array_equal(host(wf).view(np.uint16), wf_o.view(np.uint16))
+    ref = O.gptq_quantize(wf_o, xf_o, bits, gs)
+    c = host(codes)
+    agree = np.mean(c == ref["codes"])
+    assert agree >= 0.99, agree
+    y0 = x.astype(np.float64) @ w.astype(np.float64).T
+
+    def err(xq, w_hat):
+        return np.linalg.norm(xq.astype(np.float64) @ w_hat.astype(np.float64).T - y0)
+
+    e_both = err(xf_o, O.dequant(c, host(scales), host(zeros), bits, gs))
+    e_awq_rtn = err(xf_o, O.quantize_linear_layer(wf_o, bits, gs)["w_hat"])
+    e_gptq = err(x, O.gptq_quantize(w, x, bits, gs)["w_hat"])
+    print(f"codes {agree:.4f} err awq+gptq {e_both:.4g} awq+rtn {e_awq_rtn:.4g} gptq {e_gptq:.4g}")
+    assert e_both < e_awq_rtn and e_both < e_gptq
