@@ -173,8 +173,8 @@ wq_status wq_awq_clip(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N
  * index), groups are formed in that order, and g_idx int32 [K] (required
  * with act_order, ignored otherwise) receives each channel's group, the
  * group map wq_act_order_perm and wq_pack take; codes stay in channel order.
- * group_size: -1 (one group per row) or a multiple of 32 dividing K that
- * divides 64 or is a multiple of 64.  0 <= damp < 1 (0.01 is usual).
+ * group_size: -1 (one group per row, any K) or a multiple of 32 dividing K
+ * that divides 64 or is a multiple of 64.  0 <= damp < 1 (0.01 is usual).
  * workspace: device memory of at least wq_gptq_workspace_size(M, N, K)
  * bytes, 16-byte aligned (about 5 K^2 floats plus 5 N*K bytes); codes 16-byte
  * aligned.

@@ -434,7 +434,8 @@ def test_gptq_with_diagonal_hessian_is_rtn(bits, gs, sym):
 @pytest.mark.parametrize("M,N,K,bits,gs,sym", [(256, 96, 384, 4, 128, False), (128, 70, 256, 3, 32, True),
                                                (512, 64, 320, 8, -1, True), (256, 130, 448, 2, 64, False),
                                                (96, 64, 512, 4, 128, False), (256, 40, 384, 4, 192, False),
-                                               (256, 40, 768, 4, 256, False)])
+                                               (256, 40, 768, 4, 256, False), (128, 50, 352, 4, 32, False),
+                                               (64, 17, 96, 8, -1, True)])
 def test_gptq_matches_oracle(M, N, K, bits, gs, sym):
     seed = (121, M, N, K, bits)
     x = I.correlated_activations(seed, M, K)

@@ -477,7 +477,8 @@ bool gptq_args_ok(int M, int N, int K, int bits, int group_size, int* gs_out) {
     const int gs = group_size == -1 ? K : group_size;
     if (gs <= 0 || gs % 32 != 0 || K % gs != 0) return false;
     // a group never straddles a lazy-update block unless it starts at one
-    if (!(kGptqB % gs == 0 || gs % kGptqB == 0)) return false;
+    // (one group per row starts at column 0 only)
+    if (gs != K && !(kGptqB % gs == 0 || gs % kGptqB == 0)) return false;
     *gs_out = gs;
     return true;
 }
