@@ -42,7 +42,8 @@
  *    a failed check returns a status and enqueues nothing.  No entry point
  *    throws or aborts.  WQ_ERR_HIP reports a failed HIP call (launch or
  *    copy); the stream's earlier work is unaffected.
- *  - Alignment: x, y, packed and workspace pointers must be 16-byte aligned.
+ *  - Alignment: x, y, packed, perm and workspace pointers must be 16-byte
+ *    aligned.
  */
 #ifndef WQ_H
 #define WQ_H

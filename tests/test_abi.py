@@ -73,6 +73,7 @@ def test_matmul_argument_checks(name):
     assert _mm(name, x=FAKE_MIS) == WQ_ERR_ARG
     assert _mm(name, y=FAKE_MIS) == WQ_ERR_ARG
     assert _mm(name, packed=FAKE_MIS) == WQ_ERR_ARG
+    assert _mm(name, M=2, perm=FAKE_MIS, ws=FAKE, wsb=1 << 20) == WQ_ERR_ARG
     # empty problems are valid and enqueue nothing
     assert _mm(name, M=0) == WQ_OK
     assert _mm(name, N=0) == WQ_OK

@@ -411,6 +411,7 @@ extern "C" wq_status wq_gemm(const uint16_t* x, const uint32_t* packed, const ui
     int gs = 0;
     const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
     if (st != WQ_OK) return st;
+    if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;
     if (M == 0 || N == 0) return WQ_OK;
     if (workspace && !wqh::aligned16(workspace)) return WQ_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -23,6 +23,8 @@ namespace {
 
 using namespace wq;
 
+typedef int32_t i4 __attribute__((ext_vector_type(4)));
+
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const uint32_t* p, uint32_t* w) {
     if constexpr (BITS == 4) {
@@ -357,6 +359,10 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int CN = K / 32;       // chunks per row
     const int CNP = CN / CPL;    // slots per row
     float2* xsum = reinterpret_cast<float2*>(xs + MT * 4 * CN);
+    // act-order: the activations in their natural order, copied with
+    // coalesced loads, then gathered through perm from LDS
+    u4* xnat4 = xs + MT * 4 * CN + (MT * CNP + 1) / 2;
+    const uint16_t* xnat = reinterpret_cast<const uint16_t*>(xnat4);
     const int lane = threadIdx.x & 63;
     // wave-uniform (readfirstlane): row-group positions and row addresses
     // live in scalar registers, lanes only add their chunk offset
@@ -416,11 +422,14 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         const size_t xrow = (size_t)(m < M ? m : 0) * K;
         u4 v;
         if constexpr (GATHER) {
-            uint32_t el[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) el[i] = x[xrow + perm[32 * c + 8 * b + i]];
-            v.x = el[0] | (el[1] << 16); v.y = el[2] | (el[3] << 16);
-            v.z = el[4] | (el[5] << 16); v.w = el[6] | (el[7] << 16);
+            const i4 p0 = *reinterpret_cast<const i4*>(perm + 32 * c + 8 * b);
+            const i4 p1 = *reinterpret_cast<const i4*>(perm + 32 * c + 8 * b + 4);
+            const uint16_t* xr = xnat + (size_t)m * K;
+            v.x = uint32_t(xr[p0.x]) | (uint32_t(xr[p0.y]) << 16);
+            v.y = uint32_t(xr[p0.z]) | (uint32_t(xr[p0.w]) << 16);
+            v.z = uint32_t(xr[p1.x]) | (uint32_t(xr[p1.y]) << 16);
+            v.w = uint32_t(xr[p1.z]) | (uint32_t(xr[p1.w]) << 16);
+            (void)xrow;
         } else {
             v = *reinterpret_cast<const u4*>(x + xrow + 32 * c + 8 * b);
         }
@@ -509,7 +518,15 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     // keep the staging arithmetic below every weight load (it would wait for
     // the activations and hold back the loads scheduled after it)
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (GATHER) load_pre();
+    if constexpr (GATHER) {
+        const int K8 = K / 8;
+        for (int i = threadIdx.x; i < MT * K8; i += NT) {
+            const int m = i / K8;
+            xnat4[i] = m < M ? reinterpret_cast<const u4*>(x)[(size_t)m * K8 + (i - m * K8)] : u4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+        load_pre();
+    }
 
     // ---- stage activations (pair order) and per-slot sums, once per block;
     // threads past the last slot rewrite it with the same values
@@ -665,8 +682,9 @@ wq_status launch_cfg(const uint16_t* x, const uint32_t* packed, const uint16_t* 
 
 // LDS bytes the streaming kernel stages: fp16 activations plus one fp32 sum
 // per slot, per activation row.
-inline size_t stream_lds_bytes(int MT, int K, int cpl) {
-    return size_t(MT) * (size_t(K) * 2 + size_t(K / (32 * cpl)) * 8);
+inline size_t stream_lds_bytes(int MT, int K, int cpl, bool gather = false) {
+    const size_t sums = (size_t(MT) * (K / (32 * cpl)) + 1) / 2 * 16;
+    return size_t(MT) * K * 2 + sums + (gather ? size_t(MT) * K * 2 : 0);
 }
 
 // Launch shape of the streaming kernel (blocks per CU; rows per wavefront
@@ -703,7 +721,7 @@ wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_
     const int n_groups = SILU ? N / 2 : (N + R - 1) / R;
     int blocks = (n_groups + kStreamWaves - 1) / kStreamWaves;
     if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
-    const size_t lds = stream_lds_bytes(MT, K, CPL);
+    const size_t lds = stream_lds_bytes(MT, K, CPL, perm != nullptr);
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros && perm)
         hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
@@ -741,9 +759,10 @@ wq_status launch_mt(const uint16_t* x, const uint32_t* packed, const uint16_t* s
         return launch_cfg<BITS, MT, 1, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
     } else {
         constexpr int CPL = WQ_GEMV_CPL;
-        if (CPL > 1 && K % (32 * CPL) == 0 && gs % (32 * CPL) == 0 && stream_lds_bytes(MT, K, CPL) <= kLdsBudget)
+        if (CPL > 1 && K % (32 * CPL) == 0 && gs % (32 * CPL) == 0 &&
+            stream_lds_bytes(MT, K, CPL, perm != nullptr) <= kLdsBudget)
             return launch_stream_cpl<BITS, MT, CPL>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
-        if (stream_lds_bytes(MT, K, 1) <= kLdsBudget)
+        if (stream_lds_bytes(MT, K, 1, perm != nullptr) <= kLdsBudget)
             return launch_stream_cpl<BITS, MT, 1>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         if (N < 8192) return launch_cfg<BITS, MT, 1, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         if (N < 16384) return launch_cfg<BITS, MT, 2, 2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
@@ -767,7 +786,7 @@ template <int BITS>
 wq_status launch_silu(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s) {
     const int MT = M <= 1 ? 1 : M <= 2 ? 2 : 4;
-    if (stream_lds_bytes(MT, K, 1) > kLdsBudget) return WQ_ERR_UNSUPPORTED;
+    if (stream_lds_bytes(MT, K, 1, perm != nullptr) > kLdsBudget) return WQ_ERR_UNSUPPORTED;
     if (M <= 1) return launch_stream<BITS, 1, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
     if (M <= 2) return launch_stream<BITS, 2, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
     return launch_stream<BITS, 4, 2, 2, 1, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
@@ -780,7 +799,7 @@ wq_status launch_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* s
                     const int32_t* perm, const uint16_t* act_scale, const uint16_t* bias, uint16_t* y, int M, int N,
                     int K, int gs, bool silu, hipStream_t s) {
     const int MT = M <= 1 ? 1 : M <= 2 ? 2 : 4;
-    if (stream_lds_bytes(MT, K, 1) > kLdsBudget) return WQ_ERR_UNSUPPORTED;
+    if (stream_lds_bytes(MT, K, 1, perm != nullptr) > kLdsBudget) return WQ_ERR_UNSUPPORTED;
     if (silu) {
         if (M <= 1) return launch_stream<BITS, 1, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
         if (M <= 2) return launch_stream<BITS, 2, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
@@ -807,6 +826,7 @@ extern "C" wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const ui
     int gs = 0;
     const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
     if (st != WQ_OK) return st;
+    if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;  // read 16 bytes at a time
     if (M > 16) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -824,6 +844,7 @@ extern "C" wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed,
     int gs = 0;
     const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
     if (st != WQ_OK) return st;
+    if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;  // read 16 bytes at a time
     if (N % 2) return WQ_ERR_ARG;
     if (M > 4) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
@@ -843,6 +864,7 @@ extern "C" wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const
     int gs = 0;
     const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
     if (st != WQ_OK) return st;
+    if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;  // read 16 bytes at a time
     if (silu && N % 2) return WQ_ERR_ARG;
     if (act_scale && !wqh::aligned16(act_scale)) return WQ_ERR_ARG;
     if (M > 4) return WQ_ERR_UNSUPPORTED;
