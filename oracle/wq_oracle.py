@@ -24,14 +24,20 @@ What it computes, and where each step comes from:
 * AWQ's search for alpha: a 20-point grid on [0, 1], each point scored by
   the squared output error of the rescaled, quantized layer against the
   original layer on the calibration activations (same section).
+* AWQ's clipping-threshold search: per group, a symmetric threshold from a
+  grid of shrink ratios of the group's largest magnitude, scored by the
+  group's output error on the calibration activations ("AutoAWQ vs The
+  Stack v2", paragraph on scaling factors and clipping thresholds).
 * GPTQ: columns quantized in a fixed order, each rounding error compensated
   on the remaining columns through the upper Cholesky factor of the
   inverse Hessian of the layer's reconstruction loss ("GPTQ, AWQ and the
   rules of post-training quantization", section "GPTQ: pay for the error
-  with the other weights").
+  with the other weights"); optionally in act-order (descending Hessian
+  diagonal, the desc_act option of "AutoGPTQ vs The Stack v2").
 * Packing of codes into 32-bit words, dequantization (q - z) * s and the
-  product y = x . dequant(Wq)^T.  Weights stay packed and are dequantized on
-  the fly inside the product: "AutoAWQ vs The Stack v2", paragraph on the
+  product y = x . dequant(Wq)^T (+ an optional bias; the gated form
+  silu(x . Wg^T) * (x . Wu^T) of a fused epilogue).  Weights stay packed
+  and are dequantized on the fly inside the product: "AutoAWQ vs The Stack v2", paragraph on the
   WQLinear_* GEMM/GEMV modules, and "AutoAWQ vs Unsloth", the matching
   paragraph.  The product is defined exactly, so the oracle writes that
   definition out in float64.
