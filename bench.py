@@ -16,6 +16,9 @@ in one HIP graph (plus one for a remainder, so exactly --steps steps run)
 and timed with HIP events on the stream the graphs replay on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --only decode|prefill|copy|configs|silu|fused|awq|gptq
+(one leg, one JSON line: the profiler runs, every synthetic workload, the
+fused decode epilogues, AWQ's alpha and clipping searches, GPTQ)
 """
 
 from __future__ import annotations
@@ -56,7 +59,9 @@ def parse():
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
                         "copies of a known size, the reference for scaling HBM byte counters; "
                         "'configs' times every case of the five synthetic workloads; 'awq' times "
-                        "AWQ's alpha search on the prefill layer; 'silu' the fused gate/up decode projection")
+                        "AWQ's alpha and clipping searches on the prefill layer; 'silu' the fused gate/up "
+                        "decode projection; 'fused' the GEMV with x/s and bias fused; 'gptq' GPTQ of the "
+                        "prefill layer")
     return p.parse_args()
 
 
