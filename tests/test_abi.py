@@ -199,3 +199,35 @@ def test_gemv_ex_argument_checks():
     assert call(M=5) == WQ_ERR_UNSUPPORTED
     assert call(bits=5) == WQ_ERR_UNSUPPORTED
     assert call(M=0) == WQ_OK
+
+
+def _declared_names():
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "wq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(wq_[a-z_0-9]+)\s*\(", src, flags=re.M))
+
+
+def test_header_declares_exactly_the_exports():
+    declared = _declared_names()
+    assert len(declared) >= 20
+    assert declared == set(wq.exported_names())
+
+
+def test_header_is_plain_c(tmp_path):
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "use_wq.c"
+    names = sorted(_declared_names())
+    src.write_text("#include <wq.h>\n#include <stdio.h>\ntypedef void (*fn_t)(void);\nint main(void) {\n"
+                   "    const fn_t fns[] = {\n" + "".join(f"        (fn_t)&{n},\n" for n in names) + "    };\n"
+                   "    printf(\"%d\\n\", (int)(sizeof fns / sizeof fns[0]));\n    return 0;\n}\n")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", inc, "-c", str(src), "-o",
+                        str(tmp_path / "use_wq.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
