@@ -365,6 +365,7 @@ def test_awq_search_then_quantize_prefill():
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("bits,gs,sym,act,I_,K", [(4, 128, False, False, 100, 4096), (4, 128, False, True, 64, 1024),
+                                                 (4, 128, False, True, 96, 4096),
                                                  (3, 32, True, False, 40, 512), (8, -1, True, False, 33, 256)])
 def test_gemv_silu_mul_matches_oracle(M, bits, gs, sym, act, I_, K):
     seed = (111, M, bits, I_, K)

@@ -359,7 +359,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int CN = K / 32;       // chunks per row
     const int CNP = CN / CPL;    // slots per row
     float2* xsum = reinterpret_cast<float2*>(xs + MT * 4 * CN);
-    // act-order: the activations in their natural order, copied with
+    // act-order: one activation row in its natural order, copied with
     // coalesced loads, then gathered through perm from LDS
     u4* xnat4 = xs + MT * 4 * CN + (MT * CNP + 1) / 2;
     const uint16_t* xnat = reinterpret_cast<const uint16_t*>(xnat4);
@@ -424,7 +424,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         if constexpr (GATHER) {
             const i4 p0 = *reinterpret_cast<const i4*>(perm + 32 * c + 8 * b);
             const i4 p1 = *reinterpret_cast<const i4*>(perm + 32 * c + 8 * b + 4);
-            const uint16_t* xr = xnat + (size_t)m * K;
+            const uint16_t* xr = xnat;  // the row being staged
             v.x = uint32_t(xr[p0.x]) | (uint32_t(xr[p0.y]) << 16);
             v.y = uint32_t(xr[p0.z]) | (uint32_t(xr[p0.w]) << 16);
             v.z = uint32_t(xr[p1.x]) | (uint32_t(xr[p1.y]) << 16);
@@ -519,38 +519,53 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     // the activations and hold back the loads scheduled after it)
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (GATHER) {
+        // one activation row at a time: its natural order into LDS with
+        // coalesced loads, then gathered through perm while staging
         const int K8 = K / 8;
-        for (int i = threadIdx.x; i < MT * K8; i += NT) {
-            const int m = i / K8;
-            xnat4[i] = m < M ? reinterpret_cast<const u4*>(x)[(size_t)m * K8 + (i - m * K8)] : u4{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();
-        load_pre();
-    }
-
-    // ---- stage activations (pair order) and per-slot sums, once per block;
-    // threads past the last slot rewrite it with the same values
+        for (int m = 0; m < MT; ++m) {
+            for (int i = threadIdx.x; i < K8; i += NT)
+                xnat4[i] = m < M ? reinterpret_cast<const u4*>(x)[(size_t)m * K8 + i] : u4{0u, 0u, 0u, 0u};
+            __syncthreads();
+            for (int cp = threadIdx.x; cp < CNP; cp += NT) {
+                u4 v[CPL][4], sv[CPL][4];
 #pragma unroll
-    for (int p = 0; p < PRE; ++p) {
-        if (p > 0 && p * NT >= CNP) break;
-        const int cp = min(int(threadIdx.x) + p * NT, CNP - 1);
+                for (int e = 0; e < CPL; ++e)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) stage_slot(m, cp, xpre[p][m], spre[p]);
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        for (int cp = threadIdx.x + PRE * NT; cp < CNP; cp += NT) {
-            u4 v[CPL][4], sv[CPL][4];
-#pragma unroll
-            for (int e = 0; e < CPL; ++e)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    v[e][b] = load_block(m, cp * CPL + e, b);
-                    if constexpr (EX) {
-                        if (act_scale) sv[e][b] = load_sblock(cp * CPL + e, b);
+                    for (int b = 0; b < 4; ++b) {
+                        v[e][b] = load_block(m, cp * CPL + e, b);
+                        if constexpr (EX) {
+                            if (act_scale) sv[e][b] = load_sblock(cp * CPL + e, b);
+                        }
                     }
-                }
-            stage_slot(m, cp, v, sv);
+                stage_slot(m, cp, v, sv);
+            }
+            __syncthreads();  // the row buffer is rewritten for the next row
+        }
+    } else {
+        // ---- stage activations (pair order) and per-slot sums, once per
+        // block; threads past the last slot rewrite it with the same values
+#pragma unroll
+        for (int p = 0; p < PRE; ++p) {
+            if (p > 0 && p * NT >= CNP) break;
+            const int cp = min(int(threadIdx.x) + p * NT, CNP - 1);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) stage_slot(m, cp, xpre[p][m], spre[p]);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            for (int cp = threadIdx.x + PRE * NT; cp < CNP; cp += NT) {
+                u4 v[CPL][4], sv[CPL][4];
+#pragma unroll
+                for (int e = 0; e < CPL; ++e)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        v[e][b] = load_block(m, cp * CPL + e, b);
+                        if constexpr (EX) {
+                            if (act_scale) sv[e][b] = load_sblock(cp * CPL + e, b);
+                        }
+                    }
+                stage_slot(m, cp, v, sv);
+            }
         }
     }
 
@@ -684,7 +699,7 @@ wq_status launch_cfg(const uint16_t* x, const uint32_t* packed, const uint16_t* 
 // per slot, per activation row.
 inline size_t stream_lds_bytes(int MT, int K, int cpl, bool gather = false) {
     const size_t sums = (size_t(MT) * (K / (32 * cpl)) + 1) / 2 * 16;
-    return size_t(MT) * K * 2 + sums + (gather ? size_t(MT) * K * 2 : 0);
+    return size_t(MT) * K * 2 + sums + (gather ? size_t(K) * 2 : 0);
 }
 
 // Launch shape of the streaming kernel (blocks per CU; rows per wavefront
