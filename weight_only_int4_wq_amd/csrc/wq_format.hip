@@ -67,6 +67,42 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ c
     }
 }
 
+// Packing without a permutation from 16-byte aligned codes: the chunk's 32
+// codes arrive in two 16-byte loads and its words leave in vector stores
+// (same bitstream as pack_kernel).
+template <int BITS>
+__global__ void __launch_bounds__(256) pack_vec_kernel(const uint8_t* __restrict__ codes, int K, int N,
+                                                       uint32_t* __restrict__ packed) {
+    const int chunks = K / 32;
+    const long long total = (long long)N * chunks;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (long long)gridDim.x * blockDim.x) {
+        const u4* src = reinterpret_cast<const u4*>(codes + (size_t)t * 32);  // row n, chunk c = t
+        const u4 a = src[0], b = src[1];
+        const uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t words[BITS];
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) words[i] = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const uint32_t q = (in[j >> 2] >> (8 * (j & 3))) & ((1u << BITS) - 1u);
+            const int bit = j * BITS;
+            words[bit >> 5] |= q << (bit & 31);
+            if ((bit & 31) + BITS > 32) words[(bit >> 5) + 1] |= q >> (32 - (bit & 31));
+        }
+        uint32_t* dst = packed + (size_t)t * BITS;
+        if constexpr (BITS == 4) {
+            *reinterpret_cast<u4*>(dst) = u4{words[0], words[1], words[2], words[3]};
+        } else if constexpr (BITS == 8) {
+            reinterpret_cast<u4*>(dst)[0] = u4{words[0], words[1], words[2], words[3]};
+            reinterpret_cast<u4*>(dst)[1] = u4{words[4], words[5], words[6], words[7]};
+        } else {
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) dst[i] = words[i];
+        }
+    }
+}
+
 // ----------------------------------------------- unpack and dequant -----
 // One thread per (row, chunk): decode with the same routine the GEMV/GEMM
 // kernels use and scatter back to original channel order.
@@ -137,8 +173,12 @@ struct PackRun {
     static wq_status run(const uint8_t* codes, const int32_t* perm, int K, int N, uint32_t* packed,
                          hipStream_t s) {
         const long long work = (long long)N * (K / 32);
-        hipLaunchKernelGGL(pack_kernel<BITS>, dim3(grid_for(work, 256)), dim3(256), 0, s, codes, perm, K,
-                           N, packed);
+        if (!perm && wqh::aligned16(codes))
+            hipLaunchKernelGGL(pack_vec_kernel<BITS>, dim3(grid_for(work, 256)), dim3(256), 0, s, codes, K, N,
+                               packed);
+        else
+            hipLaunchKernelGGL(pack_kernel<BITS>, dim3(grid_for(work, 256)), dim3(256), 0, s, codes, perm, K,
+                               N, packed);
         return wqh::launch_status();
     }
 };
