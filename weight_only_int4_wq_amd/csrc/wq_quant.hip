@@ -188,12 +188,86 @@ __global__ void __launch_bounds__(1024) awq_scales_kernel(const uint16_t* __rest
     s_out[k] = h;
 }
 
+// The same statistics with 16-byte loads (K a multiple of 64, x 16-byte
+// aligned): thread t reads channels 8 (t % 8) .. + 7 of the block's 64 on
+// rows t / 8, + 128, ... (one 16-byte load per row); the 8 row phases of a
+// wavefront are added by lane shuffles and the 16 wavefronts' sums in
+// wavefront order (fixed order, float64 throughout).
+__device__ __forceinline__ double shfl_xor_f64(double v, int mask) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(b)), mask));
+    const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(b >> 32)), mask));
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+__global__ void __launch_bounds__(1024) awq_scales_vec_kernel(const uint16_t* __restrict__ x, int M, int K,
+                                                              double alpha, uint16_t* __restrict__ s_out) {
+    __shared__ double part[16][64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int cg = t & 7, rp = t >> 3;
+    const int k0 = blockIdx.x * 64 + 8 * cg;
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int m = rp; m < M; m += 128) {
+        const u4 v = *reinterpret_cast<const u4*>(x + (size_t)m * K + k0);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += fabs(double(h2f(uint16_t(w4[i] & 0xFFFFu))));
+            acc[2 * i + 1] += fabs(double(h2f(uint16_t(w4[i] >> 16))));
+        }
+    }
+    // lanes cg, cg + 8, ..., cg + 56 of a wavefront hold the same channels
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        acc[j] += shfl_xor_f64(acc[j], 8);
+        acc[j] += shfl_xor_f64(acc[j], 16);
+        acc[j] += shfl_xor_f64(acc[j], 32);
+    }
+    if (lane < 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part[wave][8 * cg + j] = acc[j];
+    }
+    __syncthreads();
+    if (t >= 64) return;
+    const int k = blockIdx.x * 64 + t;
+    double a = part[0][t];
+    for (int i = 1; i < 16; ++i) a += part[i][t];
+    a /= double(M);
+    const double sv = (alpha == 0.5) ? sqrt(a) : pow(a, alpha);
+    uint16_t h = f64_to_f16_rne(sv);
+    if ((h & 0x7FFFu) == 0) h = 0x0400u;
+    s_out[k] = h;
+}
+
 __global__ void __launch_bounds__(256) awq_fold_kernel(const uint16_t* __restrict__ w, const uint16_t* __restrict__ s,
                                                        long long total, int K, uint16_t* __restrict__ w_out) {
     for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
          t += (long long)gridDim.x * blockDim.x) {
         const int k = int(t % K);
         w_out[t] = f2h(h2f(w[t]) * h2f(s[k]));  // exact fp32 product, one rounding
+    }
+}
+
+// The fold with 16-byte loads and stores (K a multiple of 8, pointers
+// 16-byte aligned): 8 weights per thread, the same exact products.
+__global__ void __launch_bounds__(256) awq_fold_vec_kernel(const uint16_t* __restrict__ w,
+                                                           const uint16_t* __restrict__ s, long long total8, int K,
+                                                           uint16_t* __restrict__ w_out) {
+    const int K8 = K / 8;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total8;
+         t += (long long)gridDim.x * blockDim.x) {
+        const int k0 = int(t % K8) * 8;
+        const u4 v = reinterpret_cast<const u4*>(w)[t];
+        const u4 sv = *reinterpret_cast<const u4*>(s + k0);
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w}, sc[4] = {sv.x, sv.y, sv.z, sv.w};
+        uint32_t out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = h2f(uint16_t(in[i])) * h2f(uint16_t(sc[i]));
+            const float hi = h2f(uint16_t(in[i] >> 16)) * h2f(uint16_t(sc[i] >> 16));
+            out[i] = uint32_t(f2h(lo)) | (uint32_t(f2h(hi)) << 16);  // exact fp32 products, one rounding
+        }
+        reinterpret_cast<u4*>(w_out)[t] = u4{out[0], out[1], out[2], out[3]};
     }
 }
 
@@ -274,8 +348,12 @@ extern "C" wq_status wq_awq_scales(const uint16_t* x, int32_t M, int32_t K, doub
                                    void* stream) {
     if (!x || !s_out || M <= 0 || K <= 0) return WQ_ERR_ARG;
     if (!(alpha >= 0.0 && alpha <= 1.0)) return WQ_ERR_ARG;
-    hipLaunchKernelGGL(awq_scales_kernel, dim3((K + 63) / 64), dim3(1024), 0, static_cast<hipStream_t>(stream), x,
-                       int(M), int(K), alpha, s_out);
+    if (K % 64 == 0 && wqh::aligned16(x))
+        hipLaunchKernelGGL(awq_scales_vec_kernel, dim3(K / 64), dim3(1024), 0, static_cast<hipStream_t>(stream), x,
+                           int(M), int(K), alpha, s_out);
+    else
+        hipLaunchKernelGGL(awq_scales_kernel, dim3((K + 63) / 64), dim3(1024), 0, static_cast<hipStream_t>(stream),
+                           x, int(M), int(K), alpha, s_out);
     return wqh::launch_status();
 }
 
@@ -283,8 +361,12 @@ extern "C" wq_status wq_awq_fold(const uint16_t* w, const uint16_t* s, int32_t N
                                  void* stream) {
     if (!w || !s || !w_out || N <= 0 || K <= 0) return WQ_ERR_ARG;
     const long long total = (long long)N * K;
-    hipLaunchKernelGGL(awq_fold_kernel, dim3(grid_for(total, 256)), dim3(256), 0, static_cast<hipStream_t>(stream), w,
-                       s, total, int(K), w_out);
+    if (K % 8 == 0 && wqh::aligned16(w) && wqh::aligned16(s) && wqh::aligned16(w_out))
+        hipLaunchKernelGGL(awq_fold_vec_kernel, dim3(grid_for(total / 8, 256, 8192)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), w, s, total / 8, int(K), w_out);
+    else
+        hipLaunchKernelGGL(awq_fold_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), w, s, total, int(K), w_out);
     return wqh::launch_status();
 }
 
