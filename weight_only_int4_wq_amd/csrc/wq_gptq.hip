@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256) unpermute_kernel(const uint8_t* __restric
 template <bool TB>
 __global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float alpha, const float* __restrict__ A,
                                                     int lda, const float* __restrict__ B, int ldb, float beta,
-                                                    float* __restrict__ C, int ldc) {
+                                                    float* __restrict__ C, int ldc, int lower_only) {
     constexpr int LD = 36;  // row stride in floats: 16-byte aligned, spreads banks
     __shared__ float As[64 * LD];
     __shared__ float Bs[64 * LD];
@@ -169,6 +169,8 @@ __global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float 
     const int li = lane & 15, lg = lane >> 4;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
     const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    // lower_only: C's strictly upper 64 x 64 tiles are never read again
+    if (lower_only && j0 > i0 + 63) return;
     f4 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -231,11 +233,11 @@ __global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float 
 
 template <bool TB>
 wq_status sgemm(int M, int N, int Kd, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
-                float* C, int ldc, hipStream_t s) {
+                float* C, int ldc, hipStream_t s, bool lower_only = false) {
     if (M <= 0 || N <= 0) return WQ_OK;
     if (Kd % 4 != 0) return WQ_ERR_ARG;
     hipLaunchKernelGGL((sgemm_kernel<TB>), dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, M, N, Kd, alpha, A,
-                       lda, B, ldb, beta, C, ldc);
+                       lda, B, ldb, beta, C, ldc, lower_only ? 1 : 0);
     return wqh::launch_status();
 }
 
@@ -335,7 +337,9 @@ wq_status chol_inverse(float* A, float* L, float* Li, int K, int n0, int n, floa
     wq_status st;
     if ((st = chol_inverse(A, L, Li, K, n0, h, tmp, s)) != WQ_OK) return st;
     if ((st = sgemm<true>(n2, h, h, 1.f, A + (size_t)r0 * K + n0, K, Li11, K, 0.f, L21, K, s)) != WQ_OK) return st;
-    if ((st = sgemm<true>(n2, n2, h, -1.f, L21, K, L21, K, 1.f, A + (size_t)r0 * K + r0, K, s)) != WQ_OK) return st;
+    // the trailing update: only its lower triangle is read afterwards
+    if ((st = sgemm<true>(n2, n2, h, -1.f, L21, K, L21, K, 1.f, A + (size_t)r0 * K + r0, K, s, true)) != WQ_OK)
+        return st;
     if ((st = chol_inverse(A, L, Li, K, r0, n2, tmp, s)) != WQ_OK) return st;
     // tmp = L21 . Li11 (n2 x h), then Li21 = -Li22 . tmp
     if ((st = sgemm<false>(n2, h, h, 1.f, L21, K, Li11, K, 0.f, tmp, h, s)) != WQ_OK) return st;
