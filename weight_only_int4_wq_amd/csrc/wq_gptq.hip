@@ -10,7 +10,8 @@
 //   H[k][k] = 1 and a zero weight column; H += damp * mean(diag H) * I.
 //   U = the upper Cholesky factor of H^-1 (H^-1 = U^T U), computed as
 //   U = P L^-1 P with L L^T = P H P and P the index reversal, the factor
-//   and its inverse by recursive halving (large fp32 matrix-core products).
+//   and its inverse together, right-looking in blocks of 64 (fp32 matrix-core
+//   products for everything but the 64 x 64 diagonal blocks).
 //   For each block of 64 columns, one thread per weight row walks the
 //   block's columns in order: at the first column of a group, the RTN scale
 //   and zero from the group's running weights; the column's code and
@@ -31,7 +32,6 @@ using namespace wq;
 __device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-constexpr int kCholB = 32;   // Cholesky / inverse block
 constexpr int kGptqB = 64;   // columns walked by one launch
 constexpr int kGptqOuter = 256;  // outer lazy-update block
 
@@ -81,17 +81,15 @@ __global__ void __launch_bounds__(1024) damp_kernel(float* __restrict__ H, int K
     for (int k = threadIdx.x; k < K; k += 1024) H[(size_t)k * K + k] += lambda;
 }
 
-// dst[i][j] = src[K-1-i][K-1-j] (both K x K float32).
-__global__ void __launch_bounds__(256) reverse_kernel(const float* __restrict__ src, int K, float* __restrict__ dst) {
+// dst[i][j] = src[K-1-i][K-1-j] for j >= i, 0 below the diagonal (both
+// K x K float32; only src's lower triangle is read).
+__global__ void __launch_bounds__(256) upper_reverse_kernel(const float* __restrict__ src, int K,
+                                                            float* __restrict__ dst) {
     const long long total = (long long)K * K;
     for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
         const int i = int(t / K), j = int(t % K);
-        dst[t] = src[(size_t)(K - 1 - i) * K + (K - 1 - j)];
+        dst[t] = j >= i ? src[(size_t)(K - 1 - i) * K + (K - 1 - j)] : 0.f;
     }
-}
-
-__global__ void __launch_bounds__(256) fill_kernel(float* __restrict__ p, long long n, float v) {
-    for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < n; t += (long long)gridDim.x * 256) p[t] = v;
 }
 
 // Processing order: perm[i] = the channel of rank i.  With act-order the
@@ -150,28 +148,26 @@ __global__ void __launch_bounds__(256) unpermute_kernel(const uint8_t* __restric
     }
 }
 
-// C = beta * C + alpha * A . opB in float32 on the matrix cores
-// (v_mfma_f32_16x16x4f32), opB(k, j) = TB ? B[j][k] : B[k][j]; leading
-// dimensions lda, ldb, ldc; Kd a multiple of 4.  A 64 x 64 output tile per
-// 256-thread block, each wavefront a 32 x 32 quarter (2 x 2 instructions);
-// k in steps of 32 through LDS, A as As[m][k] and opB as Bs[n][k] so that a
-// lane reads four consecutive k of its row with one 16-byte load.  The
-// four instructions of one such load take k = 4 * (lane / 16) + t for
-// t = 0..3 in A and B alike: a permutation of the sum's terms.
+// acc = A . opB for one 64 x 64 tile in float32 on the matrix cores
+// (v_mfma_f32_16x16x4f32), opB(k, j) = TB ? B[j][k] : B[k][j]; A points at
+// the tile's first row, B at its first column (TB: first row); mlim and nlim
+// are the rows and columns of the tile that exist, Kd (a multiple of 4) the
+// depth.  256 threads, each wavefront a 32 x 32 quarter (2 x 2
+// instructions); k in steps of 32 through LDS, A as As[m][k] and opB as
+// Bs[n][k] so that a lane reads four consecutive k of its row with one
+// 16-byte load.  The four instructions of one such load take
+// k = 4 * (lane / 16) + t for t = 0..3 in A and B alike: a permutation of
+// the sum's terms.
+constexpr int kTileLd = 36;  // LDS row stride in floats: 16-byte aligned, spreads banks
+
 template <bool TB>
-__global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float alpha, const float* __restrict__ A,
-                                                    int lda, const float* __restrict__ B, int ldb, float beta,
-                                                    float* __restrict__ C, int ldc, int lower_only) {
-    constexpr int LD = 36;  // row stride in floats: 16-byte aligned, spreads banks
-    __shared__ float As[64 * LD];
-    __shared__ float Bs[64 * LD];
+__device__ __forceinline__ void tile_acc(f4 (&acc)[2][2], const float* __restrict__ A, int lda,
+                                         const float* __restrict__ B, int ldb, int mlim, int nlim, int Kd,
+                                         float* __restrict__ As, float* __restrict__ Bs) {
+    constexpr int LD = kTileLd;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-    // lower_only: C's strictly upper 64 x 64 tiles are never read again
-    if (lower_only && j0 > i0 + 63) return;
-    f4 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -182,17 +178,17 @@ __global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float 
             const int e = tid + 256 * q;
             {
                 const int r = e >> 5, k = e & 31;  // A: consecutive k per row
-                const int gi = i0 + r, gk = k0 + k;
-                As[r * LD + k] = (gi < M && gk < Kd) ? A[(size_t)gi * lda + gk] : 0.f;
+                const int gk = k0 + k;
+                As[r * LD + k] = (r < mlim && gk < Kd) ? A[(size_t)r * lda + gk] : 0.f;
             }
             if (TB) {
                 const int n = e >> 5, k = e & 31;  // B[n][k]: consecutive k
-                const int gj = j0 + n, gk = k0 + k;
-                Bs[n * LD + k] = (gj < N && gk < Kd) ? B[(size_t)gj * ldb + gk] : 0.f;
+                const int gk = k0 + k;
+                Bs[n * LD + k] = (n < nlim && gk < Kd) ? B[(size_t)n * ldb + gk] : 0.f;
             } else {
                 const int k = e >> 6, n = e & 63;  // B[k][n]: consecutive n
-                const int gj = j0 + n, gk = k0 + k;
-                Bs[n * LD + k] = (gj < N && gk < Kd) ? B[(size_t)gk * ldb + gj] : 0.f;
+                const int gk = k0 + k;
+                Bs[n * LD + k] = (n < nlim && gk < Kd) ? B[(size_t)gk * ldb + n] : 0.f;
             }
         }
         __syncthreads();
@@ -214,136 +210,169 @@ __global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float 
         }
         __syncthreads();
     }
-    // lane holds rows 4 * lg + r of column li of each 16 x 16 block
+}
+
+// C = beta * C + alpha * acc on the tile at C (beta = 0: C is not read).
+// A lane holds rows 4 * (lane / 16) + r of column lane % 16 of each 16 x 16
+// block.
+__device__ __forceinline__ void tile_store(const f4 (&acc)[2][2], float* __restrict__ C, int ldc, int mlim, int nlim,
+                                           float alpha, float beta) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int gj = j0 + wn + 16 * j + li;
+            const int n = wn + 16 * j + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int gi = i0 + wm + 16 * i + 4 * lg + r;
-                if (gi < M && gj < N) {
-                    float* p = C + (size_t)gi * ldc + gj;
+                const int m = wm + 16 * i + 4 * lg + r;
+                if (m < mlim && n < nlim) {
+                    float* p = C + (size_t)m * ldc + n;
                     *p = (beta == 0.f ? 0.f : beta * *p) + alpha * acc[i][j][r];
                 }
             }
         }
 }
 
+// C = beta * C + alpha * A . opB (leading dimensions lda, ldb, ldc), a
+// 64 x 64 output tile per 256-thread block.
+template <bool TB>
+__global__ void __launch_bounds__(256) sgemm_kernel(int M, int N, int Kd, float alpha, const float* __restrict__ A,
+                                                    int lda, const float* __restrict__ B, int ldb, float beta,
+                                                    float* __restrict__ C, int ldc) {
+    __shared__ float As[64 * kTileLd];
+    __shared__ float Bs[64 * kTileLd];
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    f4 acc[2][2];
+    tile_acc<TB>(acc, A + (size_t)i0 * lda, lda, TB ? B + (size_t)j0 * ldb : B + j0, ldb, M - i0, N - j0, Kd, As, Bs);
+    tile_store(acc, C + (size_t)i0 * ldc + j0, ldc, M - i0, N - j0, alpha, beta);
+}
+
 template <bool TB>
 wq_status sgemm(int M, int N, int Kd, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
-                float* C, int ldc, hipStream_t s, bool lower_only = false) {
+                float* C, int ldc, hipStream_t s) {
     if (M <= 0 || N <= 0) return WQ_OK;
     if (Kd % 4 != 0) return WQ_ERR_ARG;
     hipLaunchKernelGGL((sgemm_kernel<TB>), dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, M, N, Kd, alpha, A,
-                       lda, B, ldb, beta, C, ldc, lower_only ? 1 : 0);
+                       lda, B, ldb, beta, C, ldc);
     return wqh::launch_status();
 }
 
-// Factor the nb x nb diagonal block at A[j0][j0] (lower part; nb <= 32):
-// L11 into L, its inverse into Li (both leading dimension K).  256 threads,
-// thread t owns column t % 32 of rows t / 32 + 8 q (q = 0..3).  Outer-product
-// elimination without the square roots, one barrier per step: after step j,
-// a[r][c] (r, c > j) is the Schur complement and a[r][j] = L[r][j] *
-// sqrt(p_j) with pivot p_j = a[j][j]; L[r][c] = a[r][c] / sqrt(p_c) at the
-// end.  A pivot that is not positive (rounding) is clamped to 1e-30.  The
-// inverse is forward elimination on the identity, also one barrier a step:
-// t[r][c] -= L[r][j] * t[j][c] / L[j][j], rows divided by L[r][r] at the end.
-__global__ void __launch_bounds__(256) chol_diag_kernel(const float* __restrict__ A, int K, int j0, int nb,
-                                                        float* __restrict__ L, float* __restrict__ Li) {
-    __shared__ float a[kCholB][kCholB + 1];
-    __shared__ float t[kCholB][kCholB + 1];
-    const int c = threadIdx.x & 31, rb = threadIdx.x >> 5;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = rb + 8 * q;
-        a[r][c] = (r < nb && c < nb && c <= r) ? A[(size_t)(j0 + r) * K + j0 + c] : 0.f;
-        t[r][c] = (r == c) ? 1.f : 0.f;
+// ------------------------------------------- Cholesky with its inverse ----
+//
+// Right-looking and blocked by 64 on the K x K matrix A (lower triangle
+// valid on entry), with L^-1 built alongside by forward substitution on
+// the identity.  Block row / column t covers [64 t, 64 t + 64).  Before
+// step j, A's tiles (r, c) with r >= j hold: for c >= j the Schur
+// complement of the leading j blocks (lower part), for c < j the partial
+// sums B[r][c] = -sum_{k<j} L[r][k] . Li[k][c] of the substitution.  Step j:
+//   block:  L_jj = chol(A_jj), Li[j][j] = L_jj^-1;
+//   panel:  Li[j][c] = Li_jj . B[j][c] (c < j), L[r][j] = A[r][j] . Li_jj^T
+//           (r > j);
+//   update: for r > j and c <= r, A[r][c] = (c == j ? 0 : A[r][c]) -
+//           L[r][j] . R[c], R[c] = Li[j][c] for c <= j and L[c][j]^T after.
+// After the last step Li's lower triangle (diagonal blocks included) is
+// L^-1; its upper triangle is never written.
+
+// The diagonal block: nb x nb (nb <= 64) at A[j0][j0], lower triangle read
+// and mirrored, padded with the identity; writes Li's diagonal block (zeros
+// above its diagonal included).  Two wavefronts, lane c holding column c:
+// wave 0 the Schur complement, wave 1 the identity under the same row
+// operations.  Step j: wave 0 publishes row j of the complement (one entry
+// per lane), pivot p = its entry j (clamped to 1e-30 against rounding);
+// both waves do v[r] -= row[r] * v[j] / p for r > j.  At the end the
+// identity side holds the inverse of the unit factor, and
+// Li[r][c] = v[r] / sqrt(p_r).  Square roots are taken only at the end.
+__global__ void __launch_bounds__(128) chol_block_kernel(const float* __restrict__ A, int K, int j0, int nb,
+                                                         float* __restrict__ Li) {
+    __shared__ float S[64 * 65];
+    __shared__ __align__(16) float rowj[2][64];
+    __shared__ float isd[64];
+    const int c = threadIdx.x & 63;
+    const bool inv_side = threadIdx.x >= 64;
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+        const int r = (threadIdx.x >> 6) + 2 * q;
+        S[r * 65 + c] = (r < nb && c < nb) ? A[(size_t)(j0 + r) * K + j0 + c] : (r == c ? 1.f : 0.f);
     }
     __syncthreads();
-    for (int j = 0; j + 1 < nb; ++j) {
-        const float inv_p = 1.f / fmaxf(a[j][j], 1e-30f);
-        float v[4];
+    float v[64];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = rb + 8 * q;
-            const bool upd = r > j && r < nb && c > j && c <= r;
-            v[q] = upd ? a[r][c] - a[r][j] * a[c][j] * inv_p : 0.f;
-        }
+    for (int r = 0; r < 64; ++r) v[r] = inv_side ? (r == c ? 1.f : 0.f) : (r >= c ? S[r * 65 + c] : S[c * 65 + r]);
+    float piv = 1.f;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        float* rj = rowj[j & 1];
+        if (!inv_side) rj[c] = v[j];
         __syncthreads();
+        const float p = fmaxf(rj[j], 1e-30f);
+        const float f = v[j] / p;
+        if (c == j) piv = p;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = rb + 8 * q;
-            if (r > j && r < nb && c > j && c <= r) a[r][c] = v[q];
-        }
-        __syncthreads();
+        for (int r = j + 1; r < 64; ++r) v[r] = fmaf(-rj[r], f, v[r]);
     }
-    // L in place
-    float lv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = rb + 8 * q;
-        const float root = sqrtf(fmaxf(a[c][c], 1e-30f));
-        lv[q] = (r < nb && c < nb && c <= r) ? (r == c ? root : a[r][c] / root) : 0.f;
-    }
+    if (!inv_side) isd[c] = 1.f / sqrtf(piv);
     __syncthreads();
+    if (inv_side && c < nb) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[rb + 8 * q][c] = lv[q];
-    __syncthreads();
-    for (int j = 0; j + 1 < nb; ++j) {
-        // row j of t is final (up to its division by L[j][j])
-        const float inv_d = 1.f / a[j][j];
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = rb + 8 * q;
-            const bool upd = r > j && r < nb && c <= j;
-            v[q] = upd ? t[r][c] - a[r][j] * t[j][c] * inv_d : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = rb + 8 * q;
-            if (r > j && r < nb && c <= j) t[r][c] = v[q];
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = rb + 8 * q;
-        if (r < nb && c < nb) {
-            L[(size_t)(j0 + r) * K + j0 + c] = a[r][c];
-            Li[(size_t)(j0 + r) * K + j0 + c] = (c <= r) ? t[r][c] / a[r][r] : 0.f;
-        }
+        for (int r = 0; r < 64; ++r)
+            if (r < nb) Li[(size_t)(j0 + r) * K + j0 + c] = v[r] * isd[r];
     }
 }
 
-// Recursive Cholesky with the inverse of the factor, on the block
-// [n0, n0 + n) of A (lower part read; the trailing block is overwritten by
-// its Schur complement):  with halves 1 and 2,
-//   L11 = chol(A11), L21 = A21 . L11^-T, L22 = chol(A22 - L21 . L21^T),
-//   inv(L) = [[Li11, 0], [-Li22 . L21 . Li11, Li22]].
-// Blocks of kCholB go to chol_diag_kernel; everything else is large fp32
-// products.  tmp: room for n * n / 4 floats.
-wq_status chol_inverse(float* A, float* L, float* Li, int K, int n0, int n, float* tmp, hipStream_t s) {
-    if (n <= kCholB) {
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, A, K, n0, n, L, Li);
-        return wqh::launch_status();
+// The panel of step j: block t < j writes Li[j][t], block t > j writes
+// L[t][j]; block j does nothing.
+__global__ void __launch_bounds__(256) chol_panel_kernel(const float* __restrict__ A, float* __restrict__ L,
+                                                         float* __restrict__ Li, int K, int j) {
+    __shared__ float As[64 * kTileLd];
+    __shared__ float Bs[64 * kTileLd];
+    const int t = blockIdx.x;
+    if (t == j) return;
+    const int j0 = 64 * j, t0 = 64 * t;
+    const int nbj = min(64, K - j0), nt = min(64, K - t0);
+    const float* Lijj = Li + (size_t)j0 * K + j0;
+    f4 acc[2][2];
+    if (t < j) {
+        tile_acc<false>(acc, Lijj, K, A + (size_t)j0 * K + t0, K, nbj, nt, nbj, As, Bs);
+        tile_store(acc, Li + (size_t)j0 * K + t0, K, nbj, nt, 1.f, 0.f);
+    } else {
+        tile_acc<true>(acc, A + (size_t)t0 * K + j0, K, Lijj, K, nt, nbj, nbj, As, Bs);
+        tile_store(acc, L + (size_t)t0 * K + j0, K, nt, nbj, 1.f, 0.f);
     }
-    const int h = ((n / kCholB + 1) / 2) * kCholB, n2 = n - h, r0 = n0 + h;
-    float* L21 = L + (size_t)r0 * K + n0;
-    const float* Li11 = Li + (size_t)n0 * K + n0;
-    wq_status st;
-    if ((st = chol_inverse(A, L, Li, K, n0, h, tmp, s)) != WQ_OK) return st;
-    if ((st = sgemm<true>(n2, h, h, 1.f, A + (size_t)r0 * K + n0, K, Li11, K, 0.f, L21, K, s)) != WQ_OK) return st;
-    // the trailing update: only its lower triangle is read afterwards
-    if ((st = sgemm<true>(n2, n2, h, -1.f, L21, K, L21, K, 1.f, A + (size_t)r0 * K + r0, K, s, true)) != WQ_OK)
-        return st;
-    if ((st = chol_inverse(A, L, Li, K, r0, n2, tmp, s)) != WQ_OK) return st;
-    // tmp = L21 . Li11 (n2 x h), then Li21 = -Li22 . tmp
-    if ((st = sgemm<false>(n2, h, h, 1.f, L21, K, Li11, K, 0.f, tmp, h, s)) != WQ_OK) return st;
-    return sgemm<false>(n2, h, n2, -1.f, Li + (size_t)r0 * K + r0, K, tmp, h, 0.f, Li + (size_t)r0 * K + n0, K, s);
+}
+
+// The update of step j: block (c, r - j - 1) for c <= r (blocks above the
+// block diagonal return at once).
+__global__ void __launch_bounds__(256) chol_update_kernel(float* __restrict__ A, const float* __restrict__ L,
+                                                          const float* __restrict__ Li, int K, int j) {
+    __shared__ float As[64 * kTileLd];
+    __shared__ float Bs[64 * kTileLd];
+    const int c = blockIdx.x, r = j + 1 + blockIdx.y;
+    if (c > r) return;
+    const int j0 = 64 * j, r0 = 64 * r, c0 = 64 * c;
+    const int nbj = min(64, K - j0), nr = min(64, K - r0), nc = min(64, K - c0);
+    const float* P = L + (size_t)r0 * K + j0;
+    f4 acc[2][2];
+    if (c <= j)
+        tile_acc<false>(acc, P, K, Li + (size_t)j0 * K + c0, K, nr, nc, nbj, As, Bs);
+    else
+        tile_acc<true>(acc, P, K, L + (size_t)c0 * K + j0, K, nr, nc, nbj, As, Bs);
+    tile_store(acc, A + (size_t)r0 * K + c0, K, nr, nc, -1.f, c == j ? 0.f : 1.f);
+}
+
+// Li = L^-1 with L L^T = A (K x K; A is overwritten, L holds the panels).
+wq_status chol_inverse(float* A, float* L, float* Li, int K, hipStream_t s) {
+    const int T = (K + 63) / 64;
+    for (int j = 0; j < T; ++j) {
+        hipLaunchKernelGGL(chol_block_kernel, dim3(1), dim3(128), 0, s, A, K, 64 * j, min(64, K - 64 * j), Li);
+        if (T > 1) hipLaunchKernelGGL(chol_panel_kernel, dim3(T), dim3(256), 0, s, A, L, Li, K, j);
+        if (j + 1 < T) hipLaunchKernelGGL(chol_update_kernel, dim3(T, T - j - 1), dim3(256), 0, s, A, L, Li, K, j);
+        const wq_status st = wqh::launch_status();
+        if (st != WQ_OK) return st;
+    }
+    return WQ_OK;
 }
 
 // Columns [32 H, 32 H + 32) of a block (see gptq_block_kernel); a group can
@@ -578,12 +607,9 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     // L L^T = P H' P and Li = L^-1 (recursive halving), U = P Li P, with H'
     // the Hessian in processing order
     hipLaunchKernelGGL(permute_reverse_kernel, grid_for(KK), dim3(256), 0, s, H, perm, K, A);
-    hipLaunchKernelGGL(fill_kernel, grid_for(KK), dim3(256), 0, s, L, KK, 0.f);
-    hipLaunchKernelGGL(fill_kernel, grid_for(KK), dim3(256), 0, s, Li, KK, 0.f);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
-    // H is free once reversed into A: scratch for the inverse's products
-    if ((st = chol_inverse(A, L, Li, K, 0, K, H, s)) != WQ_OK) return st;
-    hipLaunchKernelGGL(reverse_kernel, grid_for(KK), dim3(256), 0, s, Li, K, U);
+    if ((st = chol_inverse(A, L, Li, K, s)) != WQ_OK) return st;
+    hipLaunchKernelGGL(upper_reverse_kernel, grid_for(KK), dim3(256), 0, s, Li, K, U);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
 
     // the column walk with lazy block updates
