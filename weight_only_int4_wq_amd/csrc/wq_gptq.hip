@@ -379,7 +379,7 @@ wq_status chol_inverse(float* A, float* L, float* Li, int K, hipStream_t s) {
 // start only at the first of them.
 template <int BITS, bool SYM, int BC, int H>
 __device__ __forceinline__ void gptq_half(float (&w)[BC], float (&e)[BC], uint32_t (&cw)[BC / 4], float& s, float& z,
-                                          const float* __restrict__ urow, const float* __restrict__ wrow, int K,
+                                          const float* __restrict__ us, const float* __restrict__ wrow, int K,
                                           int b0, int gs, int G, int n, bool live, uint16_t* __restrict__ scales,
                                           uint8_t* __restrict__ zeros) {
     constexpr float qmax = float((1 << BITS) - 1);
@@ -419,21 +419,30 @@ __device__ __forceinline__ void gptq_half(float (&w)[BC], float (&e)[BC], uint32
         const float q = fminf(fmaxf(rintf(__fdiv_rn(w[i], s)) + z, 0.f), qmax);
         cw[i / 4] |= uint32_t(q) << (8 * (i % 4));
         const float wq = h2f(f2h((q - z) * s));
-        const float err = (w[i] - wq) / urow[(size_t)i * K + i];
+        const float err = (w[i] - wq) / us[i * BC + i];
         e[i] = err;
 #pragma unroll
-        for (int j = i + 1; j < BC; ++j) w[j] = fmaf(-err, urow[(size_t)i * K + j], w[j]);
+        for (int j = i + 1; j < BC; ++j) w[j] = fmaf(-err, us[i * BC + j], w[j]);
     }
 }
 
 // One block of GPTQ columns [b0, b0 + BC) for 64 weight rows, one row per
-// lane held in registers.  U's entries are the same for every lane (uniform
-// loads); the block's codes and errors leave as 16-byte stores at the end.
+// lane held in registers.  U's entries are the same for every lane: the
+// block's BC x BC part of U is staged in LDS once and read as broadcasts
+// (LDS reads return in order, so their waits pipeline).  The block's codes
+// and errors leave as 16-byte stores at the end.
 template <int BITS, bool SYM, int BC>
 __global__ void __launch_bounds__(64) gptq_block_kernel(float* __restrict__ W32, const float* __restrict__ U, int N,
                                                         int K, int b0, int gs, uint8_t* __restrict__ codes,
                                                         uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros,
                                                         float* __restrict__ Err, int ldE) {
+    __shared__ __align__(16) float us[BC * BC];
+    for (int v = threadIdx.x; v < BC * BC / 4; v += 64) {
+        const int r = v / (BC / 4), c4 = v % (BC / 4);
+        *reinterpret_cast<f4*>(&us[r * BC + 4 * c4]) =
+            *reinterpret_cast<const f4*>(U + (size_t)(b0 + r) * K + b0 + 4 * c4);
+    }
+    __syncthreads();
     const int n = blockIdx.x * 64 + threadIdx.x;
     const bool live = n < N;
     const int nr = live ? n : N - 1;  // rows past N compute on a copy and store nothing
@@ -458,10 +467,9 @@ __global__ void __launch_bounds__(64) gptq_block_kernel(float* __restrict__ W32,
     uint32_t cw[BC / 4];
 #pragma unroll
     for (int v = 0; v < BC / 4; ++v) cw[v] = 0;
-    const float* urow = U + (size_t)b0 * K + b0;
     // groups are multiples of 32 columns: a group can only start at i = 0 or 32
-    gptq_half<BITS, SYM, BC, 0>(w, e, cw, s, z, urow, wrow, K, b0, gs, G, n, live, scales, zeros);
-    if constexpr (BC == 64) gptq_half<BITS, SYM, BC, 1>(w, e, cw, s, z, urow, wrow, K, b0, gs, G, n, live, scales, zeros);
+    gptq_half<BITS, SYM, BC, 0>(w, e, cw, s, z, us, wrow, K, b0, gs, G, n, live, scales, zeros);
+    if constexpr (BC == 64) gptq_half<BITS, SYM, BC, 1>(w, e, cw, s, z, us, wrow, K, b0, gs, G, n, live, scales, zeros);
     if (live) {
         uint8_t* crow = codes + (size_t)n * K + b0;
 #pragma unroll
