@@ -260,6 +260,111 @@ wq_status sgemm(int M, int N, int Kd, float alpha, const float* A, int lda, cons
     return wqh::launch_status();
 }
 
+// C = beta * C + alpha * A . B (B as B[k][n]) for the column walk's large
+// products: 128 x 128 output tiles per 256-thread block, each wavefront a
+// 64 x 64 quarter of 2 x 2 v_mfma_f32_32x32x2f32 blocks.  k in stages of
+// 32 through LDS (A as As[m][k], B as Bs[k][n], both written with 16-byte
+// stores); the next stage's 16-byte global loads are issued into registers
+// before the current stage's products.  A lane reads four consecutive k of
+// its A row with one 16-byte load; instruction t of such a load takes
+// k = 4 * (lane / 32) + t in A and B alike (a permutation of the sum's
+// terms).  Needs N, lda, ldb and Kd multiples of 4 and A, B 16-byte
+// aligned.
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(256) sgemm128_kernel(int M, int N, int Kd, float alpha, const float* __restrict__ A,
+                                                       int lda, const float* __restrict__ B, int ldb, float beta,
+                                                       float* __restrict__ C, int ldc) {
+    constexpr int LDA = 36, LDB = 132;
+    __shared__ __align__(16) float As[128 * LDA];
+    __shared__ __align__(16) float Bs[32 * LDB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int i0 = blockIdx.y * 128, j0 = blockIdx.x * 128;
+    f16v acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    f4 ra[4], rb[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            const int r = e >> 3, ka = k0 + 4 * (e & 7);
+            ra[q] = (i0 + r < M && ka < Kd) ? *reinterpret_cast<const f4*>(A + (size_t)(i0 + r) * lda + ka)
+                                            : f4{0.f, 0.f, 0.f, 0.f};
+            const int kb = k0 + (e >> 5), n = j0 + 4 * (e & 31);
+            rb[q] = (kb < Kd && n < N) ? *reinterpret_cast<const f4*>(B + (size_t)kb * ldb + n)
+                                       : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    gload(0);
+    for (int k0 = 0; k0 < Kd; k0 += 32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = tid + 256 * q;
+            *reinterpret_cast<f4*>(&As[(e >> 3) * LDA + 4 * (e & 7)]) = ra[q];
+            *reinterpret_cast<f4*>(&Bs[(e >> 5) * LDB + 4 * (e & 31)]) = rb[q];
+        }
+        __syncthreads();
+        if (k0 + 32 < Kd) gload(k0 + 32);
+#pragma unroll
+        for (int kk = 0; kk < 32; kk += 8) {
+            f4 a[2];
+            float b[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const f4*>(&As[(wm + 32 * i + l32) * LDA + kk + 4 * h]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) b[j][t] = Bs[(kk + 4 * h + t) * LDB + wn + 32 * j + l32];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][t], b[j][t], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    // lane holds rows 8 * (r / 4) + 4 * (lane / 32) + r % 4 of column
+    // lane % 32 of each 32 x 32 block
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int gj = j0 + wn + 32 * j + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int gi = i0 + wm + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+                if (gi < M && gj < N) {
+                    float* p = C + (size_t)gi * ldc + gj;
+                    *p = (beta == 0.f ? 0.f : beta * *p) + alpha * acc[i][j][r];
+                }
+            }
+        }
+}
+
+// NN product: the 128-tile kernel when its alignment holds and it makes at
+// least 256 tiles, else the 64-tile one.
+wq_status sgemm_nn(int M, int N, int Kd, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
+                   float* C, int ldc, hipStream_t s) {
+    if (M <= 0 || N <= 0) return WQ_OK;
+    if (Kd % 4 != 0) return WQ_ERR_ARG;
+    const long long tiles = (long long)((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles >= 256 && N % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && wqh::aligned16(A) && wqh::aligned16(B)) {
+        hipLaunchKernelGGL(sgemm128_kernel, dim3((N + 127) / 128, (M + 127) / 128), dim3(256), 0, s, M, N, Kd, alpha,
+                           A, lda, B, ldb, beta, C, ldc);
+        return wqh::launch_status();
+    }
+    return sgemm<false>(M, N, Kd, alpha, A, lda, B, ldb, beta, C, ldc, s);
+}
+
 // ------------------------------------------- Cholesky with its inverse ----
 //
 // Right-looking and blocked by 64 on the K x K matrix A (lower triangle
@@ -552,13 +657,13 @@ wq_status gptq_blocks(float* W32, const float* U, int N, int K, int gs, uint8_t*
             if ((st = wqh::launch_status()) != WQ_OK) return st;
             const int rest_in = oe - b0 - bc;
             if (rest_in > 0 &&
-                (st = sgemm<false>(N, rest_in, bc, -1.f, eb, outer, U + (size_t)b0 * K + b0 + bc, K, 1.f,
-                                   W32 + b0 + bc, K, s)) != WQ_OK)
+                (st = sgemm_nn(N, rest_in, bc, -1.f, eb, outer, U + (size_t)b0 * K + b0 + bc, K, 1.f,
+                               W32 + b0 + bc, K, s)) != WQ_OK)
                 return st;
         }
         const int rest = K - oe;
-        if (rest > 0 && (st = sgemm<false>(N, rest, oe - ob0, -1.f, Err, outer, U + (size_t)ob0 * K + oe, K, 1.f,
-                                           W32 + oe, K, s)) != WQ_OK)
+        if (rest > 0 && (st = sgemm_nn(N, rest, oe - ob0, -1.f, Err, outer, U + (size_t)ob0 * K + oe, K, 1.f,
+                                       W32 + oe, K, s)) != WQ_OK)
             return st;
     }
     return WQ_OK;
