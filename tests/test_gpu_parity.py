@@ -480,6 +480,27 @@ def test_gptq_llama_layer_sampled_rows():
     assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)
 
 
+def test_gptq_ragged_large_products():
+    # 4100 weight rows and K = 1312 (5 x 256 + 32): the walk's lazy-update
+    # products are large enough for the 128-tile product kernel and end in
+    # a partial row tile and a partial column tile.  Sampled rows include
+    # the partial tile's.
+    M, N, K = 256, 4100, 1312
+    seed = (123,)
+    x = I.correlated_activations(seed, M, K)
+    w = I.weights(seed, N, K, 0.02)
+    codes, scales, zeros, _ = wq.gptq_quantize(dev(w), dev(x), 4, 32)
+    rows = np.array([0, 127, 4095, 4096, 4099])
+    ref = O.gptq_quantize(w[rows], x, 4, 32)
+    c = host(codes)[rows]
+    agree = np.mean(c == ref["codes"])
+    w_hat = _gptq_w_hat(c, host(scales)[rows], host(zeros)[rows], 4, 32)
+    e_gpu, e_ref = _gptq_out_err(w[rows], x, w_hat), _gptq_out_err(w[rows], x, ref["w_hat"])
+    print(f"codes {agree:.5f} err gpu/ref {e_gpu / e_ref:.5f}")
+    assert agree >= 0.997, agree
+    assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)
+
+
 # ---------------------------------------------------- AWQ clip search ----
 #
 # The GPU sums fp16 matrix-core products of x and fp16(w - w_hat); the
