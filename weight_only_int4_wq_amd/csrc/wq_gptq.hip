@@ -383,47 +383,60 @@ wq_status sgemm_nn(int M, int N, int Kd, float alpha, const float* A, int lda, c
 
 // The diagonal block: nb x nb (nb <= 64) at A[j0][j0], lower triangle read
 // and mirrored, padded with the identity; writes Li's diagonal block (zeros
-// above its diagonal included).  Two wavefronts, lane c holding column c:
-// wave 0 the Schur complement, wave 1 the identity under the same row
-// operations.  Step j: wave 0 publishes row j of the complement (one entry
-// per lane), pivot p = its entry j (clamped to 1e-30 against rounding);
-// both waves do v[r] -= row[r] * v[j] / p for r > j.  At the end the
-// identity side holds the inverse of the unit factor, and
-// Li[r][c] = v[r] / sqrt(p_r).  Square roots are taken only at the end.
-__global__ void __launch_bounds__(128) chol_block_kernel(const float* __restrict__ A, int K, int j0, int nb,
+// above its diagonal included).  Four wavefronts; lane c of wave w holds
+// rows [16 w, 16 w + 16) of column c of the Schur complement (a) and of the
+// identity under the same row operations (t).  Step j: the wave holding
+// row j publishes it (a's entries past j, zeros before; t's in full) and
+// the pivot p = a[j][j] (clamped to 1e-30 against rounding); every wave
+// does a[r] -= a[j][r] * a[j][c] / p and t[r] -= a[j][r] * t[j][c] / p for
+// its rows r > j.  At the end t is the inverse of the unit factor and
+// Li[r][c] = t[r][c] / sqrt(p_r).  Square roots are taken only at the end.
+// The steps run as a loop over four unrolled runs of 16.
+__global__ void __launch_bounds__(256) chol_block_kernel(const float* __restrict__ A, int K, int j0, int nb,
                                                          float* __restrict__ Li) {
     __shared__ float S[64 * 65];
-    __shared__ __align__(16) float rowj[2][64];
-    __shared__ float isd[64];
-    const int c = threadIdx.x & 63;
-    const bool inv_side = threadIdx.x >= 64;
+    __shared__ __align__(16) float rowA[2][64];
+    __shared__ __align__(16) float rowT[2][64];
+    __shared__ float pd[64];
+    const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll 4
-    for (int q = 0; q < 32; ++q) {
-        const int r = (threadIdx.x >> 6) + 2 * q;
+    for (int q = 0; q < 16; ++q) {
+        const int r = w + 4 * q;
         S[r * 65 + c] = (r < nb && c < nb) ? A[(size_t)(j0 + r) * K + j0 + c] : (r == c ? 1.f : 0.f);
     }
     __syncthreads();
-    float v[64];
+    float a[16], t[16];
 #pragma unroll
-    for (int r = 0; r < 64; ++r) v[r] = inv_side ? (r == c ? 1.f : 0.f) : (r >= c ? S[r * 65 + c] : S[c * 65 + r]);
-    float piv = 1.f;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        float* rj = rowj[j & 1];
-        if (!inv_side) rj[c] = v[j];
-        __syncthreads();
-        const float p = fmaxf(rj[j], 1e-30f);
-        const float f = v[j] / p;
-        if (c == j) piv = p;
-#pragma unroll
-        for (int r = j + 1; r < 64; ++r) v[r] = fmaf(-rj[r], f, v[r]);
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * w + i;
+        a[i] = r >= c ? S[r * 65 + c] : S[c * 65 + r];
+        t[i] = r == c ? 1.f : 0.f;
     }
-    if (!inv_side) isd[c] = 1.f / sqrtf(piv);
-    __syncthreads();
-    if (inv_side && c < nb) {
+    for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
-        for (int r = 0; r < 64; ++r)
-            if (r < nb) Li[(size_t)(j0 + r) * K + j0 + c] = v[r] * isd[r];
+        for (int jj = 0; jj < 16; ++jj) {
+            const int j = 16 * jb + jj, buf = jj & 1;
+            if (w == jb) {
+                rowA[buf][c] = c > j ? a[jj] : 0.f;
+                rowT[buf][c] = t[jj];
+                if (c == j) pd[j] = fmaxf(a[jj], 1e-30f);
+            }
+            __syncthreads();
+            const float p = pd[j];
+            const float fa = rowA[buf][c] / p, ft = rowT[buf][c] / p;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float m = rowA[buf][16 * w + i];
+                a[i] = fmaf(-m, fa, a[i]);
+                t[i] = fmaf(-m, ft, t[i]);
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * w + i;
+        if (r < nb && c < nb) Li[(size_t)(j0 + r) * K + j0 + c] = t[i] * (1.f / sqrtf(pd[r]));
     }
 }
 
@@ -471,7 +484,7 @@ __global__ void __launch_bounds__(256) chol_update_kernel(float* __restrict__ A,
 wq_status chol_inverse(float* A, float* L, float* Li, int K, hipStream_t s) {
     const int T = (K + 63) / 64;
     for (int j = 0; j < T; ++j) {
-        hipLaunchKernelGGL(chol_block_kernel, dim3(1), dim3(128), 0, s, A, K, 64 * j, min(64, K - 64 * j), Li);
+        hipLaunchKernelGGL(chol_block_kernel, dim3(1), dim3(256), 0, s, A, K, 64 * j, min(64, K - 64 * j), Li);
         if (T > 1) hipLaunchKernelGGL(chol_panel_kernel, dim3(T), dim3(256), 0, s, A, L, Li, K, j);
         if (j + 1 < T) hipLaunchKernelGGL(chol_update_kernel, dim3(T, T - j - 1), dim3(256), 0, s, A, L, Li, K, j);
         const wq_status st = wqh::launch_status();
