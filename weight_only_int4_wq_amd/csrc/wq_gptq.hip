@@ -379,25 +379,32 @@ wq_status sgemm_nn(int M, int N, int Kd, float alpha, const float* A, int lda, c
 //   update: for r > j and c <= r, A[r][c] = (c == j ? 0 : A[r][c]) -
 //           L[r][j] . R[c], R[c] = Li[j][c] for c <= j and L[c][j]^T after.
 // After the last step Li's lower triangle (diagonal blocks included) is
-// L^-1; its upper triangle is never written.
+// L^-1; its upper triangle is never written.  The block step of j + 1 runs
+// inside the update launch of step j, in the block of tile (j + 1, j + 1).
 
 // The diagonal block: nb x nb (nb <= 64) at A[j0][j0], lower triangle read
 // and mirrored, padded with the identity; writes Li's diagonal block (zeros
 // above its diagonal included).  Four wavefronts; lane c of wave w holds
 // rows [16 w, 16 w + 16) of column c of the Schur complement (a) and of the
-// identity under the same row operations (t).  Step j: the wave holding
-// row j publishes it (a's entries past j, zeros before; t's in full) and
-// the pivot p = a[j][j] (clamped to 1e-30 against rounding); every wave
-// does a[r] -= a[j][r] * a[j][c] / p and t[r] -= a[j][r] * t[j][c] / p for
-// its rows r > j.  At the end t is the inverse of the unit factor and
-// Li[r][c] = t[r][c] / sqrt(p_r).  Square roots are taken only at the end.
-// The steps run as a loop over four unrolled runs of 16.
-__global__ void __launch_bounds__(256) chol_block_kernel(const float* __restrict__ A, int K, int j0, int nb,
-                                                         float* __restrict__ Li) {
-    __shared__ float S[64 * 65];
-    __shared__ __align__(16) float rowA[2][64];
-    __shared__ __align__(16) float rowT[2][64];
-    __shared__ float pd[64];
+// identity under the same row operations (t).  Step j publishes row j (a's
+// entries past j, zeros before; t's in full) and the pivot p = a[j][j]
+// (clamped to 1e-30 against rounding), and every row r > j takes
+// a[r] -= a[j][r] * a[j][c] / p and t[r] -= a[j][r] * t[j][c] / p.  The
+// steps go in runs of 16, the pivot rows of one wavefront: that wavefront
+// walks the run alone, updating its own rows at each step, and then the
+// wavefronts holding later rows apply the run's 16 updates in step order
+// (the same operations in the same order per element).  At the end t is
+// the inverse of the unit factor and Li[r][c] = t[r][c] / sqrt(p_r); square
+// roots are taken only at the end.
+// smem: 64 * 65 + 2 * 16 * 64 + 64 floats, 16-byte aligned.  256 threads.
+constexpr int kFactorSmem = 64 * 65 + 2 * 16 * 64 + 64;
+
+__device__ __forceinline__ void chol_factor(const float* __restrict__ A, int K, int j0, int nb, float* __restrict__ Li,
+                                            float* __restrict__ smem) {
+    float* S = smem;
+    float(*hA)[64] = reinterpret_cast<float(*)[64]>(smem + 64 * 65);
+    float(*hT)[64] = reinterpret_cast<float(*)[64]>(smem + 64 * 65 + 16 * 64);
+    float* pd = smem + 64 * 65 + 2 * 16 * 64;
     const int c = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll 4
     for (int q = 0; q < 16; ++q) {
@@ -413,31 +420,56 @@ __global__ void __launch_bounds__(256) chol_block_kernel(const float* __restrict
         t[i] = r == c ? 1.f : 0.f;
     }
     for (int jb = 0; jb < 4; ++jb) {
+        if (w == jb) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int j = 16 * jb + jj, buf = jj & 1;
-            if (w == jb) {
-                rowA[buf][c] = c > j ? a[jj] : 0.f;
-                rowT[buf][c] = t[jj];
+            for (int jj = 0; jj < 16; ++jj) {
+                const int j = 16 * jb + jj;
+                hA[jj][c] = c > j ? a[jj] : 0.f;
+                hT[jj][c] = t[jj];
                 if (c == j) pd[j] = fmaxf(a[jj], 1e-30f);
-            }
-            __syncthreads();
-            const float p = pd[j];
-            const float fa = rowA[buf][c] / p, ft = rowT[buf][c] / p;
+                // LDS writes and reads of one wavefront stay in order
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const float p = pd[j];
+                const float fa = hA[jj][c] / p, ft = hT[jj][c] / p;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float m = rowA[buf][16 * w + i];
-                a[i] = fmaf(-m, fa, a[i]);
-                t[i] = fmaf(-m, ft, t[i]);
+                for (int i = jj + 1; i < 16; ++i) {
+                    const float m = hA[jj][16 * jb + i];
+                    a[i] = fmaf(-m, fa, a[i]);
+                    t[i] = fmaf(-m, ft, t[i]);
+                }
             }
         }
+        __syncthreads();
+        if (w > jb) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const float p = pd[16 * jb + jj];
+                const float fa = hA[jj][c] / p, ft = hT[jj][c] / p;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float m = hA[jj][16 * w + i];
+                    a[i] = fmaf(-m, fa, a[i]);
+                    t[i] = fmaf(-m, ft, t[i]);
+                }
+            }
+        }
+        __syncthreads();  // the run's rows are rewritten by the next run
     }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = 16 * w + i;
         if (r < nb && c < nb) Li[(size_t)(j0 + r) * K + j0 + c] = t[i] * (1.f / sqrtf(pd[r]));
     }
+}
+
+// The first diagonal block on its own; every later one is factored by the
+// previous step's update (chol_update_kernel).
+__global__ void __launch_bounds__(256) chol_block_kernel(const float* __restrict__ A, int K, int j0, int nb,
+                                                         float* __restrict__ Li) {
+    __shared__ __align__(16) float smem[kFactorSmem];
+    chol_factor(A, K, j0, nb, Li, smem);
 }
 
 // The panel of step j: block t < j writes Li[j][t], block t > j writes
@@ -462,11 +494,15 @@ __global__ void __launch_bounds__(256) chol_panel_kernel(const float* __restrict
 }
 
 // The update of step j: block (c, r - j - 1) for c <= r (blocks above the
-// block diagonal return at once).
-__global__ void __launch_bounds__(256) chol_update_kernel(float* __restrict__ A, const float* __restrict__ L,
-                                                          const float* __restrict__ Li, int K, int j) {
-    __shared__ float As[64 * kTileLd];
-    __shared__ float Bs[64 * kTileLd];
+// block diagonal return at once).  The block of tile (j + 1, j + 1), the
+// next step's diagonal block, goes on to factor it (its writes are visible
+// to the block after a barrier) while the other tiles are updated.
+__global__ void __launch_bounds__(256, 4) chol_update_kernel(float* __restrict__ A, const float* __restrict__ L,
+                                                             float* __restrict__ Li, int K, int j) {
+    constexpr int kTiles = 2 * 64 * kTileLd;
+    __shared__ __align__(16) float smem[kTiles > kFactorSmem ? kTiles : kFactorSmem];
+    float* As = smem;
+    float* Bs = smem + 64 * kTileLd;
     const int c = blockIdx.x, r = j + 1 + blockIdx.y;
     if (c > r) return;
     const int j0 = 64 * j, r0 = 64 * r, c0 = 64 * c;
@@ -478,13 +514,17 @@ __global__ void __launch_bounds__(256) chol_update_kernel(float* __restrict__ A,
     else
         tile_acc<true>(acc, P, K, L + (size_t)c0 * K + j0, K, nr, nc, nbj, As, Bs);
     tile_store(acc, A + (size_t)r0 * K + c0, K, nr, nc, -1.f, c == j ? 0.f : 1.f);
+    if (r == j + 1 && c == j + 1) {
+        __syncthreads();
+        chol_factor(A, K, r0, nr, Li, smem);
+    }
 }
 
 // Li = L^-1 with L L^T = A (K x K; A is overwritten, L holds the panels).
 wq_status chol_inverse(float* A, float* L, float* Li, int K, hipStream_t s) {
     const int T = (K + 63) / 64;
+    hipLaunchKernelGGL(chol_block_kernel, dim3(1), dim3(256), 0, s, A, K, 0, min(64, K), Li);
     for (int j = 0; j < T; ++j) {
-        hipLaunchKernelGGL(chol_block_kernel, dim3(1), dim3(256), 0, s, A, K, 64 * j, min(64, K - 64 * j), Li);
         if (T > 1) hipLaunchKernelGGL(chol_panel_kernel, dim3(T), dim3(256), 0, s, A, L, Li, K, j);
         if (j + 1 < T) hipLaunchKernelGGL(chol_update_kernel, dim3(T, T - j - 1), dim3(256), 0, s, A, L, Li, K, j);
         const wq_status st = wqh::launch_status();
