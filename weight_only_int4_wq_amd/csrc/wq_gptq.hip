@@ -236,6 +236,106 @@ __device__ __forceinline__ void tile_store(const f4 (&acc)[2][2], float* __restr
         }
 }
 
+// C = beta * C + alpha * A . opB for one 64 x 64 tile of depth Kd <= 64
+// (a multiple of 4) in one shot: the tile's A, opB and C are requested with
+// 16-byte loads before anything waits (lda, ldb, ldc, nlim multiples of 4,
+// pointers 16-byte aligned), both operands go to LDS whole (A as As[m][k],
+// opB as Bs[n][k]), v_mfma_f32_16x16x4f32 as in tile_acc, and the result
+// returns through LDS so that C is written with 16-byte stores too.  256
+// threads; smem: 2 * 64 * 68 floats.  Thread t moves the four 16-byte
+// pieces (row t / 16 + 16 q, columns 4 (t % 16) ..).
+constexpr int kShotLd = 68;
+constexpr int kShotSmem = 2 * 64 * kShotLd;
+
+template <bool TB>
+__device__ __forceinline__ void tile_shot(const float* __restrict__ A, int lda, const float* __restrict__ B, int ldb,
+                                          float* __restrict__ C, int ldc, int mlim, int nlim, int Kd, float alpha,
+                                          float beta, float* __restrict__ smem) {
+    constexpr int LD = kShotLd;
+    float* As = smem;
+    float* Bs = smem + 64 * LD;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int pr = tid >> 4, p4 = 4 * (tid & 15);
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    f4 ra[4], rb[4], rc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = pr + 16 * q;
+        ra[q] = (r < mlim && p4 < Kd) ? *reinterpret_cast<const f4*>(A + (size_t)r * lda + p4) : zero;
+        if (TB)  // B[n][k]: row n = r, k = p4
+            rb[q] = (r < nlim && p4 < Kd) ? *reinterpret_cast<const f4*>(B + (size_t)r * ldb + p4) : zero;
+        else     // B[k][n]: row k = r, n = p4
+            rb[q] = (r < Kd && p4 < nlim) ? *reinterpret_cast<const f4*>(B + (size_t)r * ldb + p4) : zero;
+        rc[q] = (beta != 0.f && r < mlim && p4 < nlim) ? *reinterpret_cast<const f4*>(C + (size_t)r * ldc + p4)
+                                                       : zero;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = pr + 16 * q;
+        *reinterpret_cast<f4*>(&As[r * LD + p4]) = ra[q];
+        if (TB) {
+            *reinterpret_cast<f4*>(&Bs[r * LD + p4]) = rb[q];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Bs[(p4 + t) * LD + r] = rb[q][t];
+        }
+    }
+    __syncthreads();
+    const int li = lane & 15, lg = lane >> 4;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    f4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero;
+    for (int kk = 0; kk < Kd; kk += 16) {
+        f4 a[2], b[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            a[t] = *reinterpret_cast<const f4*>(&As[(wm + 16 * t + li) * LD + kk + 4 * lg]);
+            b[t] = *reinterpret_cast<const f4*>(&Bs[(wn + 16 * t + li) * LD + kk + 4 * lg]);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][t], b[j][t], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+    // lane holds rows 4 * lg + r of column li of each 16 x 16 block
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) As[(wm + 16 * i + 4 * lg + r) * LD + wn + 16 * j + li] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = pr + 16 * q;
+        if (r < mlim && p4 < nlim) {
+            const f4 v = *reinterpret_cast<const f4*>(&As[r * LD + p4]);
+            f4 o;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o[t] = (beta == 0.f ? 0.f : beta * rc[q][t]) + alpha * v[t];
+            *reinterpret_cast<f4*>(C + (size_t)r * ldc + p4) = o;
+        }
+    }
+}
+
+// C = beta * C + alpha * A . B (NN), depth Kd <= 64, one shot per 64 x 64
+// tile (the column walk's updates inside an outer block).
+__global__ void __launch_bounds__(256) sgemm_shot_kernel(int M, int N, int Kd, float alpha, const float* __restrict__ A,
+                                                         int lda, const float* __restrict__ B, int ldb, float beta,
+                                                         float* __restrict__ C, int ldc) {
+    __shared__ __align__(16) float smem[kShotSmem];
+    const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    tile_shot<false>(A + (size_t)i0 * lda, lda, B + j0, ldb, C + (size_t)i0 * ldc + j0, ldc, M - i0, N - j0, Kd, alpha,
+                     beta, smem);
+}
+
 // C = beta * C + alpha * A . opB (leading dimensions lda, ldb, ldc), a
 // 64 x 64 output tile per 256-thread block.
 template <bool TB>
@@ -365,6 +465,21 @@ wq_status sgemm_nn(int M, int N, int Kd, float alpha, const float* A, int lda, c
     return sgemm<false>(M, N, Kd, alpha, A, lda, B, ldb, beta, C, ldc, s);
 }
 
+// NN product of depth <= 64 in one shot per tile when the 16-byte rules
+// hold, else the staged 64-tile kernel.
+wq_status sgemm_shot(int M, int N, int Kd, float alpha, const float* A, int lda, const float* B, int ldb, float beta,
+                     float* C, int ldc, hipStream_t s) {
+    if (M <= 0 || N <= 0) return WQ_OK;
+    if (Kd % 4 != 0) return WQ_ERR_ARG;
+    if (Kd <= 64 && N % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 && wqh::aligned16(A) &&
+        wqh::aligned16(B) && wqh::aligned16(C)) {
+        hipLaunchKernelGGL(sgemm_shot_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, M, N, Kd, alpha, A,
+                           lda, B, ldb, beta, C, ldc);
+        return wqh::launch_status();
+    }
+    return sgemm<false>(M, N, Kd, alpha, A, lda, B, ldb, beta, C, ldc, s);
+}
+
 // ------------------------------------------- Cholesky with its inverse ----
 //
 // Right-looking and blocked by 64 on the K x K matrix A (lower triangle
@@ -476,21 +591,16 @@ __global__ void __launch_bounds__(256) chol_block_kernel(const float* __restrict
 // L[t][j]; block j does nothing.
 __global__ void __launch_bounds__(256) chol_panel_kernel(const float* __restrict__ A, float* __restrict__ L,
                                                          float* __restrict__ Li, int K, int j) {
-    __shared__ float As[64 * kTileLd];
-    __shared__ float Bs[64 * kTileLd];
+    __shared__ __align__(16) float smem[kShotSmem];
     const int t = blockIdx.x;
     if (t == j) return;
     const int j0 = 64 * j, t0 = 64 * t;
     const int nbj = min(64, K - j0), nt = min(64, K - t0);
     const float* Lijj = Li + (size_t)j0 * K + j0;
-    f4 acc[2][2];
-    if (t < j) {
-        tile_acc<false>(acc, Lijj, K, A + (size_t)j0 * K + t0, K, nbj, nt, nbj, As, Bs);
-        tile_store(acc, Li + (size_t)j0 * K + t0, K, nbj, nt, 1.f, 0.f);
-    } else {
-        tile_acc<true>(acc, A + (size_t)t0 * K + j0, K, Lijj, K, nt, nbj, nbj, As, Bs);
-        tile_store(acc, L + (size_t)t0 * K + j0, K, nt, nbj, 1.f, 0.f);
-    }
+    if (t < j)
+        tile_shot<false>(Lijj, K, A + (size_t)j0 * K + t0, K, Li + (size_t)j0 * K + t0, K, nbj, nt, nbj, 1.f, 0.f, smem);
+    else
+        tile_shot<true>(A + (size_t)t0 * K + j0, K, Lijj, K, L + (size_t)t0 * K + j0, K, nt, nbj, nbj, 1.f, 0.f, smem);
 }
 
 // The update of step j: block (c, r - j - 1) for c <= r (blocks above the
@@ -499,21 +609,18 @@ __global__ void __launch_bounds__(256) chol_panel_kernel(const float* __restrict
 // to the block after a barrier) while the other tiles are updated.
 __global__ void __launch_bounds__(256, 4) chol_update_kernel(float* __restrict__ A, const float* __restrict__ L,
                                                              float* __restrict__ Li, int K, int j) {
-    constexpr int kTiles = 2 * 64 * kTileLd;
-    __shared__ __align__(16) float smem[kTiles > kFactorSmem ? kTiles : kFactorSmem];
-    float* As = smem;
-    float* Bs = smem + 64 * kTileLd;
+    __shared__ __align__(16) float smem[kShotSmem > kFactorSmem ? kShotSmem : kFactorSmem];
     const int c = blockIdx.x, r = j + 1 + blockIdx.y;
     if (c > r) return;
     const int j0 = 64 * j, r0 = 64 * r, c0 = 64 * c;
     const int nbj = min(64, K - j0), nr = min(64, K - r0), nc = min(64, K - c0);
     const float* P = L + (size_t)r0 * K + j0;
-    f4 acc[2][2];
+    float* Ct = A + (size_t)r0 * K + c0;
+    const float beta = c == j ? 0.f : 1.f;
     if (c <= j)
-        tile_acc<false>(acc, P, K, Li + (size_t)j0 * K + c0, K, nr, nc, nbj, As, Bs);
+        tile_shot<false>(P, K, Li + (size_t)j0 * K + c0, K, Ct, K, nr, nc, nbj, -1.f, beta, smem);
     else
-        tile_acc<true>(acc, P, K, L + (size_t)c0 * K + j0, K, nr, nc, nbj, As, Bs);
-    tile_store(acc, A + (size_t)r0 * K + c0, K, nr, nc, -1.f, c == j ? 0.f : 1.f);
+        tile_shot<true>(P, K, L + (size_t)c0 * K + j0, K, Ct, K, nr, nc, nbj, -1.f, beta, smem);
     if (r == j + 1 && c == j + 1) {
         __syncthreads();
         chol_factor(A, K, r0, nr, Li, smem);
@@ -710,8 +817,8 @@ wq_status gptq_blocks(float* W32, const float* U, int N, int K, int gs, uint8_t*
             if ((st = wqh::launch_status()) != WQ_OK) return st;
             const int rest_in = oe - b0 - bc;
             if (rest_in > 0 &&
-                (st = sgemm_nn(N, rest_in, bc, -1.f, eb, outer, U + (size_t)b0 * K + b0 + bc, K, 1.f,
-                               W32 + b0 + bc, K, s)) != WQ_OK)
+                (st = sgemm_shot(N, rest_in, bc, -1.f, eb, outer, U + (size_t)b0 * K + b0 + bc, K, 1.f,
+                                 W32 + b0 + bc, K, s)) != WQ_OK)
                 return st;
         }
         const int rest = K - oe;
