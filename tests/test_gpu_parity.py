@@ -480,13 +480,15 @@ def test_gptq_llama_layer_sampled_rows():
     assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)
 
 
-def test_gptq_ragged_large_products():
-    # 4100 weight rows and K = 1312 (5 x 256 + 32): the walk's lazy-update
-    # products are large enough for the 128-tile product kernel and end in
-    # a partial row tile and a partial column tile.  Sampled rows include
-    # the partial tile's.
-    M, N, K = 256, 4100, 1312
-    seed = (123,)
+@pytest.mark.parametrize("K", [1312, 1344])
+def test_gptq_ragged_large_products(K):
+    # 4100 weight rows; K = 1312 (5 x 256 + 32: a last 32-column walk) and
+    # K = 1344 (5 x 256 + 64: a last outer block of one 64-column walk).  The
+    # walk's lazy-update products are large enough for the 128-tile product
+    # kernel and end in a partial row tile and a partial column tile.
+    # Sampled rows include the partial tile's.
+    M, N = 256, 4100
+    seed = (123, K)
     x = I.correlated_activations(seed, M, K)
     w = I.weights(seed, N, K, 0.02)
     codes, scales, zeros, _ = wq.gptq_quantize(dev(w), dev(x), 4, 32)
