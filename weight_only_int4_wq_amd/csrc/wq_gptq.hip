@@ -555,7 +555,9 @@ wq_status sgemm_shot(int M, int N, int Kd, float alpha, const float* A, int lda,
 // identity under the same row operations (t).  Step j publishes row j (a's
 // entries past j, zeros before; t's in full) and the pivot p = a[j][j]
 // (clamped to 1e-30 against rounding), and every row r > j takes
-// a[r] -= a[j][r] * a[j][c] / p and t[r] -= a[j][r] * t[j][c] / p.  The
+// a[r] -= a[j][r] * (a[j][c] * rcp(p)) and t[r] -= a[j][r] * (t[j][c] *
+// rcp(p)), rcp the hardware reciprocal (v_rcp_f32, about 1 ulp): the
+// pivot's division sits on the steps' serial chain.  The
 // steps go in runs of 16, the pivot rows of one wavefront: that wavefront
 // walks the run alone, updating its own rows at each step, and then the
 // wavefronts holding later rows apply the run's 16 updates in step order
@@ -597,8 +599,8 @@ __device__ __forceinline__ void chol_factor(const float* __restrict__ A, int K, 
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const float p = pd[j];
-                const float fa = hA[jj][c] / p, ft = hT[jj][c] / p;
+                const float ip = __builtin_amdgcn_rcpf(pd[j]);
+                const float fa = hA[jj][c] * ip, ft = hT[jj][c] * ip;
 #pragma unroll
                 for (int i = jj + 1; i < 16; ++i) {
                     const float m = hA[jj][16 * jb + i];
@@ -611,8 +613,8 @@ __device__ __forceinline__ void chol_factor(const float* __restrict__ A, int K, 
         if (w > jb) {
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
-                const float p = pd[16 * jb + jj];
-                const float fa = hA[jj][c] / p, ft = hT[jj][c] / p;
+                const float ip = __builtin_amdgcn_rcpf(pd[16 * jb + jj]);
+                const float fa = hA[jj][c] * ip, ft = hT[jj][c] * ip;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float m = hA[jj][16 * w + i];
