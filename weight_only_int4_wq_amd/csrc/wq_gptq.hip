@@ -931,8 +931,8 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     hipLaunchKernelGGL(rank_kernel, dim3((K + 255) / 256), dim3(256), 0, s, diag, K, act_order ? 1 : 0, perm);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
 
-    // L L^T = P H' P and Li = L^-1 (recursive halving), U = P Li P, with H'
-    // the Hessian in processing order
+    // L L^T = P H' P and Li = L^-1 (blocked, right-looking), U = P Li P,
+    // with H' the Hessian in processing order
     hipLaunchKernelGGL(permute_reverse_kernel, grid_for(KK), dim3(256), 0, s, H, perm, K, A);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
     if ((st = chol_inverse(A, L, Li, K, s)) != WQ_OK) return st;
