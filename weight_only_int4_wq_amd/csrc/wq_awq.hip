@@ -9,7 +9,7 @@
 // w_hat'.  The steps run on the library's own kernels: channel statistics,
 // fold, division, quantization, packing and the matrix-core GEMM (fp32
 // output).  The reference x . W^T comes from a plain fp16 matrix-core
-// product computed once per search; the squared differences are summed in
+// product (LDS-tiled) computed once per search; the squared differences are summed in
 // float64 in a fixed order (deterministic).
 #include "wq_gemm_common.h"
 
@@ -17,48 +17,82 @@ namespace {
 
 using namespace wq;
 
-// y32[m][n] = sum_k x[m][k] * w[n][k] (fp16 operands, fp32 accumulation):
-// 64 x 64 output tiles, four wavefronts of 32 x 32 (2 x 2 v_mfma_f32_16x16x32_f16),
-// fragments read straight from global memory (computed once per search).
+// y32[m][n] = sum_k x[m][k] * w[n][k] (fp16 operands, fp32 accumulation;
+// K a multiple of 32, x and w 16-byte aligned): 128 x 128 output tiles,
+// four wavefronts of 64 x 64 (4 x 4 v_mfma_f32_16x16x32_f16).  k advances
+// in stages of 32 through two LDS buffers (rows padded to 40 halves so
+// that the sixteen rows of a fragment read fall on distinct banks); the
+// next stage's 16-byte loads are in registers while the current stage is
+// multiplied, one barrier per stage.  A lane's fragment is 8 consecutive k
+// of one row, k = 8 * (lane / 16) + 0..7, the same in x and w.
+constexpr int kDenseLd = 40;  // halves per LDS row
+
 __global__ void __launch_bounds__(256) dense_ref_kernel(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ w, float* __restrict__ y32,
                                                         int M, int N, int K) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int LD = kDenseLd;
+    __shared__ __align__(16) uint16_t As[2][128 * LD];
+    __shared__ __align__(16) uint16_t Bs[2][128 * LD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int m0 = blockIdx.y * 64 + (wave >> 1) * 32, n0 = blockIdx.x * 64 + (wave & 1) * 32;
-    const uint16_t* ar[2];
-    const uint16_t* br[2];
+    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    // stage loads: 128 rows x 32 halves = 512 pieces of 16 bytes per operand,
+    // two per thread: row e / 4, halves 8 * (e % 4)
+    u4 ra[2], rb[2];
+    auto gload = [&](int k0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        ar[t] = x + (size_t)min(m0 + 16 * t + li, M - 1) * K + 8 * lg;
-        br[t] = w + (size_t)min(n0 + 16 * t + li, N - 1) * K + 8 * lg;
-    }
-    f4 acc[2][2];
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + 256 * q, r = e >> 2, c8 = 8 * (e & 3);
+            const int gm = min(m0 + r, M - 1), gn = min(n0 + r, N - 1);
+            ra[q] = *reinterpret_cast<const u4*>(x + (size_t)gm * K + k0 + c8);
+            rb[q] = *reinterpret_cast<const u4*>(w + (size_t)gn * K + k0 + c8);
+        }
+    };
+    auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + 256 * q, r = e >> 2, c8 = 8 * (e & 3);
+            *reinterpret_cast<u4*>(&As[buf][r * LD + c8]) = ra[q];
+            *reinterpret_cast<u4*>(&Bs[buf][r * LD + c8]) = rb[q];
+        }
+    };
+    f4 acc[4][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        h8 a[2], b[2];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            a[t] = *reinterpret_cast<const h8*>(ar[t] + k0);
-            b[t] = *reinterpret_cast<const h8*>(br[t] + k0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    const int stages = K / 32;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int st = 0; st < stages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < stages) gload(32 * (st + 1));
+        h8 a[4], b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a[t] = *reinterpret_cast<const h8*>(&As[buf][(wm + 16 * t + li) * LD + 8 * lg]);
+            b[t] = *reinterpret_cast<const h8*>(&Bs[buf][(wn + 16 * t + li) * LD + 8 * lg]);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        // the other buffer was last read in the previous stage, before the
+        // barrier that ended it
+        if (st + 1 < stages) sstore(buf ^ 1);
+        __syncthreads();
     }
     // lane holds rows 4*lg + r of column li of each 16 x 16 block
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + 16 * j + li;
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn + 16 * j + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + 16 * i + 4 * lg + r;
+                const int row = m0 + wm + 16 * i + 4 * lg + r;
                 if (row < M && col < N) y32[(size_t)row * N + col] = acc[i][j][r];
             }
         }
@@ -320,7 +354,8 @@ wq_status launch_clip(int gs, const uint16_t* x, const uint16_t* w, int M, int N
 
 wq_status wqh::dense_f32(const uint16_t* x, const uint16_t* w, float* y32, int M, int N, int K, hipStream_t s) {
     if (M <= 0 || N <= 0) return WQ_OK;
-    hipLaunchKernelGGL(dense_ref_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, x, w, y32, M, N, K);
+    if (K % 32 != 0) return WQ_ERR_ARG;
+    hipLaunchKernelGGL(dense_ref_kernel, dim3((N + 127) / 128, (M + 127) / 128), dim3(256), 0, s, x, w, y32, M, N, K);
     return wqh::launch_status();
 }
 
