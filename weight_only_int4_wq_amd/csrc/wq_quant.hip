@@ -108,7 +108,32 @@ __global__ void __launch_bounds__(256) rtn_row_kernel(const uint16_t* __restrict
     float* gz = gsc + G;
     const int n = blockIdx.x;
     const u4* row = reinterpret_cast<const u4*>(w + (size_t)n * K);
-    for (int u = threadIdx.x; u < U; u += 256) {
+    // the row's 16-byte pieces stay in registers for the quantizing pass
+    // (pieces past kCache * 256, for K > 16384, are read again)
+    constexpr int kCache = 8;
+    u4 cache[kCache];
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        cache[i] = u < U ? row[u] : u4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        if (u >= U) break;
+        const u4 v = cache[i];
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = h2f(uint16_t(in[e])), b = h2f(uint16_t(in[e] >> 16));
+            mn = fminf(mn, fminf(a, b));
+            mx = fmaxf(mx, fmaxf(a, b));
+        }
+        umin[u] = mn;
+        umax[u] = mx;
+    }
+    for (int u = threadIdx.x + 256 * kCache; u < U; u += 256) {
         const u4 v = row[u];
         const uint32_t in[4] = {v.x, v.y, v.z, v.w};
         float mn = INFINITY, mx = -INFINITY;
@@ -147,8 +172,7 @@ __global__ void __launch_bounds__(256) rtn_row_kernel(const uint16_t* __restrict
     __syncthreads();
     typedef uint32_t u2 __attribute__((ext_vector_type(2)));
     u2* crow = reinterpret_cast<u2*>(codes + (size_t)n * K);
-    for (int u = threadIdx.x; u < U; u += 256) {
-        const u4 v = row[u];
+    auto quant = [&](int u, const u4& v) {
         const uint32_t in[4] = {v.x, v.y, v.z, v.w};
         const int j = u / upg;
         const float sc = gsc[j], z = gz[j];
@@ -160,7 +184,13 @@ __global__ void __launch_bounds__(256) rtn_row_kernel(const uint16_t* __restrict
                 uint32_t(fminf(fmaxf(rintf(__fdiv_rn(h2f(uint16_t(in[i] >> 16)), sc)) + z, 0.f), float(qmax)));
         }
         crow[u] = u2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24), q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+    };
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+        const int u = threadIdx.x + 256 * i;
+        if (u < U) quant(u, cache[i]);
     }
+    for (int u = threadIdx.x + 256 * kCache; u < U; u += 256) quant(u, row[u]);
 }
 
 // --------------------------------------------------------------- AWQ ----
