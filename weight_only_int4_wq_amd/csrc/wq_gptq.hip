@@ -263,9 +263,10 @@ __device__ __forceinline__ void tile_acc(f4 (&acc)[2][2], const float* __restric
     }
 }
 
-// C = beta * C + alpha * acc on the tile at C (beta = 0: C is not read).
-// A lane holds rows 4 * (lane / 16) + r of column lane % 16 of each 16 x 16
-// block.
+// C = beta * C + alpha * acc on the tile at C (beta = 0: C is not read;
+// beta = 1: an atomic add in L2, one per element, the same rounded sum
+// without a read).  A lane holds rows 4 * (lane / 16) + r of column
+// lane % 16 of each 16 x 16 block.
 __device__ __forceinline__ void tile_store(const f4 (&acc)[2][2], float* __restrict__ C, int ldc, int mlim, int nlim,
                                            float alpha, float beta) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -281,7 +282,10 @@ __device__ __forceinline__ void tile_store(const f4 (&acc)[2][2], float* __restr
                 const int m = wm + 16 * i + 4 * lg + r;
                 if (m < mlim && n < nlim) {
                     float* p = C + (size_t)m * ldc + n;
-                    *p = (beta == 0.f ? 0.f : beta * *p) + alpha * acc[i][j][r];
+                    if (beta == 1.f)
+                        unsafeAtomicAdd(p, alpha * acc[i][j][r]);
+                    else
+                        *p = (beta == 0.f ? 0.f : beta * *p) + alpha * acc[i][j][r];
                 }
             }
         }
@@ -420,7 +424,8 @@ wq_status sgemm(int M, int N, int Kd, float alpha, const float* A, int lda, cons
 // its A row with one 16-byte load; instruction t of such a load takes
 // k = 4 * (lane / 32) + t in A and B alike (a permutation of the sum's
 // terms).  Needs N, lda, ldb and Kd multiples of 4 and A, B 16-byte
-// aligned.
+// aligned.  With beta = 1 the result goes to C by atomic adds (one per
+// element and launch, so the sum is the same; C is not read).
 typedef float f16v __attribute__((ext_vector_type(16)));
 
 __global__ void __launch_bounds__(256) sgemm128_kernel(int M, int N, int Kd, float alpha, const float* __restrict__ A,
@@ -495,7 +500,12 @@ __global__ void __launch_bounds__(256) sgemm128_kernel(int M, int N, int Kd, flo
                 const int gi = i0 + wm + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
                 if (gi < M && gj < N) {
                     float* p = C + (size_t)gi * ldc + gj;
-                    *p = (beta == 0.f ? 0.f : beta * *p) + alpha * acc[i][j][r];
+                    // one addition per element and launch: an atomic add
+                    // in L2 gives the same rounded sum without a read
+                    if (beta == 1.f)
+                        unsafeAtomicAdd(p, alpha * acc[i][j][r]);
+                    else
+                        *p = (beta == 0.f ? 0.f : beta * *p) + alpha * acc[i][j][r];
                 }
             }
         }
