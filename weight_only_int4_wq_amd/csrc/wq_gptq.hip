@@ -187,6 +187,28 @@ __global__ void __launch_bounds__(256) init_w_kernel(const uint16_t* __restrict_
     }
 }
 
+// The same without act-order (processing order = channel order): eight
+// columns per thread, 16-byte loads and stores (K a multiple of 8, w
+// 16-byte aligned).
+__global__ void __launch_bounds__(256) init_w_vec_kernel(const uint16_t* __restrict__ w,
+                                                         const uint8_t* __restrict__ dead, long long total8, int K,
+                                                         float* __restrict__ W32) {
+    for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total8; t += (long long)gridDim.x * 256) {
+        const long long e = 8 * t;
+        const int k0 = int(e % K);
+        const u4 v = *reinterpret_cast<const u4*>(w + e);
+        const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = dead[k0 + 2 * i] ? 0.f : h2f(uint16_t(in[i]));
+            o[2 * i + 1] = dead[k0 + 2 * i + 1] ? 0.f : h2f(uint16_t(in[i] >> 16));
+        }
+        *reinterpret_cast<f4*>(W32 + e) = f4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<f4*>(W32 + e + 4) = f4{o[4], o[5], o[6], o[7]};
+    }
+}
+
 // codes[n][perm[i]] = cp[n][i] and g_idx[perm[i]] = i / gs (act-order).
 __global__ void __launch_bounds__(256) unpermute_kernel(const uint8_t* __restrict__ cp, const int32_t* __restrict__ perm,
                                                         long long total, int K, int gs, uint8_t* __restrict__ codes,
@@ -951,7 +973,10 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
 
     // the column walk with lazy block updates
     const long long NK = (long long)N * K;
-    hipLaunchKernelGGL(init_w_kernel, grid_for(NK), dim3(256), 0, s, w, dead, perm, NK, K, W32);
+    if (act_order)
+        hipLaunchKernelGGL(init_w_kernel, grid_for(NK), dim3(256), 0, s, w, dead, perm, NK, K, W32);
+    else
+        hipLaunchKernelGGL(init_w_vec_kernel, grid_for(NK / 8), dim3(256), 0, s, w, dead, NK / 8, K, W32);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
     const bool sym = symmetric != 0;
     switch (bits) {
