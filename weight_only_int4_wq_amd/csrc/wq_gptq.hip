@@ -746,11 +746,13 @@ __device__ __forceinline__ void gptq_half(float (&w)[BC], float (&e)[BC], uint32
                 mx = fmaxf(mx, w[k]);
             }
         }
+        // 16-byte pieces: the group's columns past the block start and end
+        // on multiples of 32
 #pragma unroll 4
-        for (int k = b0 + BC; k < col0 + gs; ++k) {
-            const float v = wrow[k];
-            mn = fminf(mn, v);
-            mx = fmaxf(mx, v);
+        for (int k = b0 + BC; k < col0 + gs; k += 4) {
+            const f4 v = *reinterpret_cast<const f4*>(wrow + k);
+            mn = fminf(fminf(mn, v[0]), fminf(fminf(v[1], v[2]), v[3]));
+            mx = fmaxf(fmaxf(mx, v[0]), fmaxf(fmaxf(v[1], v[2]), v[3]));
         }
         const float amax = fmaxf(fabsf(mn), fabsf(mx));
         const float s32 = SYM ? __fdiv_rn(2.0f * amax, qmax) : __fdiv_rn(mx - mn, qmax);
