@@ -692,7 +692,7 @@ __global__ void __launch_bounds__(256) chol_panel_kernel(const float* __restrict
 // block diagonal return at once).  The block of tile (j + 1, j + 1), the
 // next step's diagonal block, goes on to factor it (its writes are visible
 // to the block after a barrier) while the other tiles are updated.
-__global__ void __launch_bounds__(256, 4) chol_update_kernel(float* __restrict__ A, const float* __restrict__ L,
+__global__ void __launch_bounds__(256, 3) chol_update_kernel(float* __restrict__ A, const float* __restrict__ L,
                                                              float* __restrict__ Li, int K, int j) {
     __shared__ __align__(16) float smem[kShotSmem > kFactorSmem ? kShotSmem : kFactorSmem];
     const int c = blockIdx.x, r = j + 1 + blockIdx.y;
