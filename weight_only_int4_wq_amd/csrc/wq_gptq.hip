@@ -6,8 +6,8 @@
 // Cholesky factor; the compensation is applied lazily, a block of 64
 // columns at a time, so most of the work is a matrix product.
 //
-//   H = x^T x (float32 sums of fp16 products on the matrix cores, its lower
-//   triangle only: H is symmetric); a channel with H[k][k] = 0 gets
+//   H = x^T x (float32 sums of fp16 products on the matrix cores; only its
+//   lower triangle is read afterwards); a channel with H[k][k] = 0 gets
 //   H[k][k] = 1 and a zero weight column; H += damp * mean(diag H) * I.
 //   U = the upper Cholesky factor of H^-1 (H^-1 = U^T U), computed as
 //   U = P L^-1 P with L L^T = P H P and P the index reversal, the factor
@@ -54,55 +54,6 @@ __global__ void __launch_bounds__(256) transpose_kernel(const uint16_t* __restri
         const int k = k0 + r, m = m0 + c;
         if (k < K && m < M) xt[(size_t)k * M + m] = t[c][r];
     }
-}
-
-// H = xt . xt^T (xt: [K][M] fp16, M a multiple of 32; fp32 sums on
-// v_mfma_f32_16x16x32_f16), lower 64 x 64 tiles only (tile column <= tile
-// row; blocks above return at once, the upper triangle is not written).
-// Four wavefronts of 32 x 32 per tile, fragments read straight from global
-// memory with 16-byte loads.
-__global__ void __launch_bounds__(256) gram_lower_kernel(const uint16_t* __restrict__ xt, float* __restrict__ H, int K,
-                                                         int M) {
-    if (blockIdx.x > blockIdx.y) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int li = lane & 15, lg = lane >> 4;
-    const int r0 = blockIdx.y * 64 + (wave >> 1) * 32, c0 = blockIdx.x * 64 + (wave & 1) * 32;
-    const uint16_t* ar[2];
-    const uint16_t* br[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        ar[t] = xt + (size_t)min(r0 + 16 * t + li, K - 1) * M + 8 * lg;
-        br[t] = xt + (size_t)min(c0 + 16 * t + li, K - 1) * M + 8 * lg;
-    }
-    f4 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < M; k0 += 32) {
-        h8 a[2], b[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            a[t] = *reinterpret_cast<const h8*>(ar[t] + k0);
-            b[t] = *reinterpret_cast<const h8*>(br[t] + k0);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    // lane holds rows 4 * lg + r of column li of each 16 x 16 block
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = c0 + 16 * j + li;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = r0 + 16 * i + 4 * lg + r;
-                if (row < K && col < K) H[(size_t)row * K + col] = acc[i][j][r];
-            }
-        }
 }
 
 // Dead channels and damping, one block, fixed order: dead[k] = (H[k][k] == 0),
@@ -959,8 +910,9 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     // H = x^T x, dead channels, damping
     hipLaunchKernelGGL(transpose_kernel, dim3((K + 31) / 32, (M + 31) / 32), dim3(256), 0, s, x, M, K, xt);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
-    hipLaunchKernelGGL(gram_lower_kernel, dim3((K + 63) / 64, (K + 63) / 64), dim3(256), 0, s, xt, H, K, M);
-    if ((st = wqh::launch_status()) != WQ_OK) return st;
+    // the library's LDS-tiled fp16 product (symmetric to the bit: element
+    // (i, j) and (j, i) sum the same products in the same order)
+    if ((st = wqh::dense_f32(xt, xt, H, K, K, M, s)) != WQ_OK) return st;
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, s, H, K, float(damp), dead, diag);
     hipLaunchKernelGGL(rank_kernel, dim3((K + 255) / 256), dim3(256), 0, s, diag, K, act_order ? 1 : 0, perm);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
