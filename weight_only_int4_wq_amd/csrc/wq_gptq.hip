@@ -6,8 +6,8 @@
 // Cholesky factor; the compensation is applied lazily, a block of 64
 // columns at a time, so most of the work is a matrix product.
 //
-//   H = x^T x (float32 sums of fp16 products on the matrix cores; only its
-//   lower triangle is read afterwards); a channel with H[k][k] = 0 gets
+//   H = x^T x (float32 sums of fp16 products on the matrix cores); a
+//   channel with H[k][k] = 0 gets
 //   H[k][k] = 1 and a zero weight column; H += damp * mean(diag H) * I.
 //   U = the upper Cholesky factor of H^-1 (H^-1 = U^T U), computed as
 //   U = P L^-1 P with L L^T = P H P and P the index reversal, the factor
@@ -114,15 +114,14 @@ __global__ void __launch_bounds__(256) rank_kernel(const float* __restrict__ dia
 }
 
 // dst[i][j] = H[perm[K-1-i]][perm[K-1-j]]: the Hessian in processing order,
-// index-reversed (H's lower triangle read).
+// index-reversed.
 __global__ void __launch_bounds__(256) permute_reverse_kernel(const float* __restrict__ H,
                                                               const int32_t* __restrict__ perm, int K,
                                                               float* __restrict__ dst) {
     const long long total = (long long)K * K;
     for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < total; t += (long long)gridDim.x * 256) {
         const int i = int(t / K), j = int(t % K);
-        const int a = perm[K - 1 - i], b = perm[K - 1 - j];
-        dst[t] = a >= b ? H[(size_t)a * K + b] : H[(size_t)b * K + a];
+        dst[t] = H[(size_t)perm[K - 1 - i] * K + perm[K - 1 - j]];
     }
 }
 
@@ -910,8 +909,7 @@ extern "C" wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int3
     // H = x^T x, dead channels, damping
     hipLaunchKernelGGL(transpose_kernel, dim3((K + 31) / 32, (M + 31) / 32), dim3(256), 0, s, x, M, K, xt);
     if ((st = wqh::launch_status()) != WQ_OK) return st;
-    // the library's LDS-tiled fp16 product (symmetric to the bit: element
-    // (i, j) and (j, i) sum the same products in the same order)
+    // the library's LDS-tiled fp16 product
     if ((st = wqh::dense_f32(xt, xt, H, K, K, M, s)) != WQ_OK) return st;
     hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, s, H, K, float(damp), dead, diag);
     hipLaunchKernelGGL(rank_kernel, dim3((K + 255) / 256), dim3(256), 0, s, diag, K, act_order ? 1 : 0, perm);
