@@ -178,7 +178,9 @@ wq_status wq_awq_clip(const uint16_t* x, const uint16_t* w, int32_t M, int32_t N
  * that divides 64 or is a multiple of 64.  0 <= damp < 1 (0.01 is usual).
  * workspace: device memory of at least wq_gptq_workspace_size(M, N, K)
  * bytes, 16-byte aligned (about 5 K^2 floats plus 5 N*K bytes); codes 16-byte
- * aligned.
+ * aligned.  The workspace must be ordinary (coarse-grained) device memory,
+ * as hipMalloc returns: the lazy updates add into it with floating-point
+ * atomics, which fine-grained or host memory does not support.
  * Asynchronous on `stream`.  Returns WQ_ERR_ARG for null/misaligned
  * pointers, bad sizes or a short workspace, WQ_ERR_UNSUPPORTED for other
  * bit widths. */
