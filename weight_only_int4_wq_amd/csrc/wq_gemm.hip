@@ -321,7 +321,7 @@ inline size_t split_bytes(int M, int N, int K, int bits) {
     wqh::SplitPlan p;
     const size_t inf = ~size_t(0);
     switch (tile_kind(M, N, K, bits)) {
-        case TileKind::k16: p = tile_plan<16, 128>(M, N, K, bits, inf); break;
+        case TileKind::k16: p = tile_plan<16, 64>(M, N, K, bits, inf); break;
         case TileKind::k32: p = tile_plan<32, 128>(M, N, K, bits, inf); break;
         case TileKind::k64: p = tile_plan<64, 128>(M, N, K, bits, inf); break;
         case TileKind::kLarge: p = wqh::gemm_large_plan(M, N, K, bits, inf); break;
@@ -336,7 +336,7 @@ wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t*
                       float* out32 = nullptr) {
     switch (tile_kind(M, N, K, BITS)) {
         case TileKind::k16:
-            return launch_tile<BITS, 16, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
+            return launch_tile<BITS, 16, 64, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
                                                             out32, s);
         case TileKind::k32:
             return launch_tile<BITS, 32, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
