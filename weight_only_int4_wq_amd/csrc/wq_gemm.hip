@@ -322,7 +322,7 @@ inline size_t split_bytes(int M, int N, int K, int bits) {
     const size_t inf = ~size_t(0);
     switch (tile_kind(M, N, K, bits)) {
         case TileKind::k16: p = tile_plan<16, 64>(M, N, K, bits, inf); break;
-        case TileKind::k32: p = tile_plan<32, 128>(M, N, K, bits, inf); break;
+        case TileKind::k32: p = tile_plan<32, 64>(M, N, K, bits, inf); break;
         case TileKind::k64: p = tile_plan<64, 128>(M, N, K, bits, inf); break;
         case TileKind::kLarge: p = wqh::gemm_large_plan(M, N, K, bits, inf); break;
         default: p = tile_plan<128, 256>(M, N, K, bits, inf); break;
@@ -339,7 +339,7 @@ wq_status launch_bits(const uint16_t* x, const uint32_t* packed, const uint16_t*
             return launch_tile<BITS, 16, 64, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
                                                             out32, s);
         case TileKind::k32:
-            return launch_tile<BITS, 32, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
+            return launch_tile<BITS, 32, 64, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
                                                             out32, s);
         case TileKind::k64:
             return launch_tile<BITS, 64, 128, 1, kSmallNst>(x, packed, scales, zeros, y, M, N, K, gs, part, part_bytes,
