@@ -80,6 +80,9 @@ FORMAT_CASES = [
     (8, 128, True, True, 33, 512),
     (8, 32, False, False, 33, 512),
     (4, 64, True, False, 17, 4096),
+    # rows longer than the 16384 channels the RTN kernel keeps in registers
+    (4, 128, False, False, 9, 16896),
+    (8, -1, True, False, 5, 16896),
 ]
 
 
