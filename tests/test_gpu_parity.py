@@ -531,8 +531,10 @@ def _check_clip(x, w, bits, gs, sym, ref, w_clip, best, losses, n_grid=20):
     Lmin = L.min(axis=2)
     Lb = np.take_along_axis(L, b[:, :, None], axis=2)[:, :, 0]
     assert np.all(Lb <= Lmin * (1 + 1e-2) + 1e-9 * scale)
+    # every case measured agrees on all groups; near-tied losses may still
+    # pick a neighbouring ratio, which the minimum check above accepts
     agree = np.mean(b == ref["best"])
-    assert agree >= 0.9, agree
+    assert agree >= 0.99, agree
     # clipped weights: bit-exact against the clip at the chosen ratio
     N, K = w.shape
     gsz = K if gs == -1 else gs
@@ -637,10 +639,9 @@ def test_gptq_act_order_matches_oracle(M, N, K, bits, gs, sym):
     assert np.array_equal(host(g_idx), ref["g_idx"])
     c = host(codes)
     agree = np.mean(c == ref["codes"])
-    # a decision that flips in fp32 cascades through the rest of its row's
-    # compensation: bound the rows that differ, and the codes overall
-    rows_equal = np.mean(np.all(c == ref["codes"], axis=1))
-    assert agree >= 0.99 and rows_equal >= 0.9, (agree, rows_equal)
+    # the fixed-order bar: every case measured at 100 % agreement, and the
+    # bar leaves room for one fp32 decision flip cascading through a row
+    assert agree >= 0.997, agree
     w_hat = O.dequant(c, host(scales), None if sym else host(zeros), bits, gs, ref["g_idx"])
     e_gpu, e_ref = _gptq_out_err(w, x, w_hat), _gptq_out_err(w, x, ref["w_hat"])
     assert abs(e_gpu / e_ref - 1) <= 0.01, (e_gpu, e_ref)

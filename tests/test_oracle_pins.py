@@ -11,17 +11,7 @@ import pytest
 import oracle as O
 import wq_inputs as I
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-
-
-def _read_fixture(name):
-    rows = []
-    with open(os.path.join(GOLDEN, name)) as f:
-        for line in f:
-            line = line.strip()
-            if line and not line.startswith("#"):
-                rows.append(line.split())
-    return rows
+from fixtures import read_fixture as _read_fixture
 
 
 # ----------------------------------------------------------------- packing

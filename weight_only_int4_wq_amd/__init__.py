@@ -57,8 +57,15 @@ for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
                                   _VP, ctypes.c_size_t, _VP])
 
 
+WQ_ERR_ARG, WQ_ERR_UNSUPPORTED, WQ_ERR_HIP = 1, 2, 3
+
+
 class WQError(RuntimeError):
-    """A libwq entry point returned a non-zero status."""
+    """A libwq entry point returned a non-zero status (kept in `status`)."""
+
+    def __init__(self, msg, status=0):
+        super().__init__(msg)
+        self.status = status
 
 
 def lib() -> ctypes.CDLL:
@@ -99,7 +106,7 @@ def gemv_max_m() -> int:
 
 def _check(code: int, what: str) -> None:
     if code != 0:
-        raise WQError(f"{what}: {status_str(code)} (status {code})")
+        raise WQError(f"{what}: {status_str(code)} (status {code})", code)
 
 
 # ----------------------------------------------------------- marshalling --
@@ -109,7 +116,11 @@ def _torch():
     return torch
 
 
-def _dev(t, dtype, name, ndim=None, allow_none=False):
+def _dev(t, dtype, name, ndim=None, allow_none=False, shape=None, device=None):
+    """Check a tensor argument: dtype, contiguity, rank, and when given its
+    exact shape and device (the C ABI sees only pointers, so a short or
+    misplaced buffer must be caught here).  That it is a GPU tensor is
+    checked when its pointer is taken, after every shape check."""
     torch = _torch()
     if t is None:
         if allow_none:
@@ -117,19 +128,25 @@ def _dev(t, dtype, name, ndim=None, allow_none=False):
         raise ValueError(f"{name} is required")
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor arguments must be GPU tensors, got one on {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(device=None):
@@ -148,8 +165,8 @@ def quantize_rtn(w, bits: int, group_size: int, perm=None, symmetric: bool = Fal
     [N][G], zeros u8 [N][G] or None)."""
     torch = _torch()
     w = _dev(w, torch.float16, "w", 2)
-    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
     N, K = w.shape
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True, shape=(K,), device=w.device)
     G = _groups(K, group_size)
     codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     scales = torch.empty((N, G), dtype=torch.float16, device=w.device)
@@ -174,9 +191,9 @@ def awq_fold(w, s, out=None):
     """fp16(W[n][k] * s[k])."""
     torch = _torch()
     w = _dev(w, torch.float16, "w", 2)
-    s = _dev(s, torch.float16, "s", 1)
     N, K = w.shape
-    out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2)
+    s = _dev(s, torch.float16, "s", 1, shape=(K,), device=w.device)
+    out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2, shape=(N, K), device=w.device)
     _check(lib().wq_awq_fold(_ptr(w), _ptr(s), N, K, _ptr(out), _stream(w.device)), "wq_awq_fold")
     return out
 
@@ -187,7 +204,7 @@ def awq_search(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, sym
     index); alpha_i = i / (n_grid - 1).  Synchronizes the stream."""
     torch = _torch()
     x = _dev(x, torch.float16, "x", 2)
-    w = _dev(w, torch.float16, "w", 2)
+    w = _dev(w, torch.float16, "w", 2, device=x.device)
     M, K = x.shape
     N = w.shape[0]
     if w.shape[1] != K:
@@ -212,12 +229,12 @@ def awq_clip(x, w, bits: int = 4, group_size: int = 128, n_grid: int = 20, n_rat
     [N][G], losses fp32 [N][G][n_ratios] or None).  out may be w (in place)."""
     torch = _torch()
     x = _dev(x, torch.float16, "x", 2)
-    w = _dev(w, torch.float16, "w", 2)
+    w = _dev(w, torch.float16, "w", 2, device=x.device)
     N, K = w.shape
     if x.shape[1] != K:
         raise ValueError("x must be [M][K] with the K of w")
     G = _groups(K, group_size)
-    out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2)
+    out = torch.empty_like(w) if out is None else _dev(out, torch.float16, "out", 2, shape=(N, K), device=w.device)
     best = torch.empty((N, G), dtype=torch.int32, device=w.device)
     losses = torch.empty((N, G, n_ratios), dtype=torch.float32, device=w.device) if with_losses else None
     _check(lib().wq_awq_clip(_ptr(x), _ptr(w), x.shape[0], N, K, bits, group_size, int(bool(symmetric)), n_grid,
@@ -233,7 +250,7 @@ def gptq_quantize(w, x, bits: int = 4, group_size: int = 128, symmetric: bool = 
     group map."""
     torch = _torch()
     w = _dev(w, torch.float16, "w", 2)
-    x = _dev(x, torch.float16, "x", 2)
+    x = _dev(x, torch.float16, "x", 2, device=w.device)
     N, K = w.shape
     M = x.shape[0]
     if x.shape[1] != K:
@@ -269,8 +286,8 @@ def pack(codes, bits: int, group_size: int = -1, g_idx=None):
     words, perm int32 [K] or None)."""
     torch = _torch()
     codes = _dev(codes, torch.uint8, "codes", 2)
-    g_idx = _dev(g_idx, torch.int32, "g_idx", 1, allow_none=True)
     N, K = codes.shape
+    g_idx = _dev(g_idx, torch.int32, "g_idx", 1, allow_none=True, shape=(K,), device=codes.device)
     if (K * bits) % 32:
         raise ValueError("K * bits must be a multiple of 32")
     packed = torch.empty((N, K * bits // 32), dtype=torch.int32, device=codes.device)
@@ -283,7 +300,7 @@ def pack(codes, bits: int, group_size: int = -1, g_idx=None):
 def unpack(packed, bits: int, K: int, perm=None):
     torch = _torch()
     packed = _dev(packed, torch.int32, "packed", 2)
-    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True, shape=(K,), device=packed.device)
     N = packed.shape[0]
     if packed.shape[1] * 32 != K * bits:
         raise ValueError("packed width does not match K * bits / 32")
@@ -297,9 +314,10 @@ def dequant(packed, scales, zeros, bits: int, group_size: int, K: int, perm=None
     """fp16 dequantized weights [N][K] in original channel order."""
     torch = _torch()
     packed = _dev(packed, torch.int32, "packed", 2)
-    scales = _dev(scales, torch.float16, "scales", 2)
-    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
-    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    d = packed.device
+    scales = _dev(scales, torch.float16, "scales", 2, device=d)
+    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True, device=d)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True, device=d)
     N = packed.shape[0]
     _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
     w = torch.empty((N, K), dtype=torch.float16, device=packed.device)
@@ -320,15 +338,29 @@ def _check_meta(N, K, bits, group_size, packed, scales, zeros, perm):
         raise ValueError("perm must be [K]")
 
 
+def _layer_args(x, packed, scales, zeros, perm, bits, group_size):
+    """Check the operands of a product call: types, shapes against x's K and
+    packed's N, and that every one lives on x's device."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x", 2)
+    d = x.device
+    packed = _dev(packed, torch.int32, "packed", 2, device=d)
+    scales = _dev(scales, torch.float16, "scales", 2, device=d)
+    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True, device=d)
+    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True, device=d)
+    _check_meta(packed.shape[0], x.shape[1], bits, group_size, packed, scales, zeros, perm)
+    return x, packed, scales, zeros, perm
+
+
 # ----------------------------------------------------------- hot path ----
 
 def scale_act(x, s, out=None):
     """fp16(x / s) per input channel (AWQ activation side)."""
     torch = _torch()
     x = _dev(x, torch.float16, "x", 2)
-    s = _dev(s, torch.float16, "s", 1)
     M, K = x.shape
-    out = torch.empty_like(x) if out is None else _dev(out, torch.float16, "out", 2)
+    s = _dev(s, torch.float16, "s", 1, shape=(K,), device=x.device)
+    out = torch.empty_like(x) if out is None else _dev(out, torch.float16, "out", 2, shape=(M, K), device=x.device)
     _check(lib().wq_scale_act(_ptr(x), _ptr(s), M, K, _ptr(out), _stream(x.device)), "wq_scale_act")
     return out
 
@@ -341,23 +373,18 @@ def workspace_size(M: int, N: int, K: int, bits: int, has_perm: bool) -> int:
 
 def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, out=None, workspace=None):
     torch = _torch()
-    x = _dev(x, torch.float16, "x", 2)
-    packed = _dev(packed, torch.int32, "packed", 2)
-    scales = _dev(scales, torch.float16, "scales", 2)
-    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
-    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    x, packed, scales, zeros, perm = _layer_args(x, packed, scales, zeros, perm, bits, group_size)
     M, K = x.shape
     N = packed.shape[0]
-    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
     y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
-        _dev(out, torch.float16, "out", 2)
+        _dev(out, torch.float16, "out", 2, shape=(M, N), device=x.device)
     uses_gemm = entry == "wq_gemm" or (entry == "wq_linear" and M > gemv_max_m())
     need = workspace_size(M, N, K, bits, perm is not None) if uses_gemm else 0
     ws_bytes = 0
     if need:
         if workspace is None:
             workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
-        workspace = _dev(workspace, torch.uint8, "workspace", 1)
+        workspace = _dev(workspace, torch.uint8, "workspace", 1, device=x.device)
         ws_bytes = workspace.numel()
     else:
         workspace = None
@@ -386,18 +413,13 @@ def gemv_silu_mul(x, packed, scales, zeros, bits: int, group_size: int, perm=Non
     """Fused gate/up decode projection: packed holds the gate rows stacked
     over the up rows (N = 2I); returns fp16 [M][I] = silu(gate) * up."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x", 2)
-    packed = _dev(packed, torch.int32, "packed", 2)
-    scales = _dev(scales, torch.float16, "scales", 2)
-    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
-    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
+    x, packed, scales, zeros, perm = _layer_args(x, packed, scales, zeros, perm, bits, group_size)
     M, K = x.shape
     N = packed.shape[0]
-    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
     if N % 2:
         raise ValueError("the stacked gate/up weight needs an even row count")
     y = torch.empty((M, N // 2), dtype=torch.float16, device=x.device) if out is None else \
-        _dev(out, torch.float16, "out", 2)
+        _dev(out, torch.float16, "out", 2, shape=(M, N // 2), device=x.device)
     _check(lib().wq_gemv_silu_mul(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(y), M, N, K,
                                   bits, group_size, _stream(x.device)), "wq_gemv_silu_mul")
     return y
@@ -410,23 +432,16 @@ def gemv_ex(x, packed, scales, zeros, bits: int, group_size: int, perm=None, act
     (fp16 [N]) added before the output rounding; with silu the stacked
     gate/up epilogue of gemv_silu_mul (bias on both halves first)."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x", 2)
-    packed = _dev(packed, torch.int32, "packed", 2)
-    scales = _dev(scales, torch.float16, "scales", 2)
-    zeros = _dev(zeros, torch.uint8, "zeros", 2, allow_none=True)
-    perm = _dev(perm, torch.int32, "perm", 1, allow_none=True)
-    act_scale = _dev(act_scale, torch.float16, "act_scale", 1, allow_none=True)
-    bias = _dev(bias, torch.float16, "bias", 1, allow_none=True)
+    x, packed, scales, zeros, perm = _layer_args(x, packed, scales, zeros, perm, bits, group_size)
     M, K = x.shape
     N = packed.shape[0]
-    _check_meta(N, K, bits, group_size, packed, scales, zeros, perm)
-    if act_scale is not None and act_scale.shape[0] != K:
-        raise ValueError("act_scale must have K entries")
-    if bias is not None and bias.shape[0] != N:
-        raise ValueError("bias must have N entries")
+    act_scale = _dev(act_scale, torch.float16, "act_scale", 1, allow_none=True, shape=(K,), device=x.device)
+    bias = _dev(bias, torch.float16, "bias", 1, allow_none=True, shape=(N,), device=x.device)
+    if silu and N % 2:
+        raise ValueError("the stacked gate/up weight needs an even row count")
     cols = N // 2 if silu else N
     y = torch.empty((M, cols), dtype=torch.float16, device=x.device) if out is None else \
-        _dev(out, torch.float16, "out", 2)
+        _dev(out, torch.float16, "out", 2, shape=(M, cols), device=x.device)
     _check(lib().wq_gemv_ex(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(act_scale),
                             _ptr(bias), _ptr(y), M, N, K, bits, group_size, int(bool(silu)), _stream(x.device)),
            "wq_gemv_ex")
@@ -462,13 +477,15 @@ class QuantizedLinear:
 
     def __call__(self, x, out=None, workspace=None, kernel: str = "linear"):
         if self.act_scale is not None:
-            M = x.shape[0]
-            mt = 1 if M <= 1 else 2 if M <= 2 else 4
-            fits = 1 <= M <= 4 and mt * (2 * self.K + (self.K // 32) * 8) <= 64 * 1024
-            if kernel in ("linear", "gemv") and fits:
-                # decode: the division happens while the GEMV stages x
-                return gemv_ex(x, self.packed, self.scales, self.zeros, self.bits, self.group_size, perm=self.perm,
-                               act_scale=self.act_scale, out=out)
+            if kernel in ("linear", "gemv") and 1 <= x.shape[0] <= gemv_max_m():
+                # decode: the division happens while the GEMV stages x; the
+                # library reports the shapes its fused kernel does not take
+                try:
+                    return gemv_ex(x, self.packed, self.scales, self.zeros, self.bits, self.group_size,
+                                   perm=self.perm, act_scale=self.act_scale, out=out)
+                except WQError as e:
+                    if e.status != WQ_ERR_UNSUPPORTED:
+                        raise
             x = scale_act(x, self.act_scale)
         fn = {"linear": linear, "gemv": gemv, "gemm": gemm}[kernel]
         return fn(x, self.packed, self.scales, self.zeros, self.bits, self.group_size, self.perm, out, workspace)

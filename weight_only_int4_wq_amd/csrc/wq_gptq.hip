@@ -93,9 +93,21 @@ __global__ void __launch_bounds__(256) upper_reverse_kernel(const float* __restr
     }
 }
 
+// Sort key of a float under a total order: the bit pattern mapped so that
+// unsigned comparison follows the float order (-inf < ... < -0 < +0 < ...
+// < +inf), with every NaN below all numbers.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    if (v != v) return 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 // Processing order: perm[i] = the channel of rank i.  With act-order the
 // rank is the position in descending diag order, ties by channel index (a
-// stable sort); otherwise the identity.
+// stable sort); otherwise the identity.  The comparison is a strict total
+// order on (key, index), so the ranks are a permutation of 0..K-1 even when
+// the diagonal holds NaN (from non-finite calibration data): every perm slot
+// is written exactly once.
 __global__ void __launch_bounds__(256) rank_kernel(const float* __restrict__ diag, int K, int act_order,
                                                    int32_t* __restrict__ perm) {
     const int k = blockIdx.x * 256 + threadIdx.x;
@@ -104,10 +116,10 @@ __global__ void __launch_bounds__(256) rank_kernel(const float* __restrict__ dia
         perm[k] = k;
         return;
     }
-    const float d = diag[k];
+    const uint32_t d = order_key(diag[k]);
     int rank = 0;
     for (int j = 0; j < K; ++j) {
-        const float e = diag[j];
+        const uint32_t e = order_key(diag[j]);
         rank += (e > d || (e == d && j < k)) ? 1 : 0;
     }
     perm[rank] = k;
