@@ -59,7 +59,8 @@ typedef enum {
     WQ_OK = 0,
     WQ_ERR_ARG = 1,          /* null/misaligned pointer, bad shape or group map */
     WQ_ERR_UNSUPPORTED = 2,  /* bit width or M outside what the kernel handles  */
-    WQ_ERR_HIP = 3           /* a HIP runtime call failed                        */
+    WQ_ERR_HIP = 3,          /* a HIP runtime call failed                        */
+    WQ_ERR_TOO_LARGE = 4     /* needs more than wq_linear_noalloc's static scratch */
 } wq_status;
 
 /* Static, NUL-terminated description of a status code. */
@@ -274,6 +275,28 @@ wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const uint16_t* s
                     const uint8_t* zeros, const int32_t* perm, uint16_t* y,
                     int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* wq_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same dispatch and kernels as wq_linear, with the GEMM's scratch (the
+ * act-order activation gather, then split-K fp32 partials) in a static
+ * device array of WQ_NOALLOC_SCRATCH_BYTES bytes inside the library instead
+ * of a caller workspace.  Each GPU holds its own copy of the array from the
+ * first call on it until the process ends; the call looks up the current
+ * device's copy (hipGetSymbolAddress) on its first use there and allocates
+ * nothing.  The array keeps the last call's contents and nothing in it
+ * needs clearing (every byte read is first written by the same call).
+ * Every call on one GPU shares the array, so calls on one GPU must be
+ * ordered (one stream, or synchronized): overlapping calls race.  The
+ * current device must be the stream's device.  Returns WQ_ERR_TOO_LARGE
+ * when act-order needs a gather of more than WQ_NOALLOC_SCRATCH_BYTES
+ * (M*K*2 bytes, rounded up to 256); with too little room for the split-K
+ * partials the GEMM splits K fewer ways.  Otherwise as wq_linear. */
+#define WQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+wq_status wq_linear_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                            const uint8_t* zeros, const int32_t* perm, uint16_t* y,
+                            int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
+                            void* stream);
 
 /* Fused gate/up projection with its activation, for decode batches
  * (1 <= M <= 4): the N rows of packed/scales/zeros are a gate projection

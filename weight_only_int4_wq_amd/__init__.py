@@ -18,6 +18,7 @@ __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
     "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "awq_clip", "gptq_quantize", "act_order_perm", "pack", "unpack",
     "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_ex", "gemv_max_m",
+    "linear_noalloc", "noalloc_scratch_bytes",
     "status_str", "version", "QuantizedLinear",
 ]
 
@@ -51,13 +52,14 @@ _SIG = {
     "wq_awq_clip": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
 }
 _SIG["wq_gemv_silu_mul"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
+_SIG["wq_linear_noalloc"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
 _SIG["wq_gemv_ex"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _VP])
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
     _SIG[_name] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
                                   _VP, ctypes.c_size_t, _VP])
 
 
-WQ_ERR_ARG, WQ_ERR_UNSUPPORTED, WQ_ERR_HIP = 1, 2, 3
+WQ_ERR_ARG, WQ_ERR_UNSUPPORTED, WQ_ERR_HIP, WQ_ERR_TOO_LARGE = 1, 2, 3, 4
 
 
 class WQError(RuntimeError):
@@ -407,6 +409,28 @@ def gemm(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=No
 def linear(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
     """Batch-size dispatch between gemv and gemm."""
     return _matmul("wq_linear", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of linear_noalloc's static scratch array (WQ_NOALLOC_SCRATCH_BYTES
+    in include/wq.h)."""
+    with open(header_path) as f:
+        m = re.search(r"#define\s+WQ_NOALLOC_SCRATCH_BYTES\s+\((\d+)u \* (\d+)u \* (\d+)u\)", f.read())
+    return int(m.group(1)) * int(m.group(2)) * int(m.group(3))
+
+
+def linear_noalloc(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None):
+    """linear without a workspace: the library's static scratch array holds
+    the GEMM's intermediates.  Calls on one GPU must be ordered."""
+    torch = _torch()
+    x, packed, scales, zeros, perm = _layer_args(x, packed, scales, zeros, perm, bits, group_size)
+    M, K = x.shape
+    N = packed.shape[0]
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
+        _dev(out, torch.float16, "out", 2, shape=(M, N), device=x.device)
+    _check(lib().wq_linear_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(zeros), _ptr(perm), _ptr(y), M, N, K,
+                                   bits, group_size, _stream(x.device)), "wq_linear_noalloc")
+    return y
 
 
 def gemv_silu_mul(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None):

@@ -37,6 +37,9 @@ extern "C" const char* wq_status_str(wq_status s) {
         case WQ_ERR_ARG: return "invalid argument (null or misaligned pointer, bad shape, group size or group map)";
         case WQ_ERR_UNSUPPORTED: return "unsupported configuration (bit width or row count)";
         case WQ_ERR_HIP: return "HIP runtime call failed";
+        case WQ_ERR_TOO_LARGE:
+            return "problem needs more scratch memory than wq_linear_noalloc's static buffer holds "
+                   "(act-order gather of M*K fp16 values over WQ_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
