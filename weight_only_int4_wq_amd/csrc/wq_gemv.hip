@@ -17,6 +17,8 @@
 // the activations are staged so the two latencies overlap.  Activations are
 // staged once per block in LDS, in the pair order the decoder produces,
 // gathered through perm for act-order; long K runs in LDS-sized slabs.
+#include <algorithm>
+
 #include "wq_common.h"
 
 namespace {
@@ -382,35 +384,49 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int my_groups = wg0 < n_groups ? (n_groups - wg0 + wstride - 1) / wstride : 0;
     const int T = my_groups * J;  // flat (row group, slot iteration) count of this wave
 
-    // issue-side and compute-side positions in the flat sequence
-    int i_rg = wg0, i_j = 0, c_rg = wg0, c_j = 0;
+    // issue-side and compute-side positions in the flat sequence (the
+    // compute side's row group is counted by c_k below)
+    int i_rg = wg0, i_j = 0, c_j = 0;
 
+    // Loads are issued unconditionally: a wait-count merge at a branch around
+    // them would make every later wait drain all loads in flight.  The issue
+    // position stops at the wavefront's last one (t = T - 1), so the refills
+    // past it re-read the chunks it loaded last, and lanes past a row's end
+    // re-read its last chunk (same cache lines, no extra memory traffic and
+    // no address shared by the whole grid).
     WideSlot<BITS, R, CPL> slot[D];
     auto issue = [&](WideSlot<BITS, R, CPL>& sl, int t) {
         const bool tv = t < T;  // wave-uniform
         const int cp = lane + 64 * i_j;
         const bool valid = tv && cp < CNP;
-        const int cpc = valid ? cp : 0;
+        const int cpc = cp < CNP ? cp : CNP - 1;
         const int g = chunk_group(cpc * CPL, gd);
+        // row bases are wave-uniform (scalar registers), lane offsets
+        // unsigned 32-bit: the loads take the scalar-base form with no
+        // per-lane 64-bit address arithmetic
+        const uint32_t woff = uint32_t(cpc) * uint32_t(CPL * BITS * 4);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int n = SILU ? i_rg + r * half : i_rg * R + r;
-            const bool nok = tv && n < N;  // wave-uniform
-            const int nn = nok ? n : 0;
+            const bool nok = n < N;  // wave-uniform
+            const int nn = __builtin_amdgcn_readfirstlane(nok ? n : N - 1);
             sl.ok[r] = valid && nok;
-            const uint32_t* rowp = packed + (size_t)nn * row_words;
-            const uint32_t* src = rowp + cpc * (CPL * BITS);
+            const char* rowp = reinterpret_cast<const char*>(packed) + size_t(nn) * row_words * 4;
 #pragma unroll
-            for (int e = 0; e < CPL; ++e) load_chunk<BITS>(src + e * BITS, sl.w[r][e]);
-            sl.s[r] = (scales + (size_t)nn * G)[g];
+            for (int e = 0; e < CPL; ++e)
+                load_chunk<BITS>(reinterpret_cast<const uint32_t*>(rowp + woff + e * BITS * 4), sl.w[r][e]);
+            sl.s[r] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(scales) + size_t(nn) * G * 2 +
+                                                         uint32_t(g) * 2u);
             if constexpr (HAS_Z)
-                sl.z[r] = (zeros + (size_t)nn * G)[g];
+                sl.z[r] = *(reinterpret_cast<const uint8_t*>(zeros) + size_t(nn) * G + uint32_t(g));
             else
                 sl.z[r] = 1u << (BITS - 1);
         }
-        const bool wrap = (i_j + 1 == J);
-        i_j = wrap ? 0 : i_j + 1;
-        i_rg += wrap ? wstride : 0;
+        if (t + 1 < T) {  // advance (no memory access on either path)
+            const bool wrap = (i_j + 1 == J);
+            i_j = wrap ? 0 : i_j + 1;
+            i_rg += wrap ? wstride : 0;
+        }
     };
 
     // ---- activation loads of the first staging pass go out before the
@@ -571,11 +587,12 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
 
     __syncthreads();
 
-    float acc[R][MT];
+    float acc[R][MT], out[R][MT];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+        for (int m = 0; m < MT; ++m) acc[r][m] = out[r][m] = 0.f;
+    int c_k = 0;  // ordinal of the compute side's row group in this wavefront
 
     for (int t0 = 0; t0 < T; t0 += D) {
 #pragma unroll
@@ -627,50 +644,61 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                     }
                 }
             }
-            // ---- end of a row group: reduce across the wavefront and store
+            // ---- end of a row group: reduce across the wavefront and keep
+            // the sums in the `out` registers of lane k * R + r, k the group's
+            // ordinal in this wavefront (no store inside the loop: a store on
+            // some paths would also make the wait counts conservative)
             if (c_j == J - 1 && t < T) {
-                if constexpr (SILU) {
+                const int k = c_k * (SILU ? 1 : R);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        float g = wave_sum_last(acc[0][m]);
-                        float u = wave_sum_last(acc[1][m]);
-                        acc[0][m] = 0.f;
-                        acc[1][m] = 0.f;
-                        if (lane == 63 && m < M) {
-                            if constexpr (EX) {
-                                if (bias) {
-                                    g += float(__builtin_bit_cast(_Float16, bias[c_rg]));
-                                    u += float(__builtin_bit_cast(_Float16, bias[c_rg + half]));
-                                }
-                            }
-                            const float v = g / (1.0f + expf(-g)) * u;
-                            y[(size_t)m * half + c_rg] = __builtin_bit_cast(uint16_t, (_Float16)v);
-                        }
+                        const float v = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_sum_last(acc[r][m])), 63));
+                        acc[r][m] = 0.f;
+                        out[r][m] = lane == k + (SILU ? 0 : r) ? v : out[r][m];
                     }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const int n = c_rg * R + r;
-#pragma unroll
-                        for (int m = 0; m < MT; ++m) {
-                            float v = wave_sum_last(acc[r][m]);
-                            acc[r][m] = 0.f;
-                            if constexpr (EX) {
-                                if (bias && lane == 63 && n < N) v += float(__builtin_bit_cast(_Float16, bias[n]));
-                            }
-                            if (lane == 63 && n < N && m < M)
-                                y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
-                        }
-                    }
-                }
+                ++c_k;
             }
-            {
-                const bool wrap = (c_j + 1 == J);
-                c_j = wrap ? 0 : c_j + 1;
-                c_rg += wrap ? wstride : 0;
-            }
+            c_j = c_j + 1 == J ? 0 : c_j + 1;
             // ---- refill slot d with iteration t + D
             issue(slot[d], t + D);
+        }
+    }
+    // ---- outputs: lane k * R + r holds row R * (wg0 + k * wstride) + r (with
+    // SILU: lane k holds gate/up pair wg0 + k * wstride)
+    const int k = SILU ? lane : lane / R;
+    if (k < my_groups) {
+        const int rg = wg0 + k * wstride;
+        if constexpr (SILU) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                float g = out[0][m], u = out[1][m];
+                if constexpr (EX) {
+                    if (bias) {
+                        g += float(__builtin_bit_cast(_Float16, bias[rg]));
+                        u += float(__builtin_bit_cast(_Float16, bias[rg + half]));
+                    }
+                }
+                const float v = g / (1.0f + expf(-g)) * u;
+                if (m < M) y[(size_t)m * half + rg] = __builtin_bit_cast(uint16_t, (_Float16)v);
+            }
+        } else {
+            const int r = lane % R;
+            const int n = rg * R + r;
+            if (n < N) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int q = 0; q < R; ++q) v = q == r ? out[q][m] : v;
+                    if constexpr (EX) {
+                        if (bias) v += float(__builtin_bit_cast(_Float16, bias[n]));
+                    }
+                    if (m < M) y[(size_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
+                }
+            }
         }
     }
 }
@@ -733,9 +761,14 @@ wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
+    // One round of resident blocks (more wavefronts in flight beat equal
+    // shares: measured), unless a wavefront would take more than 64 / R row
+    // groups (it keeps one finished output per lane until its end).
     const int n_groups = SILU ? N / 2 : (N + R - 1) / R;
+    const int max_per_wave = SILU ? 64 : 64 / R;
     int blocks = (n_groups + kStreamWaves - 1) / kStreamWaves;
     if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
+    blocks = std::max(blocks, (n_groups + kStreamWaves * max_per_wave - 1) / (kStreamWaves * max_per_wave));
     const size_t lds = stream_lds_bytes(MT, K, CPL, perm != nullptr);
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros && perm)
