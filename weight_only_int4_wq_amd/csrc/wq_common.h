@@ -33,13 +33,19 @@ constexpr uint32_t kMagic2 = 0x64006400u;  // fp16 pair (1024, 1024)
 __device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// (a & mask) | magic in one VALU instruction.  The compiler splits this into
-// two (its VOP3 form cannot take two literal constants), so it is written
-// out: mask travels in an SGPR, magic in a VGPR.
+// (a & mask) | magic in one v_and_or_b32.  With both constants visible the
+// compiler splits it into an and and an or (the VOP3 encoding cannot carry
+// two literals), so the empty asm statements hide their values: mask comes
+// to sit in an SGPR, magic in a VGPR, and the compiler selects the single
+// instruction itself.  The instruction must not be written as inline asm:
+// the compiler does not count an asm statement as a vector-ALU instruction
+// when it inserts the wait states between the vector ALU and the matrix
+// cores, and a decoded word written over the accumulator input of a matrix
+// instruction still in flight corrupts its result.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-    return r;
+    asm("" : "+s"(mask));
+    asm("" : "+v"(magic));
+    return (a & mask) | magic;
 }
 
 // Number of 32-bit words in one 32-code chunk of a `bits`-wide code stream.
