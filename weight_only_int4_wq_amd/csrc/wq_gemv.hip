@@ -861,7 +861,14 @@ wq_status launch_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* s
 
 }  // namespace
 
+#ifndef WQ_SKINNY_MIN_M
+#define WQ_SKINNY_MIN_M 2
+#endif
+
 namespace wqh {
+wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                      const int32_t* perm, uint16_t* y, int M, int N, int K, int bits, int gs, hipStream_t s,
+                      const uint16_t* act_scale, const uint16_t* bias);
 wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* y,
                             int M, int N, int K, int bits, int group_size, int* gs_out);
 }
@@ -878,6 +885,10 @@ extern "C" wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const ui
     if (M > 16) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M >= WQ_SKINNY_MIN_M) {
+        const wq_status st2 = wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, nullptr, nullptr);
+        if (st2 != WQ_ERR_UNSUPPORTED) return st2;
+    }
     switch (bits) {
         case 2: return launch_bits<2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
         case 3: return launch_bits<3>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
@@ -919,6 +930,10 @@ extern "C" wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool sl = silu != 0;
+    if (!sl && M >= WQ_SKINNY_MIN_M) {  // the kernel wq_gemv uses for this M
+        const wq_status st2 = wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, act_scale, bias);
+        if (st2 != WQ_ERR_UNSUPPORTED) return st2;
+    }
     switch (bits) {
         case 2: return launch_ex<2>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);
         case 3: return launch_ex<3>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);
