@@ -332,6 +332,16 @@ wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* 
                      const uint16_t* bias, uint16_t* y, int32_t M, int32_t N, int32_t K,
                      int32_t bits, int32_t group_size, int32_t silu, void* stream);
 
+/* Measurement reference, not part of the layer: reads `bytes` bytes (a
+ * multiple of 16) from device memory src (16-byte aligned) with coalesced
+ * 16-byte non-temporal loads, grid-stride, and writes to the device word
+ * sink only in the astronomically unlikely case that the XOR of the data
+ * equals a fixed constant (so the loads cannot be optimized away).  It is
+ * the achievable streaming-read bandwidth the decode kernels are compared
+ * with, launched and timed the same way.  WQ_ERR_ARG for null or misaligned
+ * pointers or a size that is not a multiple of 16; asynchronous. */
+wq_status wq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Largest M that wq_linear sends to wq_gemv. */
 int32_t wq_gemv_max_m(void);
 

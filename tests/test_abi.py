@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
                 "wq_act_order_perm", "wq_pack", "wq_unpack", "wq_dequant", "wq_scale_act",
                 "wq_workspace_size", "wq_gemv", "wq_gemm", "wq_linear", "wq_gemv_max_m",
                 "wq_awq_search", "wq_awq_search_workspace_size", "wq_gemv_silu_mul",
-                "wq_gptq_quantize", "wq_gptq_workspace_size", "wq_awq_clip", "wq_gemv_ex", "wq_linear_noalloc"}
+                "wq_gptq_quantize", "wq_gptq_workspace_size", "wq_awq_clip", "wq_gemv_ex", "wq_linear_noalloc", "wq_stream_read"}
     assert set(names) == expected
     handle = wq.lib()
     for name in names:

@@ -18,7 +18,7 @@ __all__ = [
     "lib", "lib_path", "header_path", "exported_names", "WQError",
     "quantize_rtn", "awq_scales", "awq_fold", "awq_search", "awq_clip", "gptq_quantize", "act_order_perm", "pack", "unpack",
     "dequant", "scale_act", "workspace_size", "gemv", "gemm", "linear", "gemv_silu_mul", "gemv_ex", "gemv_max_m",
-    "linear_noalloc", "noalloc_scratch_bytes",
+    "linear_noalloc", "noalloc_scratch_bytes", "stream_read",
     "status_str", "version", "QuantizedLinear",
 ]
 
@@ -52,6 +52,7 @@ _SIG = {
     "wq_awq_clip": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
 }
 _SIG["wq_gemv_silu_mul"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
+_SIG["wq_stream_read"] = (ctypes.c_int, [_VP, ctypes.c_size_t, _VP, _VP])
 _SIG["wq_linear_noalloc"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP])
 _SIG["wq_gemv_ex"] = (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, _VP])
 for _name in ("wq_gemv", "wq_gemm", "wq_linear"):
@@ -409,6 +410,17 @@ def gemm(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=No
 def linear(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
     """Batch-size dispatch between gemv and gemm."""
     return _matmul("wq_linear", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
+
+
+def stream_read(src, nbytes: int, sink):
+    """Measurement reference: read nbytes of src (a device tensor) with the
+    plain streaming-read kernel; sink is an int32 device tensor of >= 1 entry."""
+    torch = _torch()
+    src = _dev(src, src.dtype if src is not None else torch.uint8, "src")
+    sink = _dev(sink, torch.int32, "sink", 1)
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds src")
+    _check(lib().wq_stream_read(_ptr(src), int(nbytes), _ptr(sink), _stream(src.device)), "wq_stream_read")
 
 
 def noalloc_scratch_bytes() -> int:
