@@ -184,6 +184,32 @@ def test_gemv_ragged_shapes(M, N, K):
     check_y(run("gemv", x, L, 4, gs), O.linear_ref(x, ref["w_hat"]), f"gemv M={M} N={N} K={K}")
 
 
+# Batches of 2..16 rows run on the matrix-core decode kernel: every code
+# width and group form, K long enough that at M = 16 the activations are
+# staged in several K-slabs, and K below eight 256-channel steps (masked
+# steps on the idle wavefronts).
+SKINNY_CASES = [(2, 32, True, 40, 8192), (3, 128, False, 70, 8448), (8, -1, True, 33, 8192),
+                (4, 64, False, 100, 9216), (4, 128, False, 50, 11008), (4, 128, True, 20, 512),
+                (8, 128, False, 17, 1280)]
+
+
+@pytest.mark.parametrize("M", [2, 7, 16])
+@pytest.mark.parametrize("bits,gs,sym,N,K", SKINNY_CASES)
+def test_skinny_formats_and_slabs(M, bits, gs, sym, N, K):
+    seed = (109, bits, gs % 997, N, K, M)
+    w = I.weights(seed, N, K, 0.02)
+    ref = O.quantize_linear_layer(w, bits, gs, symmetric=sym)
+    L = gpu_layer(w, bits, gs, sym=sym)
+    x = I.activations(seed, M, K)
+    check_y(run("gemv", x, L, bits, gs), O.linear_ref(x, ref["w_hat"]), f"gemv b={bits} g={gs} M={M} K={K}")
+    # the fused AWQ input division is bit-identical to dividing first
+    _, s_h = O.awq_channel_scales(x, 0.5)
+    xd, sd = dev(x), dev(s_h)
+    y_a = wq.gemv(wq.scale_act(xd, sd), L["packed"], L["scales"], L["zeros"], bits, gs)
+    y_b = wq.gemv_ex(xd, L["packed"], L["scales"], L["zeros"], bits, gs, act_scale=sd)
+    assert np.array_equal(host(y_a).view(np.uint16), host(y_b).view(np.uint16))
+
+
 @pytest.mark.parametrize("M", [1, 16, 17, 33, 100, 130, 300])
 @pytest.mark.parametrize("N,K", [(1000, 512), (4104, 256), (72, 4128)])
 def test_gemm_ragged_shapes(M, N, K):

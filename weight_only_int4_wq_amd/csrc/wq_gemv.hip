@@ -926,13 +926,13 @@ extern "C" wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const
     if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;  // read 16 bytes at a time
     if (silu && N % 2) return WQ_ERR_ARG;
     if (act_scale && !wqh::aligned16(act_scale)) return WQ_ERR_ARG;
-    if (M > 4) return WQ_ERR_UNSUPPORTED;
+    const bool sl = silu != 0;
+    if (M > 16 || (sl && M > 4)) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool sl = silu != 0;
     if (!sl && M >= WQ_SKINNY_MIN_M) {  // the kernel wq_gemv uses for this M
         const wq_status st2 = wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, act_scale, bias);
-        if (st2 != WQ_ERR_UNSUPPORTED) return st2;
+        if (st2 != WQ_ERR_UNSUPPORTED || M > 4) return st2;
     }
     switch (bits) {
         case 2: return launch_ex<2>(x, packed, scales, zeros, perm, act_scale, bias, y, M, N, K, gs, sl, s);

@@ -7,7 +7,7 @@
 // weight pair and runs out of ALU long before memory.  Here the products go
 // to the matrix cores ("AutoAWQ vs The Stack v2", WQLinear_* paragraph: a
 // GEMM variant for batches, a GEMV variant for single tokens; this is the
-// bridge between the two) and the vector ALU only decodes and dequantizes.
+// bridge between the two) and the vector ALU only decodes the codes.
 //
 // One v_mfma_f32_16x16x32_f16 multiplies a 16 x 32 activation fragment by a
 // 32 x 16 weight fragment.  Lane l supplies activation row l % 16 (rows at
@@ -30,12 +30,18 @@
 // D items refill conditionally), so the compiler's wait counts stay exact;
 // the barriers wait for LDS only.
 //
-// The activations are staged once per block in LDS, each row padded by 16
-// bytes (conflict-free fragment reads), in the decoder's pair order (codes
-// i and i + 4 of an 8-code block share a pair), and every weight is
-// dequantized exactly as in wq_dequant: fp16((q - z) * s), one rounding,
-// then multiplied in the matrix cores with fp32 accumulation.
+// The activations are staged in LDS, each row padded by 16 bytes
+// (conflict-free fragment reads), in the decoder's pair order (codes i and
+// i + 4 of an 8-code block share a pair).  When M rows of K channels do not
+// fit, K is cut into slabs of KS channels (a multiple of 256): the block
+// streams all its tiles over one slab, adds the slab's sums into the output
+// buffer, stages the next slab and goes on (the weight loads stay in flight
+// across the switch).  A wavefront with no step of a slab (fewer than eight
+// steps) runs one masked step per tile so every wavefront meets every barrier.
+// The scales and zero-points of the block's rows and the slab's groups are
+// staged alongside.
 #include <algorithm>
+#include <type_traits>
 
 #include "wq_common.h"
 
@@ -46,6 +52,11 @@ using namespace wq;
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 
 constexpr int kSkinnyWaves = 8;
+
+// weight loads in flight per lane, in steps of two 16-byte chunks
+#ifndef WQ_SKINNY_D
+#define WQ_SKINNY_D 2
+#endif
 
 template <int BITS>
 __device__ __forceinline__ void load_chunk_nt(const uint32_t* p, uint32_t* w) {
@@ -92,16 +103,6 @@ __device__ __forceinline__ void decode_pairs(const uint32_t* w, uint32_t* h) {
     }
 }
 
-// Sum over the 16 lanes of a DPP row, valid in every lane of the row: quad
-// permutes, then half-row and row mirrors (fixed order).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-    return v;
-}
-
 // x' = fp16(fp32(x) / fp32(s)) for 8 activations, correctly rounded
 // division then one rounding (the AWQ input scaling of wq_scale_act).
 __device__ __forceinline__ u4 divide_block(u4 v, u4 t) {
@@ -119,111 +120,142 @@ __device__ __forceinline__ u4 divide_block(u4 v, u4 t) {
     return u4{o[0], o[1], o[2], o[3]};
 }
 
+// Slab geometry, the same in every block.
+struct SlabGeo {
+    int KS;    // channels per slab (multiple of 256); the last slab may be shorter
+    int GSL;   // scale entries per staged row (groups any slab touches, at most)
+};
+
 // EX: act_scale (nullable, fp16 [K]) divides the activations while they are
 // staged, bit-identical to wq_scale_act; bias (nullable, fp16 [N]) is added
 // to the fp32 sums before the output rounding.
-// FACT (group size a multiple of 128 and K a multiple of 256): the matrix
-// cores multiply the decoded codes B + q themselves, and each 128-channel
-// group's product C (one group for all four lane groups of an instruction:
-// they hold four consecutive chunks) is corrected once per lane,
-//     sum_k x_k (q_k - z) s = s (C - (1024 + z) Xe - (kOdd + z) Xo),
-// with Xe, Xo the sums of the group's activations over the pairs of base
-// 1024 and base kOdd, computed when x is staged.  Otherwise every weight is
-// dequantized, fp16((q - z) s), before the product.
-template <int BITS, int D, bool HAS_Z, bool EX, bool FACT>
+// ZSUB (group size a multiple of 128): the decoded pairs B + q have B + z
+// subtracted in fp16, which is exact (both are integers below 2048), so the
+// matrix cores multiply x by q - z itself; the four chunks of one
+// instruction group are 128 channels of one group, so its product is
+// scaled once per lane, in fp32, before it joins the accumulator:
+//     sum_k x_k (q_k - z) s = s * sum_k x_k (q_k - z).
+// Otherwise every weight is dequantized, fp16((q - z) s), before the product.
+// SLABS: K is cut into several slabs (without it the slab switch is compiled
+// out, which keeps the streaming loop's scalar state small).
+template <int BITS, int D, bool HAS_Z, bool EX, bool ZSUB, bool SLABS>
 __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_t* __restrict__ x,
                                                                  const uint32_t* __restrict__ packed,
                                                                  const uint16_t* __restrict__ scales,
                                                                  const uint8_t* __restrict__ zeros,
                                                                  uint16_t* __restrict__ y, int M, int N, int K,
-                                                                 GroupDiv gd, int tpb,
+                                                                 GroupDiv gd, int tpb, SlabGeo geo,
                                                                  const uint16_t* __restrict__ act_scale,
                                                                  const uint16_t* __restrict__ bias) {
     constexpr int WPB = kSkinnyWaves;
+    constexpr int NT = 64 * WPB;
     extern __shared__ u4 smem[];
     const int CN = K / 32;
     const int G = chunk_group(CN - 1, gd) + 1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int li = lane & 15, lg = lane >> 4;
+    const int KS = geo.KS, GSL = geo.GSL;
+    const int KSc = KS / 32;                   // chunks per slab
+    const int nslab = SLABS ? (CN + KSc - 1) / KSc : 1;
 
-    // LDS: x rows [M][K * 2 + 16 bytes], partials [2][WPB][64 lanes][4],
-    // outputs [tpb][M][16] (fp32), [FACT] group sums float2 [K / 128][16],
-    // the block's scales u16 [tpb * 16][G] and zero-points u8 [tpb * 16][G]
-    const int xrs = K * 2 + 16;
+    // LDS: x rows [M][KS * 2 + 16 bytes], partials [2][WPB][64 lanes][4],
+    // outputs [tpb][M][16] (fp32), the block's scales u16 [tpb * 16][GSL]
+    // and zero-points u8 [tpb * 16][GSL] of the current slab
+    const int xrs = KS * 2 + 16;
     char* lds = reinterpret_cast<char*>(smem);
     float* red = reinterpret_cast<float*>(lds + size_t(M) * xrs);
     float* outb = red + 2 * WPB * 256;
-    float2* xsum = reinterpret_cast<float2*>(outb + size_t(tpb) * M * 16);
-    uint16_t* ssc = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(xsum) + (FACT ? K : 0));
-    uint8_t* szr = reinterpret_cast<uint8_t*>(ssc + size_t(tpb) * 16 * G);
+    uint16_t* ssc = reinterpret_cast<uint16_t*>(outb + size_t(tpb) * M * 16);
+    uint8_t* szr = reinterpret_cast<uint8_t*>(ssc + size_t(tpb) * 16 * GSL);
 
     const int n_tiles = (N + 15) / 16;
     const int t0 = blockIdx.x * tpb;
     const int T = max(0, min(tpb, n_tiles - t0));
     const int RB = max(0, min(T * 16, N - t0 * 16));  // rows of this block
-    const int sc_n = RB * G;                          // their scale entries
-    const size_t sbase = size_t(t0) * 16 * G;
-    const int steps = (CN + 7) / 8;                                // 256-k steps per row
-    const int my = wave < steps ? (steps - wave + WPB - 1) / WPB : 0;  // steps per tile of this wavefront
-    const int items = T * my;
 
-    // ---- activations, first batch: up to XU 8-element blocks per thread
-    // are loaded before the weights (vector-memory loads complete in issue
-    // order, so staging them waits for these only); x is contiguous [M][K],
-    // block e is row e / K8, block e % K8
-    const int K8 = K / 8;
-    const int total = M * K8;
-    constexpr int NT = 64 * WPB;
-    constexpr int XU = 16;
-    const int nx = (total + NT - 1) / NT;  // blocks per thread
-    u4 xv[XU], xs_[XU];
+    // steps (256 channels) of slab s, and this wavefront's steps per tile
+    // there (at least one: a wavefront past the slab's steps runs one masked
+    // step)
+    auto slab_steps = [&](int s) { return (min(KSc, CN - s * KSc) + 7) / 8; };
+    auto my_of = [&](int s) { return max(1, (slab_steps(s) - wave + WPB - 1) / WPB); };
+    const int my_first = my_of(0);
+    const int items = T * ((nslab - 1) * my_first + my_of(nslab - 1));
+
+    // the slab's first group and its number of groups
+    auto slab_g0 = [&](int s) { return chunk_group(s * KSc, gd); };
+    auto slab_ng = [&](int s) { return chunk_group(min(CN, (s + 1) * KSc) - 1, gd) - slab_g0(s) + 1; };
+
+    // ---- first slab, first batch of activations and scales, loaded before
+    // the weights (vector-memory loads complete in issue order, so staging
+    // them waits for these only).  Thread t stages 8-element blocks
+    // j = t, t + NT, ... of every row; the first batch is j = t, rows below
+    // XU (fewer with the division, whose temporaries would spill)
+    constexpr int XU = EX ? 8 : 16;
+    const int KB0 = min(KS, K) / 8;  // real blocks per row in slab 0
+    u4 xv[XU], xs0 = {0u, 0u, 0u, 0u};
+    {
+        const int j = min(int(threadIdx.x), KB0 - 1);
 #pragma unroll
-    for (int u = 0; u < XU; ++u) {
-        if (u < nx) {
-            const int e = min(int(threadIdx.x) + NT * u, total - 1);
-            xv[u] = *reinterpret_cast<const u4*>(x + size_t(e) * 8);
-            if constexpr (EX) {
-                if (act_scale) xs_[u] = *reinterpret_cast<const u4*>(act_scale + size_t(e % K8) * 8);
-            }
+        for (int u = 0; u < XU; ++u)
+            if (u < M) xv[u] = *reinterpret_cast<const u4*>(x + size_t(u) * K + 8 * j);
+        if constexpr (EX) {
+            if (act_scale) xs0 = *reinterpret_cast<const u4*>(act_scale + 8 * j);
         }
     }
-
-    // ---- the block's scales and zero-points (contiguous: its rows are
-    // consecutive), coalesced, also before the weights: a per-lane load of
-    // its row's scale at every step would touch 16 rows' lines per
-    // instruction, which costs more than the weight loads themselves
+    // scale entries of the block's rows and a slab's groups: entry e is row
+    // e / ng, group g0 + e % ng (the division by the float reciprocal is
+    // exact while e < 2^21: (e + 0.5) / ng stays at least 0.5 / ng away from
+    // an integer, farther than the rounding error)
+    auto sc_index = [&](int e, int ng, float inv, int g0) {
+        const int r = int((float(e) + 0.5f) * inv);
+        return size_t(min(t0 * 16 + r, N - 1)) * G + g0 + (e - r * ng);
+    };
     constexpr int SU = 8;
-    const int ns = (sc_n + NT - 1) / NT;
     uint32_t sv[SU], zv[SU];
+    const int ng0 = slab_ng(0);
+    const float inv0 = 1.0f / float(ng0);
+    const int sc_n0 = RB * ng0;
+    {
+        const int g0 = slab_g0(0);
 #pragma unroll
-    for (int u = 0; u < SU; ++u) {
-        if (u < ns) {
-            const int e = min(int(threadIdx.x) + NT * u, sc_n - 1);
-            sv[u] = scales[sbase + e];
-            if constexpr (HAS_Z) zv[u] = zeros[sbase + e];
+        for (int u = 0; u < SU; ++u) {
+            const size_t gi = sc_index(min(int(threadIdx.x) + NT * u, max(sc_n0 - 1, 0)), ng0, inv0, g0);
+            sv[u] = scales[gi];
+            if constexpr (HAS_Z) zv[u] = zeros[gi];
         }
     }
 
-    // ---- weights: issue cursor (tile ordinal it, step ordinal ij); loads
-    // are unconditional and the cursor stops at the last item
+    // ---- weights: issue cursor (slab is, tile ordinal it, step ordinal
+    // ij); loads are unconditional and the cursor stops at the last item
     uint32_t wr[D][2][BITS];
-    int it = 0, ij = 0, ii = 0;
+    // (the lane's row pointer and the step's first chunk are kept up to
+    // date incrementally: the per-item work is two adds)
+    int is = 0, it = 0, ij = 0, ii = 0, imy = my_first;
+    int icb = 8 * wave;  // global chunk of the step's first 32-code chunk
+    auto row_ptr = [&](int t) {
+        const int n = min((t0 + min(t, max(T - 1, 0))) * 16 + li, N - 1);
+        return reinterpret_cast<const char*>(packed) + size_t(n) * CN * BITS * 4;
+    };
+    const char* irow = row_ptr(0);
     auto issue = [&](int d) {
-        const int tile = t0 + min(it, max(T - 1, 0));
-        const int n = min(tile * 16 + li, N - 1);
-        const int s = wave + WPB * ij;
-        const char* rowp = reinterpret_cast<const char*>(packed) + size_t(n) * CN * BITS * 4;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int c = min(8 * s + 4 * p + lg, CN - 1);
-            load_chunk_nt<BITS>(reinterpret_cast<const uint32_t*>(rowp + uint32_t(c) * uint32_t(BITS * 4)), wr[d][p]);
+            const int c = min(icb + 4 * p + lg, CN - 1);
+            load_chunk_nt<BITS>(reinterpret_cast<const uint32_t*>(irow + uint32_t(c) * uint32_t(BITS * 4)), wr[d][p]);
         }
         if (ii + 1 < items) {
             ++ii;
-            if (++ij == my) {
+            icb += 8 * WPB;
+            if (++ij == imy) {
                 ij = 0;
-                ++it;
+                if (++it == T) {
+                    it = 0;
+                    ++is;
+                    imy = my_of(is);
+                }
+                icb = is * KSc + 8 * wave;
+                irow = row_ptr(it);
             }
         }
     };
@@ -231,64 +263,67 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     for (int d = 0; d < D; ++d) issue(d);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- scales and zero-points to LDS
-#pragma unroll
-    for (int u = 0; u < SU; ++u) {
-        const int e = int(threadIdx.x) + NT * u;
-        if (u < ns && e < sc_n) {
-            ssc[e] = uint16_t(sv[u]);
-            if constexpr (HAS_Z) szr[e] = uint8_t(zv[u]);
+    // ---- staging of slab s: activations (zero past K), scales, zero-points
+    auto put_x = [&](int m, int j, u4 v, u4 t) {
+        if constexpr (EX) {
+            if (act_scale) v = divide_block(v, t);
         }
-    }
-    for (int e = int(threadIdx.x) + NT * SU; e < sc_n; e += NT) {
-        ssc[e] = scales[sbase + e];
-        if constexpr (HAS_Z) szr[e] = zeros[sbase + e];
-    }
-
-    // ---- stage the activations: row m, 8-element block j at byte
-    // m * xrs + 16 j, in pair order
-    {
-        // e runs over consecutive blocks in consecutive lanes and K8 is a
-        // multiple of 16, so the 16 blocks of a 128-channel group sit in one
-        // 16-lane row of a wavefront: their sums reduce by DPP (fixed order)
-        auto put = [&](int e, u4 v, u4 t) {
+        *reinterpret_cast<u4*>(lds + size_t(m) * xrs + 16 * j) = stage_block(v);
+    };
+    auto put_zero = [&](int m, int j) {
+        *reinterpret_cast<u4*>(lds + size_t(m) * xrs + 16 * j) = u4{0u, 0u, 0u, 0u};
+    };
+    auto put_sc = [&](int e, uint32_t s, uint32_t z) {
+        ssc[e] = uint16_t(s);
+        if constexpr (HAS_Z) szr[e] = uint8_t(z);
+    };
+    auto stage_rest = [&](int s, int jfirst, int mfirst) {
+        // blocks j >= jfirst of slab s (rows from mfirst in the first one);
+        // zeros past the end of K
+        const int kb = s * KS;
+        const int KBr = min(KS, K - kb) / 8;
+        for (int j = jfirst, m0 = mfirst; j < KS / 8; j += NT, m0 = 0) {
+            if (j >= KBr) {
+                for (int m = m0; m < M; ++m) put_zero(m, j);
+                continue;
+            }
+            u4 t = {0u, 0u, 0u, 0u};
             if constexpr (EX) {
-                if (act_scale) v = divide_block(v, t);
+                if (act_scale) t = *reinterpret_cast<const u4*>(act_scale + kb + 8 * j);
             }
-            const int m = e / K8;
-            const int j = e - m * K8;
-            const u4 o = stage_block(v);
-            *reinterpret_cast<u4*>(lds + size_t(m) * xrs + 16 * j) = o;
-            if constexpr (FACT) {
-                const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-                float se = __builtin_amdgcn_fdot2(as_h2(o.x), one, 0.f, false);
-                se = __builtin_amdgcn_fdot2(as_h2(o.z), one, se, false);
-                float so = __builtin_amdgcn_fdot2(as_h2(o.y), one, 0.f, false);
-                so = __builtin_amdgcn_fdot2(as_h2(o.w), one, so, false);
-                se = row16_sum(se);
-                so = row16_sum(so);
-                if ((lane & 15) == 0) xsum[(j >> 4) * 16 + m] = make_float2(se, so);
-            }
-        };
+            for (int mb = m0; mb < M; mb += XU) {
+                u4 v[XU];
 #pragma unroll
-        for (int u = 0; u < XU; ++u) {
-            const int e = int(threadIdx.x) + NT * u;
-            if (e < total) put(e, xv[u], xs_[u]);
+                for (int u = 0; u < XU; ++u)
+                    if (mb + u < M) v[u] = *reinterpret_cast<const u4*>(x + size_t(mb + u) * K + kb + 8 * j);
+#pragma unroll
+                for (int u = 0; u < XU; ++u)
+                    if (mb + u < M) put_x(mb + u, j, v[u], t);
+            }
         }
-        // the rest (large M * K), batch by batch
-        for (int e0 = int(threadIdx.x) + NT * XU; e0 < total; e0 += NT * XU) {
-#pragma unroll
-            for (int u = 0; u < XU; ++u) {
-                const int e = min(e0 + NT * u, total - 1);
-                xv[u] = *reinterpret_cast<const u4*>(x + size_t(e) * 8);
-                if constexpr (EX) {
-                    if (act_scale) xs_[u] = *reinterpret_cast<const u4*>(act_scale + size_t(e % K8) * 8);
-                }
-            }
+    };
+    auto stage_scales = [&](int s, int efirst) {
+        const int ng = slab_ng(s), g0 = slab_g0(s);
+        const float inv = 1.0f / float(ng);
+        for (int e = efirst; e < RB * ng; e += NT) {
+            const size_t gi = sc_index(e, ng, inv, g0);
+            put_sc(e, scales[gi], HAS_Z ? uint32_t(zeros[gi]) : 0u);
+        }
+    };
+    {
+        const int j = int(threadIdx.x);
+        if (j < KB0) {
 #pragma unroll
             for (int u = 0; u < XU; ++u)
-                if (e0 + NT * u < total) put(e0 + NT * u, xv[u], xs_[u]);
+                if (u < M) put_x(u, j, xv[u], xs0);
         }
+        stage_rest(0, j, j < KB0 ? XU : 0);
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int e = int(threadIdx.x) + NT * u;
+            if (e < sc_n0) put_sc(e, sv[u], HAS_Z ? zv[u] : 0u);
+        }
+        stage_scales(0, int(threadIdx.x) + NT * SU);
     }
     __syncthreads();
 
@@ -297,98 +332,109 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     // of matrix instructions
     f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
     const char* xrow = lds + size_t(min(li, M - 1)) * xrs;
-    int cj = 0, ct = 0;  // compute cursor: step ordinal in the tile, tile ordinal
-    auto tile_end = [&](int tord, f4 v) {
-        float* mine = red + ((tord & 1) * WPB + wave) * 256 + lane * 4;
+    int cs = 0, ct = 0, cj = 0, cmy = my_first, te = 0;  // compute cursor, tile ends so far
+    int css8 = 8 * slab_steps(0), cg0 = slab_g0(0), cng = ng0;
+    int ccb = 8 * wave;                                   // the step's first chunk within the slab
+    int srow = min(li, RB - 1) * cng;                     // this lane's row in ssc / szr
+    auto tile_end = [&](f4 v) {
+        float* mine = red + ((te & 1) * WPB + wave) * 256 + lane * 4;
         *reinterpret_cast<f4*>(mine) = v;
         // workgroup barrier: its fences wait for LDS only (weight loads in
         // flight stay in flight), and the compiler keeps its own count of
-        // those loads across it (a hand-written wait here made it drop a
-        // later wait on a refilled slot)
+        // those loads across it
         __syncthreads();
-        // output (m, n): lane 16 (m / 4) + n, element m % 4 of each partial
-        for (int o = threadIdx.x; o < M * 16; o += 64 * WPB) {
+        // output (m, n): lane 16 (m / 4) + n, element m % 4 of each partial;
+        // thread o always owns the same outputs, so the slabs add up without
+        // further synchronization
+        for (int o = threadIdx.x; o < M * 16; o += NT) {
             const int m = o >> 4, nn = o & 15;
-            const float* src = red + (tord & 1) * WPB * 256 + (16 * (m >> 2) + nn) * 4 + (m & 3);
+            const float* src = red + (te & 1) * WPB * 256 + (16 * (m >> 2) + nn) * 4 + (m & 3);
             float sum = 0.f;
 #pragma unroll
             for (int w = 0; w < WPB; ++w) sum += src[w * 256];
-            outb[(tord * M + m) * 16 + nn] = sum;
+            float* dst = outb + (ct * M + m) * 16 + nn;
+            *dst = cs == 0 ? sum : *dst + sum;
+        }
+        ++te;
+    };
+    // One item: the step of slab cs, tile ct, step ordinal cj, from slot d.
+    auto compute = [&](int d) {
+        const bool live = ccb < css8;  // else a masked step
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int cl = min(ccb + 4 * p + lg, KSc - 1);  // chunk within the slab
+            // ZSUB: the four chunks of the instruction group share the group
+            const int sg = srow - cg0 +
+                           (ZSUB ? chunk_group(min(cs * KSc + ccb + 4 * p, CN - 1), gd)
+                                 : chunk_group(min(cs * KSc + cl, CN - 1), gd));
+            // read unconditionally, then mask (a read under the condition
+            // would wait for the LDS at once)
+            const uint32_t sr_ = uint32_t(ssc[sg]) & (live ? 0xFFFFu : 0u);
+            const uint32_t z = HAS_Z ? uint32_t(szr[sg]) : (1u << (BITS - 1));
+            const uint32_t ze = (0x6400u | z) * 0x10001u;
+            const uint32_t zo = BITS == 4 ? (0x5400u + (z << 4)) * 0x10001u : ze;
+            uint32_t h[16];
+            decode_pairs<BITS>(wr[d][p], h);
+            f4& a = p == 0 ? acc : acc2;
+            if constexpr (ZSUB) {
+                f4 cp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u4 bv;
+                    bv.x = as_u32(as_h2(h[4 * q + 0]) - as_h2(ze));
+                    bv.y = as_u32(as_h2(h[4 * q + 1]) - as_h2(zo));
+                    bv.z = as_u32(as_h2(h[4 * q + 2]) - as_h2(ze));
+                    bv.w = as_u32(as_h2(h[4 * q + 3]) - as_h2(zo));
+                    const h8v av = *reinterpret_cast<const h8v*>(xrow + 64 * cl + 16 * q);
+                    cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), cp, 0, 0, 0);
+                }
+                const float sf = float(__builtin_bit_cast(_Float16, uint16_t(sr_)));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(sf, cp[r], a[r]);
+            } else {
+                const uint32_t ss = scale_pair(uint16_t(sr_));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    u4 bv;
+                    bv.x = as_u32((as_h2(h[4 * q + 0]) - as_h2(ze)) * as_h2(ss));
+                    bv.y = as_u32((as_h2(h[4 * q + 1]) - as_h2(zo)) * as_h2(ss));
+                    bv.z = as_u32((as_h2(h[4 * q + 2]) - as_h2(ze)) * as_h2(ss));
+                    bv.w = as_u32((as_h2(h[4 * q + 3]) - as_h2(zo)) * as_h2(ss));
+                    // x fragment: row li, k = 32 cl + 8 q (the lane group's chunk)
+                    const h8v av = *reinterpret_cast<const h8v*>(xrow + 64 * cl + 16 * q);
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), a, 0, 0, 0);
+                }
+            }
         }
     };
-    // One item: the step of slot d (its loads arrived with the D ahead).
-    auto compute = [&](int d) {
-                    const int s = wave + WPB * cj;
-                    const int srow = min(ct * 16 + li, RB - 1) * G;  // this lane's row in ssc / szr
-#pragma unroll
-                    for (int p = 0; p < 2; ++p) {
-                        const int c = 8 * s + 4 * p + lg;
-                        const int sg = srow + chunk_group(min(c, CN - 1), gd);
-                        const uint32_t sr_ = ssc[sg];
-                        const uint32_t zr_ = HAS_Z ? uint32_t(szr[sg]) : (1u << (BITS - 1));
-                        uint32_t h[16];
-                        decode_pairs<BITS>(wr[d][p], h);
-                        if constexpr (FACT) {
-                            f4 cp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const u4 bv = {h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]};
-                                const h8v av = *reinterpret_cast<const h8v*>(xrow + 64 * c + 16 * q);
-                                cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), cp, 0, 0,
-                                                                           0);
-                            }
-                            // correction of the group's product: rows 4 lg + r
-                            const float4* xg = reinterpret_cast<const float4*>(xsum + ((8 * s + 4 * p) >> 2) * 16 + 4 * lg);
-                            const float4 x01 = xg[0], x23 = xg[1];
-                            const float zf = float(zr_);
-                            const float ce = -(1024.f + zf), co = -(float(kOdd<BITS>) + zf);
-                            const float sf = float(__builtin_bit_cast(_Float16, uint16_t(sr_)));
-                            f4& a = p == 0 ? acc : acc2;
-                            a[0] = __builtin_fmaf(sf, __builtin_fmaf(co, x01.y, __builtin_fmaf(ce, x01.x, cp[0])), a[0]);
-                            a[1] = __builtin_fmaf(sf, __builtin_fmaf(co, x01.w, __builtin_fmaf(ce, x01.z, cp[1])), a[1]);
-                            a[2] = __builtin_fmaf(sf, __builtin_fmaf(co, x23.y, __builtin_fmaf(ce, x23.x, cp[2])), a[2]);
-                            a[3] = __builtin_fmaf(sf, __builtin_fmaf(co, x23.w, __builtin_fmaf(ce, x23.z, cp[3])), a[3]);
-                            continue;
-                        }
-                        const bool kval = c < CN;
-                        const uint32_t z = zr_;
-                        const uint32_t ze = (0x6400u | z) * 0x10001u;
-                        const uint32_t zo = BITS == 4 ? (0x5400u + (z << 4)) * 0x10001u : ze;
-                        const uint32_t ss = kval ? scale_pair(uint16_t(sr_)) : 0u;
-                        const int cc = min(c, CN - 1);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            uint32_t f[4];
-                            f[0] = as_u32((as_h2(h[4 * q + 0]) - as_h2(ze)) * as_h2(ss));
-                            f[1] = as_u32((as_h2(h[4 * q + 1]) - as_h2(zo)) * as_h2(ss));
-                            f[2] = as_u32((as_h2(h[4 * q + 2]) - as_h2(ze)) * as_h2(ss));
-                            f[3] = as_u32((as_h2(h[4 * q + 3]) - as_h2(zo)) * as_h2(ss));
-                            const u4 bv = {f[0], f[1], f[2], f[3]};
-                            // x fragment: row li, k = 32 cc' + 8 q where the
-                            // lane group's chunk is cc' = c
-                            const h8v av = *reinterpret_cast<const h8v*>(xrow + 64 * cc + 16 * q);
-                            if (p == 0)
-                                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), acc, 0,
-                                                                            0, 0);
-                            else
-                                acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), acc2,
-                                                                             0, 0, 0);
-                        }
-                    }
-                    };
-    // after an item (and its slot's refill): the tile's last step ends it
+    // after an item: the tile's last step ends the tile, the slab's last
+    // tile stages the next slab (every wavefront has left the slab's
+    // activations by the tile end's barrier)
     auto advance = [&]() {
-        if (++cj == my) {
-            tile_end(ct, acc + acc2);
+        ccb += 8 * WPB;
+        if (++cj == cmy) {
+            tile_end(acc + acc2);
             acc = f4{0.f, 0.f, 0.f, 0.f};
             acc2 = f4{0.f, 0.f, 0.f, 0.f};
             cj = 0;
-            ++ct;
+            ccb = 8 * wave;
+            if (++ct == T) {
+                ct = 0;
+                if (SLABS && cs + 1 < nslab) {
+                    ++cs;
+                    stage_rest(cs, int(threadIdx.x), 0);
+                    stage_scales(cs, int(threadIdx.x));
+                    __syncthreads();
+                    cmy = my_of(cs);
+                    css8 = 8 * slab_steps(cs);
+                    cg0 = slab_g0(cs);
+                    cng = slab_ng(cs);
+                }
+            }
+            srow = min(ct * 16 + li, RB - 1) * cng;
         }
     };
-    if (my == 0) {
-        for (int t = 0; t < T; ++t) tile_end(t, acc);
-    } else {
+    {
         // full rounds: every refill loads a real item, unconditionally
         int q0 = 0;
         for (; q0 + 2 * D <= items; q0 += D) {
@@ -418,7 +464,7 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     }
     // ---- outputs
     __syncthreads();
-    for (int o = threadIdx.x; o < T * M * 16; o += 64 * WPB) {
+    for (int o = threadIdx.x; o < T * M * 16; o += NT) {
         const int tord = o / (M * 16), r = o - tord * M * 16;
         const int m = r >> 4, n = (t0 + tord) * 16 + (r & 15);
         if (n < N) {
@@ -435,15 +481,15 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
 
 namespace wqh {
 
-// LDS bytes of the skinny kernel for M rows, K channels and tpb tiles per block.
-static size_t skinny_lds(int M, int K, int G, int tpb, bool fact) {
-    return size_t(M) * (size_t(K) * 2 + 16) + 2 * kSkinnyWaves * 256 * 4 + size_t(tpb) * M * 16 * 4 +
-           (fact ? size_t(K) : 0) + size_t(tpb) * 16 * G * 3;
+// LDS bytes of the skinny kernel for M rows, slabs of KS channels, tpb
+// tiles per block and GSL scale entries per row.
+static size_t skinny_lds(int M, int KS, int tpb, int GSL) {
+    return size_t(M) * (size_t(KS) * 2 + 16) + 2 * kSkinnyWaves * 256 * 4 + size_t(tpb) * M * 16 * 4 +
+           size_t(tpb) * 16 * GSL * 3;
 }
 
 // Launch the skinny kernel; WQ_ERR_UNSUPPORTED when it does not apply
-// (act-order, M outside 1..16, K below 256, or activations beyond the LDS
-// limit).
+// (act-order, M outside 1..16, K below 256).
 wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       const int32_t* perm, uint16_t* y, int M, int N, int K, int bits, int gs, hipStream_t s,
                       const uint16_t* act_scale, const uint16_t* bias) {
@@ -458,34 +504,55 @@ wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t*
     const int n_tiles = (N + 15) / 16;
     const int blocks = std::min(n_tiles, cus);
     const int tpb = (n_tiles + blocks - 1) / blocks;
-    const bool fact = gs % 128 == 0 && K % 256 == 0;
-    const size_t lds = skinny_lds(M, K, K / gs, tpb, fact);
-    if (lds > size_t(lds_max)) return WQ_ERR_UNSUPPORTED;
+    // fewest slabs that fit: KS a multiple of 256, groups per slab at most
+    // KS / gs + 1 (+ 1 for a group cut by the slab's start)
+    const int Kp = (K + 255) / 256 * 256;
+    const int G = (K + gs - 1) / gs;
+    SlabGeo geo{0, 0};
+    for (int nslab = 1; nslab <= Kp / 256; ++nslab) {
+        const int KS = ((Kp / 256 + nslab - 1) / nslab) * 256;
+        const int GSL = nslab == 1 ? G : std::min(G, KS / gs + 2);
+        if (skinny_lds(M, KS, tpb, GSL) <= size_t(lds_max)) {
+            geo = SlabGeo{KS, GSL};
+            break;
+        }
+    }
+    if (geo.KS == 0) return WQ_ERR_UNSUPPORTED;
+    const size_t lds = skinny_lds(M, geo.KS, tpb, geo.GSL);
     const GroupDiv gd = group_magic(gs);
-    constexpr int D = 2;
+    const bool zsub = gs % 128 == 0;
+    const bool slabs = geo.KS < K;
+    constexpr int D = WQ_SKINNY_D;
     auto go = [&](auto kern) {
         if (lds > 64 * 1024)
             (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                       int(lds));
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kSkinnyWaves), lds, s, x, packed, scales, zeros, y, M, N, K,
-                           gd, tpb, act_scale, bias);
+                           gd, tpb, geo, act_scale, bias);
         return launch_status();
     };
     const bool ex = act_scale || bias;
-#define WQ_SKINNY_GO2(B, F)                                                                                 \
-    return ex ? (zeros ? go(skinny_kernel<B, D, true, true, F>) : go(skinny_kernel<B, D, false, true, F>)) \
-              : (zeros ? go(skinny_kernel<B, D, true, false, F>) : go(skinny_kernel<B, D, false, false, F>))
-#define WQ_SKINNY_GO(B)          \
-    if (fact) WQ_SKINNY_GO2(B, true); \
-    WQ_SKINNY_GO2(B, false)
+    // pick the instantiation: bits, zero-points, fused epilogue, ZSUB, slabs
+    auto pick = [&](auto bits_c) -> wq_status {
+        constexpr int B = decltype(bits_c)::value;
+        auto by_slab = [&](auto z_c, auto ex_c, auto zs_c) -> wq_status {
+            constexpr bool Z = decltype(z_c)::value, E = decltype(ex_c)::value, F = decltype(zs_c)::value;
+            return slabs ? go(skinny_kernel<B, D, Z, E, F, true>) : go(skinny_kernel<B, D, Z, E, F, false>);
+        };
+        auto by_zsub = [&](auto z_c, auto ex_c) -> wq_status {
+            return zsub ? by_slab(z_c, ex_c, std::true_type{}) : by_slab(z_c, ex_c, std::false_type{});
+        };
+        auto by_ex = [&](auto z_c) -> wq_status {
+            return ex ? by_zsub(z_c, std::true_type{}) : by_zsub(z_c, std::false_type{});
+        };
+        return zeros ? by_ex(std::true_type{}) : by_ex(std::false_type{});
+    };
     switch (bits) {
-        case 2: WQ_SKINNY_GO(2);
-        case 3: WQ_SKINNY_GO(3);
-        case 4: WQ_SKINNY_GO(4);
-        default: WQ_SKINNY_GO(8);
+        case 2: return pick(std::integral_constant<int, 2>{});
+        case 3: return pick(std::integral_constant<int, 3>{});
+        case 4: return pick(std::integral_constant<int, 4>{});
+        default: return pick(std::integral_constant<int, 8>{});
     }
-#undef WQ_SKINNY_GO
-#undef WQ_SKINNY_GO2
 }
 
 }  // namespace wqh
