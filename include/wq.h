@@ -252,8 +252,8 @@ size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t 
  * wq_gemm: the prefill kernel for any M: dequantizes weight tiles to
  *   fp16 and feeds fp16 matrix-core (MFMA) instructions with fp32
  *   accumulators.
- * wq_linear: picks wq_gemv for M <= wq_gemv_max_m() and wq_gemm otherwise
- *   (the batch-size dispatch).
+ * wq_linear: picks wq_gemv for M <= wq_gemv_max_m() (16; with act-order,
+ *   M <= 4) and wq_gemm otherwise (the batch-size dispatch).
  *
  * workspace: device memory of wq_workspace_size(M, N, K, bits, perm != NULL)
  * bytes (16-byte aligned), or NULL when that size is 0; WQ_ERR_ARG if
@@ -342,7 +342,8 @@ wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* 
  * pointers or a size that is not a multiple of 16; asynchronous. */
 wq_status wq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
-/* Largest M that wq_linear sends to wq_gemv. */
+/* Largest M that wq_linear sends to wq_gemv (16; layers with act-order go
+ * to wq_gemm from M = 5). */
 int32_t wq_gemv_max_m(void);
 
 #ifdef __cplusplus

@@ -381,7 +381,9 @@ def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, o
     N = packed.shape[0]
     y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
         _dev(out, torch.float16, "out", 2, shape=(M, N), device=x.device)
-    uses_gemm = entry == "wq_gemm" or (entry == "wq_linear" and M > gemv_max_m())
+    # wq_linear may send act-order layers to the GEMM below gemv_max_m(); the
+    # gather workspace is then allocated either way (unused by the GEMV)
+    uses_gemm = entry == "wq_gemm" or (entry == "wq_linear" and (M > gemv_max_m() or perm is not None))
     need = workspace_size(M, N, K, bits, perm is not None) if uses_gemm else 0
     ws_bytes = 0
     if need:

@@ -6,14 +6,21 @@
 #include "wq_common.h"
 
 namespace {
-// Largest activation row count sent to the GEMV kernel by wq_linear.  The
-// GEMV's dot products cost M fp16-pair instructions per weight pair, the
-// matrix-core GEMM's dequantization a fixed few: measured on the decode and
-// 70B layer shapes, the GEMV is faster up to M = 4 and the GEMM from M = 8.
-constexpr int kGemvMaxM = 4;
+// Largest activation row count sent to wq_gemv by wq_linear.  From M = 2 the
+// decode path runs on the skinny matrix-core kernel, which streams the
+// weights once for up to 16 rows.  Measured at M = 16 (MI355X, 4-bit, group
+// 128): 6.3-17.5 us on the Llama-7B decode projections against 11.2-26.1 us
+// for the tiled GEMM, 20.8-54.1 us against 28.0-64.6 us on the Llama-70B
+// ones; at M = 4 the gap is wider.  Act-order layers take the skinny kernel's
+// vector-ALU fallback, whose cost grows with M, so from M = 5 they go to the
+// GEMM, whose activation copy applies the gather.
+constexpr int kGemvMaxM = 16;
+constexpr int kGemvMaxMActOrder = 4;
 }  // namespace
 
 namespace wqh {
+
+bool linear_uses_gemv(int M, bool act_order) { return M <= (act_order ? kGemvMaxMActOrder : kGemvMaxM); }
 
 wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* y,
                             int M, int N, int K, int bits, int group_size, int* gs_out) {
@@ -52,7 +59,7 @@ extern "C" wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const 
                                const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
                                int32_t K, int32_t bits, int32_t group_size, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    if (M <= kGemvMaxM)
+    if (wqh::linear_uses_gemv(M, perm != nullptr))
         return wq_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, workspace, workspace_bytes,
                        stream);
     return wq_gemm(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream);

@@ -45,10 +45,14 @@ size_t gather_need(int32_t M, int32_t K, const int32_t* perm) {
 
 }  // namespace
 
+namespace wqh {
+bool linear_uses_gemv(int M, bool act_order);
+}
+
 extern "C" wq_status wq_linear_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                                        const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
                                        int32_t K, int32_t bits, int32_t group_size, void* stream) {
-    if (M <= wq_gemv_max_m())  // the decode kernel uses no scratch
+    if (wqh::linear_uses_gemv(M, perm != nullptr))  // the decode kernels use no scratch
         return wq_linear(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, nullptr, 0, stream);
     if (M > 0 && K > 0 && gather_need(M, K, perm) > kScratchBytes) return WQ_ERR_TOO_LARGE;
     int dev = 0;
