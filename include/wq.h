@@ -100,7 +100,10 @@ wq_status wq_awq_scales(const uint16_t* x, int32_t M, int32_t K, double alpha,
                         uint16_t* s_out, void* stream);
 
 /* AWQ fold: w_out[n][k] = fp16(fp32(w[n][k]) * fp32(s[k])) - input channel
- * k of the weights multiplied by s_k.  w_out may equal w (in place). */
+ * k of the weights multiplied by s_k (the weight side of AWQ's equivalent
+ * rescaling, "GPTQ, AWQ and the rules of post-training quantization",
+ * section "AWQ: find the one percent that matters").  w_out may equal w (in
+ * place).  Asynchronous; WQ_ERR_ARG for null or misaligned pointers. */
 wq_status wq_awq_fold(const uint16_t* w, const uint16_t* s, int32_t N, int32_t K,
                       uint16_t* w_out, void* stream);
 
@@ -193,7 +196,9 @@ wq_status wq_gptq_quantize(const uint16_t* x, const uint16_t* w, int32_t M, int3
 /* Bytes of device workspace wq_gptq_quantize needs (0 for invalid sizes). */
 size_t wq_gptq_workspace_size(int32_t M, int32_t N, int32_t K);
 
-/* Act-order packing order: perm = stable sort of k by g_idx[k].  Checks that
+/* Act-order packing order (desc_act: groups formed in a permuted channel
+ * order, "AutoGPTQ vs The Stack v2", first capability paragraph):
+ * perm = stable sort of k by g_idx[k].  Checks that
  * every g_idx lies in [0, K/group_size) and every group holds exactly
  * group_size channels; returns WQ_ERR_ARG otherwise.  This call SYNCHRONIZES
  * `stream`: it copies g_idx and the computed perm back to the host to check
@@ -202,7 +207,10 @@ wq_status wq_act_order_perm(const int32_t* g_idx, int32_t K, int32_t group_size,
                             int32_t* perm, void* stream);
 
 /* Pack codes uint8 [N][K] (original channel order, each < 2^bits; higher bits
- * are ignored) into packed uint32 [N][K*bits/32].  With g_idx (nullable) the
+ * are ignored) into packed uint32 [N][K*bits/32] (weights stay packed in
+ * memory at 2/3/4/8 bits: "AutoGPTQ vs The Stack v2", first capability
+ * paragraph; "AutoAWQ vs The Stack v2", WQLinear_* paragraph).  With g_idx
+ * (nullable) the
  * packing order is first computed into perm (int32 [K], caller-allocated,
  * required when g_idx is given) as by wq_act_order_perm, and this call then
  * synchronizes `stream`; without g_idx, perm is ignored and the call is
@@ -211,14 +219,21 @@ wq_status wq_pack(const uint8_t* codes, const int32_t* g_idx, int32_t K, int32_t
                   int32_t bits, int32_t group_size, uint32_t* packed, int32_t* perm,
                   void* stream);
 
-/* Inverse of wq_pack: codes uint8 [N][K] in original channel order. */
+/* Inverse of wq_pack: codes uint8 [N][K] in original channel order (the
+ * unpack step of the on-the-fly dequantization, "AutoAWQ vs The Stack v2",
+ * WQLinear_* paragraph).  perm: as returned by wq_pack (NULL without
+ * act-order).  Asynchronous; WQ_ERR_ARG for null or misaligned pointers or
+ * bad sizes, WQ_ERR_UNSUPPORTED for other bit widths. */
 wq_status wq_unpack(const uint32_t* packed, const int32_t* perm, int32_t K, int32_t N,
                     int32_t bits, uint8_t* codes, void* stream);
 
 /* Materialize the dequantized weights w fp16 [N][K] (original channel
  * order): w[n][perm[k']] = fp16((q - z) * s), q the code at packed column k',
- * with one round-to-nearest-even.  Same dequantization arithmetic as the
- * GEMV/GEMM kernels; used to check it bit for bit. */
+ * with one round-to-nearest-even (the group-wise affine dequantization of
+ * "GPTQ, AWQ and the rules of post-training quantization", section "The
+ * problem both methods solve").  Same dequantization arithmetic as the
+ * GEMV/GEMM kernels; used to check it bit for bit.  Asynchronous;
+ * WQ_ERR_ARG / WQ_ERR_UNSUPPORTED as wq_unpack. */
 wq_status wq_dequant(const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                      const int32_t* perm, int32_t K, int32_t N, int32_t bits,
                      int32_t group_size, uint16_t* w, void* stream);
@@ -226,7 +241,11 @@ wq_status wq_dequant(const uint32_t* packed, const uint16_t* scales, const uint8
 /* ------------------------------------------------------------- hot path --
  * AWQ input scaling: x_out[m][k] = fp16(fp32(x[m][k]) / fp32(s[k])), IEEE
  * fp32 division then one round-to-nearest-even (the activation side of the
- * AWQ rescaling).  x_out may equal x. */
+ * AWQ rescaling: the weights' input channel k is multiplied by s_k, the
+ * matching activation divided by it, "GPTQ, AWQ and the rules of
+ * post-training quantization", section "AWQ: find the one percent that
+ * matters").  x, s, x_out fp16, 16-byte aligned; x_out may equal x.
+ * Asynchronous; WQ_ERR_ARG for null or misaligned pointers or bad sizes. */
 wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t K,
                        uint16_t* x_out, void* stream);
 
@@ -243,12 +262,19 @@ wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t 
 size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t has_perm);
 
 /* y fp16 [M][N] = x fp16 [M][K] . dequant(packed)^T with fp32 accumulation
- * and one rounding of the sum to fp16.
+ * and one rounding of the sum to fp16: the weight-only quantized linear
+ * layer, weights kept packed and dequantized on the fly, a GEMV kernel for
+ * single-token decode and a GEMM kernel for batches chosen by batch size
+ * ("AutoAWQ vs The Stack v2" and "AutoAWQ vs Unsloth", WQLinear_*
+ * paragraphs).
  *
- * wq_gemv: the decode kernel for M <= 16 (returns WQ_ERR_UNSUPPORTED
- *   above): streams the packed words with 128-bit loads, unpacks and
- *   dequantizes in registers, accumulates with fp16-pair dot products into
- *   fp32, and reduces the split-K partial sums across the wavefront.
+ * wq_gemv: the decode kernels for M <= 16 (returns WQ_ERR_UNSUPPORTED
+ *   above).  M = 1 (and act-order layers): streams the packed words with
+ *   128-bit loads, unpacks in registers, accumulates with fp16-pair dot
+ *   products into fp32 and reduces the split-K partial sums across the
+ *   wavefront.  2 <= M <= 16 without act-order: one pass over the weights
+ *   with the products on fp16 matrix-core instructions (16 x 16 x 32), the
+ *   activations staged in LDS (in K-slabs when M rows of K do not fit).
  * wq_gemm: the prefill kernel for any M: dequantizes weight tiles to
  *   fp16 and feeds fp16 matrix-core (MFMA) instructions with fp32
  *   accumulators.
@@ -315,18 +341,18 @@ wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed, const uint
                            int32_t M, int32_t N, int32_t K, int32_t bits, int32_t group_size,
                            void* stream);
 
-/* The decode GEMV with its neighbours fused (the pages: fusing a block's
- * operations into single kernels saves launches and intermediate tensors,
- * "AutoAWQ vs The Stack v2", paragraph on fused attention and transformer
- * blocks).  act_scale (nullable, fp16 [K], 16-byte aligned): the AWQ
+/* The decode GEMV with its neighbours fused (fusing a block's operations
+ * into single kernels saves launches and intermediate tensors, "AutoAWQ vs
+ * The Stack v2", paragraph on fused attention and transformer blocks).  act_scale (nullable, fp16 [K], 16-byte aligned): the AWQ
  * activation scaling x' = fp16(fp32(x) / fp32(act_scale[k])), done while the
  * activations are staged, bit-identical to wq_scale_act followed by
  * wq_gemv.  bias (nullable, fp16 [N]): added to the fp32 sum of each output
  * before its rounding.  silu = 0: y fp16 [M][N] = x' . dequant(Wq)^T + bias.
  * silu = 1: the stacked gate/up layout of wq_gemv_silu_mul (N even), y fp16
  * [M][N/2] = silu(g + bias[j]) * (u + bias[j + N/2]).  Other arguments as
- * wq_gemv; 1 <= M <= 4 and fp16 x of K within the 64 KB staging budget
- * (K <= 16384 at M = 1), else WQ_ERR_UNSUPPORTED. */
+ * wq_gemv.  silu = 0: 1 <= M <= 16 (act-order: M <= 4); silu = 1:
+ * 1 <= M <= 4 and fp16 x of K within the 64 KB staging budget (K <= 16384
+ * at M = 1); else WQ_ERR_UNSUPPORTED. */
 wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                      const uint8_t* zeros, const int32_t* perm, const uint16_t* act_scale,
                      const uint16_t* bias, uint16_t* y, int32_t M, int32_t N, int32_t K,
