@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--gemm-steps", type=int, default=0, help="prefill iterations (default: steps // 5)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cfg", default=None, help="with --only configs: comma-separated workload names to run "
+                   "(single-gemv, llama7b-decode, prefill-awq, 70b-layer, gptq-variant)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--only", choices=["decode", "prefill", "copy", "configs", "awq", "silu", "gptq", "fused"], default=None,
                    help="run one leg only (for profiler runs); 'copy' runs plain device-to-device "
@@ -296,11 +298,25 @@ def config_cases():
     return cases
 
 
-def configs_leg(wq, torch, launches):
+def kernel_name(M, act_order, gemv_max_m):
+    """Which kernel wq_linear runs for this case (a label for the record)."""
+    if M == 1:
+        return "gemv-stream"
+    if M <= gemv_max_m and not act_order:
+        return "gemv-skinny-mfma"
+    if M <= 4:
+        return "gemv-stream"
+    return "gemm"
+
+
+def configs_leg(wq, torch, launches, only=None):
     """Time wq_linear on every config case (rotating weight pools of at least
-    1 GiB, graph replays, HIP events); one JSON line per case."""
+    1 GiB, graph replays, HIP events); one JSON line per case.  only: names
+    of the workloads to run (all when None)."""
     rows = []
     for ci, c in enumerate(config_cases()):
+        if only and c["cfg"] not in only:
+            continue
         K, N, M, bits, group = c["K"], c["N"], c["M"], c["bits"], c["group"]
         seed = (7, ci)
         x = torch.from_numpy(I.activations(seed, M, K)).cuda()
@@ -341,7 +357,7 @@ def configs_leg(wq, torch, launches):
         bound = "hbm" if all_b / (HBM_PEAK_GBS * 1e9) > flops / (FP16_MFMA_PEAK_TFLOPS * 1e12) else "mfma"
         row = dict(cfg=c["cfg"], K=K, N=N, M=M, bits=bits, group=group, sym=bool(c.get("sym")),
                    act_order=bool(c.get("act_order")), awq=bool(c.get("awq")),
-                   kernel="gemv" if M <= wq.gemv_max_m() else "gemm", us=round(ms * 1e3, 2),
+                   kernel=kernel_name(M, layer.perm is not None, wq.gemv_max_m()), us=round(ms * 1e3, 2),
                    packed_GBs=round(packed_b / t / 1e9, 1), all_GBs=round(all_b / t / 1e9, 1),
                    TFLOPs=round(flops / t / 1e12, 2), bound=bound,
                    frac=round(all_b / t / 1e9 / HBM_PEAK_GBS if bound == "hbm" else
@@ -731,7 +747,7 @@ def main():
         print(json.dumps(gptq_leg(wq, torch, 3, not args.no_cpu_baseline)), flush=True)
         return
     if args.only == "configs":
-        configs_leg(wq, torch, max(args.steps, 1))
+        configs_leg(wq, torch, max(args.steps, 1), args.cfg.split(",") if args.cfg else None)
         return
     if args.only == "prefill":
         pre = prefill_leg(wq, torch, gemm_steps, max(5, args.warmup // 5))

@@ -308,10 +308,13 @@ enum class TileKind { k16, k32, k64, kLarge, k128 };
 #endif
 constexpr int kSmallNst = WQ_GEMM_SMALL_NST;
 
+#ifndef WQ_GEMM_K64_MAX_M
+#define WQ_GEMM_K64_MAX_M 64
+#endif
 inline TileKind tile_kind(int M, int N, int K, int bits) {
     if (M <= 16) return TileKind::k16;
     if (M <= 32) return TileKind::k32;
-    if (M <= 64) return TileKind::k64;
+    if (M <= WQ_GEMM_K64_MAX_M) return TileKind::k64;
     if (wqh::gemm_large_fits(M, N, K, bits)) return TileKind::kLarge;
     return TileKind::k128;
 }

@@ -8,6 +8,8 @@
 // same page, section "AWQ: find the one percent that matters".
 #include <math.h>
 
+#include <algorithm>
+
 #include "wq_common.h"
 
 namespace {
@@ -303,24 +305,44 @@ __global__ void __launch_bounds__(256) awq_fold_vec_kernel(const uint16_t* __res
 
 // x_out = fp16(x / s), 8 elements per thread (K is a multiple of 32, so rows
 // split into whole 8-element groups).
+// Thread (blockIdx.x, threadIdx.x) owns 8-channel block kb of every row in
+// its row range: s and its conversions are read once, RU rows' loads go out
+// together before any division, and no per-element index division is needed.
+constexpr int kScaleActRows = 4;
 __global__ void __launch_bounds__(256) scale_act_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ s,
-                                                        long long total8, int K, uint16_t* __restrict__ x_out) {
+                                                        int M, int K, int rows_per_block, uint16_t* __restrict__ x_out) {
+    constexpr int RU = kScaleActRows;
     const int K8 = K / 8;
-    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total8;
-         t += (long long)gridDim.x * blockDim.x) {
-        const int k0 = int(t % K8) * 8;
-        const u4 v = reinterpret_cast<const u4*>(x)[t];
-        const u4 sv = *reinterpret_cast<const u4*>(s + k0);
-        u4 o;
-        uint32_t in[4] = {v.x, v.y, v.z, v.w}, sc[4] = {sv.x, sv.y, sv.z, sv.w}, out[4];
+    const int kb = blockIdx.x * blockDim.x + threadIdx.x;
+    if (kb >= K8) return;
+    const u4 sv = reinterpret_cast<const u4*>(s)[kb];
+    const uint32_t sc[4] = {sv.x, sv.y, sv.z, sv.w};
+    float sf[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = __fdiv_rn(h2f(uint16_t(in[i])), h2f(uint16_t(sc[i])));
-            const float hi = __fdiv_rn(h2f(uint16_t(in[i] >> 16)), h2f(uint16_t(sc[i] >> 16)));
-            out[i] = uint32_t(f2h(lo)) | (uint32_t(f2h(hi)) << 16);
+    for (int i = 0; i < 4; ++i) {
+        sf[2 * i] = h2f(uint16_t(sc[i]));
+        sf[2 * i + 1] = h2f(uint16_t(sc[i] >> 16));
+    }
+    const int m_begin = blockIdx.y * rows_per_block;
+    const int m_end = min(M, m_begin + rows_per_block);
+    for (int m0 = m_begin; m0 < m_end; m0 += RU) {
+        u4 v[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+            v[u] = reinterpret_cast<const u4*>(x)[size_t(min(m0 + u, m_end - 1)) * K8 + kb];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            if (m0 + u >= m_end) break;
+            const uint32_t in[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t out[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __fdiv_rn(h2f(uint16_t(in[i])), sf[2 * i]);
+                const float hi = __fdiv_rn(h2f(uint16_t(in[i] >> 16)), sf[2 * i + 1]);
+                out[i] = uint32_t(f2h(lo)) | (uint32_t(f2h(hi)) << 16);
+            }
+            reinterpret_cast<u4*>(x_out)[size_t(m0 + u) * K8 + kb] = u4{out[0], out[1], out[2], out[3]};
         }
-        o.x = out[0]; o.y = out[1]; o.z = out[2]; o.w = out[3];
-        reinterpret_cast<u4*>(x_out)[t] = o;
     }
 }
 
@@ -406,8 +428,15 @@ extern "C" wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t 
     if (M == 0) return WQ_OK;  // empty problem: no pointer is read
     if (!x || !s || !x_out) return WQ_ERR_ARG;
     if (!wqh::aligned16(x) || !wqh::aligned16(x_out) || !wqh::aligned16(s)) return WQ_ERR_ARG;
-    const long long total8 = (long long)M * K / 8;
-    hipLaunchKernelGGL(scale_act_kernel, dim3(grid_for(total8, 256, 8192)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), x, s, total8, int(K), x_out);
+    // about 4096 blocks: K/2048 column strips times row ranges of at least
+    // kScaleActRows rows
+    const int K8 = K / 8;
+    const int gx = (K8 + 255) / 256;
+    int gy = std::max(1, std::min(M, 4096 / gx));
+    int rows = (M + gy - 1) / gy;
+    rows = std::max(rows, std::min(M, kScaleActRows));
+    gy = (M + rows - 1) / rows;
+    hipLaunchKernelGGL(scale_act_kernel, dim3(gx, gy), dim3(256), 0, static_cast<hipStream_t>(stream), x, s, int(M),
+                       int(K), rows, x_out);
     return wqh::launch_status();
 }
