@@ -188,6 +188,7 @@ __device__ __forceinline__ void decode_block_nat<3>(const uint32_t* w, int b, ui
 struct GroupDiv {
     uint32_t mul;
     uint32_t shift;
+    int chunks;  // d, the divisor
 };
 
 __device__ __forceinline__ int chunk_group(int cg, GroupDiv gd) {
@@ -252,7 +253,7 @@ inline wq::GroupDiv group_magic(int gs) {
     while ((uint64_t(1) << lg) < d) ++lg;
     const uint32_t sh = 24 + lg;
     const uint64_t mul = ((uint64_t(1) << sh) + d - 1) / d;
-    return wq::GroupDiv{uint32_t(mul), sh};
+    return wq::GroupDiv{uint32_t(mul), sh, int(d)};
 }
 
 inline wq_status hip_status(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HIP; }

@@ -48,6 +48,38 @@ __device__ __forceinline__ void load_chunk(const uint32_t* p, uint32_t* w) {
     }
 }
 
+// Buffer resource over `bytes` bytes at p (word 3: raw 32-bit data format).
+// An access through it adds a 32-bit lane offset to a wave-uniform base held
+// in scalar registers, so a lane's address costs no 64-bit vector arithmetic;
+// offsets at or past `bytes` read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
+}
+constexpr int kBufNT = 2;  // cache policy: nontemporal
+
+// One chunk (32 codes, 4 * BITS bytes) at byte offset off of a row resource.
+// (Whole-vector bit casts only: a bit cast of one element of a vector
+// reads element 0.)
+template <int BITS>
+__device__ __forceinline__ void load_chunk_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t* w) {
+    if constexpr (BITS == 4) {
+        const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufNT));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (BITS == 8) {
+        const u4 a = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufNT));
+        const u4 b = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, kBufNT));
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else if constexpr (BITS == 2) {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kBufNT));
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        const u4 v = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, kBufNT));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z;
+    }
+}
+
 // Sum over the 64 lanes of a wavefront; the result is valid in every lane.
 // Within each row of 16 lanes the partial sums move through DPP (quad
 // permutes, then half-row and row mirrors); the four row sums are then read
@@ -330,10 +362,7 @@ __device__ __forceinline__ void decode_chunk_split(const uint32_t* w, uint32_t* 
 // dequantized weights by about 2^-12 relative per weight, averaged over K.
 // Wavefronts per block of the streaming kernel (the activations are staged
 // once per block).
-#ifndef WQ_GEMV_WPB
-#define WQ_GEMV_WPB 4
-#endif
-constexpr int kStreamWaves = WQ_GEMV_WPB;
+constexpr int kStreamWaves = 4;
 
 template <int BITS, int R, int CPL>
 struct WideSlot {
@@ -342,8 +371,9 @@ struct WideSlot {
     bool ok[R];
 };
 
-template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER, bool SILU = false, bool EX = false>
-__global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const uint16_t* __restrict__ x,
+template <int BITS, int MT, int R, int D, int CPL, bool HAS_Z, bool GATHER, bool SILU = false, bool EX = false,
+          int WPB = kStreamWaves, bool EARLY = false>
+__global__ void __launch_bounds__(64 * WPB) gemv_stream_kernel(const uint16_t* __restrict__ x,
                                                           const uint32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
@@ -371,6 +401,10 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int G = chunk_group(CN - 1, gd) + 1;
     const size_t row_words = (size_t)CN * BITS;
+    // group of chunk c = floor((c + 0.5) / d), d chunks per group, by the
+    // float reciprocal: exact while c < 2^21, since (c + 0.5) / d stays at
+    // least 0.5 / d away from an integer, farther than the rounding error
+    const float ginv = 1.0f / float(gd.chunks);
     // With SILU the N rows are a stacked gate (rows [0, N/2)) and up
     // (rows [N/2, N)) projection: row group g is the pair (g, g + N/2) and
     // the epilogue writes y[m][g] = silu(gate) * up, N/2 outputs per row.
@@ -379,8 +413,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     const int n_groups = SILU ? half : (N + R - 1) / R;
     const int J = (CNP + 63) / 64;  // slot iterations per row group
 
-    const int wg0 = blockIdx.x * kStreamWaves + wave;
-    const int wstride = gridDim.x * kStreamWaves;
+    const int wg0 = blockIdx.x * WPB + wave;
+    const int wstride = gridDim.x * WPB;
     const int my_groups = wg0 < n_groups ? (n_groups - wg0 + wstride - 1) / wstride : 0;
     const int T = my_groups * J;  // flat (row group, slot iteration) count of this wave
 
@@ -400,10 +434,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
         const int cp = lane + 64 * i_j;
         const bool valid = tv && cp < CNP;
         const int cpc = cp < CNP ? cp : CNP - 1;
-        const int g = chunk_group(cpc * CPL, gd);
-        // row bases are wave-uniform (scalar registers), lane offsets
-        // unsigned 32-bit: the loads take the scalar-base form with no
-        // per-lane 64-bit address arithmetic
+        const int g = int(__builtin_fmaf(float(cpc * CPL), ginv, 0.5f * ginv));
         const uint32_t woff = uint32_t(cpc) * uint32_t(CPL * BITS * 4);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -411,14 +442,18 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
             const bool nok = n < N;  // wave-uniform
             const int nn = __builtin_amdgcn_readfirstlane(nok ? n : N - 1);
             sl.ok[r] = valid && nok;
-            const char* rowp = reinterpret_cast<const char*>(packed) + size_t(nn) * row_words * 4;
+            // row bases wave-uniform (buffer resources in scalar registers),
+            // lane offsets 32-bit
+            const auto rw = buf_rsrc(reinterpret_cast<const char*>(packed) + size_t(nn) * row_words * 4,
+                                     uint32_t(row_words * 4));
 #pragma unroll
-            for (int e = 0; e < CPL; ++e)
-                load_chunk<BITS>(reinterpret_cast<const uint32_t*>(rowp + woff + e * BITS * 4), sl.w[r][e]);
-            sl.s[r] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(scales) + size_t(nn) * G * 2 +
-                                                         uint32_t(g) * 2u);
+            for (int e = 0; e < CPL; ++e) load_chunk_buf<BITS>(rw, woff + uint32_t(e * BITS * 4), sl.w[r][e]);
+            sl.s[r] = __builtin_amdgcn_raw_buffer_load_b16(
+                buf_rsrc(reinterpret_cast<const char*>(scales) + size_t(nn) * G * 2, uint32_t(G * 2)), uint32_t(g) * 2u,
+                0, 0);
             if constexpr (HAS_Z)
-                sl.z[r] = *(reinterpret_cast<const uint8_t*>(zeros) + size_t(nn) * G + uint32_t(g));
+                sl.z[r] = __builtin_amdgcn_raw_buffer_load_b8(
+                    buf_rsrc(reinterpret_cast<const char*>(zeros) + size_t(nn) * G, uint32_t(G)), uint32_t(g), 0, 0);
             else
                 sl.z[r] = 1u << (BITS - 1);
         }
@@ -503,7 +538,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
     // stores are unconditional; a pass that starts past the last slot is
     // skipped.  A gather through perm needs the perm values first, so with
     // act-order the weights still go out first.
-    constexpr int NT = 64 * kStreamWaves;
+    constexpr int NT = 64 * WPB;
     constexpr int PRE = (MT == 1 && !GATHER) ? 2 : 1;
     u4 xpre[PRE][MT][CPL][4];
     u4 spre[PRE][CPL][4];  // scales, loaded with the activations (EX)
@@ -598,7 +633,12 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int t = t0 + d;
-            // ---- compute iteration t from slot d
+            // ---- take iteration t out of slot d; EARLY refills the slot with
+            // iteration t + D at once, so that the refill is in flight while
+            // t is decoded and summed (otherwise after the sums)
+            const WideSlot<BITS, R, CPL> cur = slot[d];
+            if constexpr (EARLY) issue(slot[d], t + D);
+            // ---- compute iteration t
             {
                 const int cp = min(lane + 64 * c_j, CNP - 1);
                 float2 X[MT];
@@ -623,7 +663,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         uint32_t h[16];
-                        decode_chunk_split<BITS>(slot[d].w[r][e], h);
+                        decode_chunk_split<BITS>(cur.w[r][e], h);
 #pragma unroll
                         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -634,8 +674,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const float sf =
-                        slot[d].ok[r] ? float(__builtin_bit_cast(_Float16, uint16_t(slot[d].s[r]))) : 0.f;
-                    const float zf = float(slot[d].z[r]);
+                        cur.ok[r] ? float(__builtin_bit_cast(_Float16, uint16_t(cur.s[r]))) : 0.f;
+                    const float zf = float(cur.z[r]);
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         float t = __builtin_fmaf(-(1024.f + zf), X[m].x, a[r][m]);
@@ -662,8 +702,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves) gemv_stream_kernel(const ui
                 ++c_k;
             }
             c_j = c_j + 1 == J ? 0 : c_j + 1;
-            // ---- refill slot d with iteration t + D
-            issue(slot[d], t + D);
+            if constexpr (!EARLY) issue(slot[d], t + D);
         }
     }
     // ---- outputs: lane k * R + r holds row R * (wg0 + k * wstride) + r (with
@@ -730,71 +769,90 @@ inline size_t stream_lds_bytes(int MT, int K, int cpl, bool gather = false) {
     return size_t(MT) * K * 2 + sums + (gather ? size_t(K) * 2 : 0);
 }
 
-// Launch shape of the streaming kernel (blocks per CU; rows per wavefront
-// and pipeline depth for layers narrower / wider than 8192 columns).
+// Launch shape of the streaming kernel: resident blocks per CU of the
+// default shape (R = 2 rows per wavefront, D = 2 slots, refill after the
+// sums).
 #ifndef WQ_GEMV_BPC
 #define WQ_GEMV_BPC 3
-#endif
-#ifndef WQ_GEMV_NARROW_R
-#define WQ_GEMV_NARROW_R 2
-#endif
-#ifndef WQ_GEMV_NARROW_D
-#define WQ_GEMV_NARROW_D 2
-#endif
-#ifndef WQ_GEMV_WIDE_R
-#define WQ_GEMV_WIDE_R 2
-#endif
-#ifndef WQ_GEMV_WIDE_D
-#define WQ_GEMV_WIDE_D 2
 #endif
 #ifndef WQ_GEMV_CPL
 #define WQ_GEMV_CPL 1
 #endif
 constexpr int kStreamBlocksPerCU = WQ_GEMV_BPC;
 
-template <int BITS, int MT, int R, int D, int CPL, bool SILU = false, bool EX = false>
+// Compute units and LDS bytes per compute unit of the current device
+// (MI355X values when the query fails).
+struct CuLimits {
+    int cus = 256;
+    size_t lds = 160 * 1024;
+};
+inline CuLimits cu_limits() {
+    CuLimits c;
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return c;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) c.cus = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess && v > 0)
+        c.lds = size_t(v);
+    return c;
+}
+
+template <int BITS, int MT, int R, int D, int CPL, bool SILU = false, bool EX = false, int WPB = kStreamWaves,
+          bool EARLY = false>
 wq_status launch_stream(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                         const int32_t* perm, uint16_t* y, int M, int N, int K, int gs, hipStream_t s,
-                        const uint16_t* act_scale = nullptr, const uint16_t* bias = nullptr) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
+                        const uint16_t* act_scale = nullptr, const uint16_t* bias = nullptr,
+                        int bpc = kStreamBlocksPerCU) {
+    const CuLimits cl = cu_limits();
+    const size_t lds = stream_lds_bytes(MT, K, CPL, perm != nullptr);
     // One round of resident blocks (more wavefronts in flight beat equal
-    // shares: measured), unless a wavefront would take more than 64 / R row
-    // groups (it keeps one finished output per lane until its end).
+    // shares: measured): at most bpc per CU and no more than the CU's LDS
+    // holds (a block past those would wait for a whole earlier block),
+    // unless a wavefront would take more than 64 / R row groups (it keeps
+    // one finished output per lane until its end).
+    const int per_cu = std::max(1, std::min(bpc, int(cl.lds / lds)));
     const int n_groups = SILU ? N / 2 : (N + R - 1) / R;
     const int max_per_wave = SILU ? 64 : 64 / R;
-    int blocks = (n_groups + kStreamWaves - 1) / kStreamWaves;
-    if (blocks > cus * kStreamBlocksPerCU) blocks = cus * kStreamBlocksPerCU;
-    blocks = std::max(blocks, (n_groups + kStreamWaves * max_per_wave - 1) / (kStreamWaves * max_per_wave));
-    const size_t lds = stream_lds_bytes(MT, K, CPL, perm != nullptr);
+    int blocks = (n_groups + WPB - 1) / WPB;
+    if (blocks > cl.cus * per_cu) blocks = cl.cus * per_cu;
+    blocks = std::max(blocks, (n_groups + WPB * max_per_wave - 1) / (WPB * max_per_wave));
     const GroupDiv gd = wqh::group_magic(gs);
     if (zeros && perm)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s, x,
-                           packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, true, SILU, EX, WPB, EARLY>), dim3(blocks),
+                           dim3(64 * WPB), lds, s, x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     else if (zeros)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
-                           x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, true, false, SILU, EX, WPB, EARLY>), dim3(blocks),
+                           dim3(64 * WPB), lds, s, x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     else if (perm)
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
-                           x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, true, SILU, EX, WPB, EARLY>), dim3(blocks),
+                           dim3(64 * WPB), lds, s, x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     else
-        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false, SILU, EX>), dim3(blocks), dim3(64 * kStreamWaves), lds, s,
-                           x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
+        hipLaunchKernelGGL((gemv_stream_kernel<BITS, MT, R, D, CPL, false, false, SILU, EX, WPB, EARLY>), dim3(blocks),
+                           dim3(64 * WPB), lds, s, x, packed, scales, zeros, perm, y, M, N, K, gd, act_scale, bias);
     return wqh::launch_status();
 }
 
+// Launch shape by layer (measured on the decode and 70B shapes at M = 1):
+// - K <= 4096 (at most two slot iterations per row group): one slot per
+//   wavefront refilled before its sums, four blocks per CU;
+// - activations too long for three blocks per CU in LDS (K above about 24K):
+//   8-wavefront blocks, two per CU, one slot refilled before its sums, so the
+//   CU keeps 16 wavefronts;
+// - otherwise (and for M > 1) two slots refilled after the sums, three blocks
+//   per CU.
 template <int BITS, int MT, int CPL>
 wq_status launch_stream_cpl(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                             const uint8_t* zeros, const int32_t* perm, uint16_t* y, int M, int N, int K, int gs,
                             hipStream_t s) {
-    if (N < 8192)
-        return launch_stream<BITS, MT, WQ_GEMV_NARROW_R, WQ_GEMV_NARROW_D, CPL>(x, packed, scales, zeros, perm, y, M,
-                                                                               N, K, gs, s);
-    return launch_stream<BITS, MT, WQ_GEMV_WIDE_R, WQ_GEMV_WIDE_D, CPL>(x, packed, scales, zeros, perm, y, M, N, K,
-                                                                       gs, s);
+    if constexpr (MT == 1) {
+        const size_t lds = stream_lds_bytes(MT, K, CPL, perm != nullptr);
+        if (3 * lds > cu_limits().lds)
+            return launch_stream<BITS, MT, 2, 1, CPL, false, false, 8, true>(x, packed, scales, zeros, perm, y, M, N,
+                                                                             K, gs, s, nullptr, nullptr, 2);
+        if (K <= 4096)
+            return launch_stream<BITS, MT, 2, 1, CPL, false, false, kStreamWaves, true>(
+                x, packed, scales, zeros, perm, y, M, N, K, gs, s, nullptr, nullptr, 4);
+    }
+    return launch_stream<BITS, MT, 2, 2, CPL>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
 }
 
 // Streaming kernel when the activations fit in LDS and M <= 4 (two chunks
@@ -853,7 +911,7 @@ wq_status launch_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* s
         if (M <= 2) return launch_stream<BITS, 2, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
         return launch_stream<BITS, 4, 2, 2, 1, true, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
     }
-    constexpr int R = WQ_GEMV_NARROW_R, D = WQ_GEMV_NARROW_D;
+    constexpr int R = 2, D = 2;
     if (M <= 1) return launch_stream<BITS, 1, R, D, 1, false, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
     if (M <= 2) return launch_stream<BITS, 2, R, D, 1, false, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
     return launch_stream<BITS, 4, R, D, 1, false, true>(x, packed, scales, zeros, perm, y, M, N, K, gs, s, act_scale, bias);
