@@ -78,7 +78,10 @@ def layer_bytes(M, K, N, bits=BITS, group=GROUP):
 # Device sources each timed kernel is built from (kernel file + shared headers).
 GEMV_SOURCES = ("wq_gemv.hip", "wq_common.h")
 GEMM_SOURCES = ("wq_gemm_large.hip", "wq_gemm_common.h", "wq_common.h")
-GEMV_KERNEL = "gemv_stream_kernel<4,1,2,2,1,true,false,false,false>"
+# the decode projections' M = 1 kernels: K = 4096 layers refill one slot
+# before its sums (4 blocks per CU), the K = 11008 layer keeps two slots
+GEMV_KERNEL = ("gemv_stream_kernel<4,1,2,1,1,true,false,false,false,4,true> (qkv, o_proj, gate+up); "
+               "gemv_stream_kernel<4,1,2,2,1,true,false,false,false,4,false> (down)")
 GEMM_KERNEL = "gemm_large_kernel<4,true,true,false>"
 
 

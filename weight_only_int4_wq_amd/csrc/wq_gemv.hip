@@ -424,16 +424,18 @@ __global__ void __launch_bounds__(64 * WPB) gemv_stream_kernel(const uint16_t* _
 
     // Loads are issued unconditionally: a wait-count merge at a branch around
     // them would make every later wait drain all loads in flight.  The issue
-    // position stops at the wavefront's last one (t = T - 1), so the refills
-    // past it re-read the chunks it loaded last, and lanes past a row's end
-    // re-read its last chunk (same cache lines, no extra memory traffic and
-    // no address shared by the whole grid).
+    // position stops at the wavefront's last one (t = T - 1); the refills past
+    // it read the first 16 bytes of the last row group's rows in every lane
+    // (one cache line per row: re-reading the chunks loaded last could fetch
+    // them from memory again, since those loads bypass the caches' retention),
+    // and lanes past a row's end re-read its last chunk (same cache lines; no
+    // address is shared by the whole grid).
     WideSlot<BITS, R, CPL> slot[D];
     auto issue = [&](WideSlot<BITS, R, CPL>& sl, int t) {
         const bool tv = t < T;  // wave-uniform
         const int cp = lane + 64 * i_j;
         const bool valid = tv && cp < CNP;
-        const int cpc = cp < CNP ? cp : CNP - 1;
+        const int cpc = tv ? (cp < CNP ? cp : CNP - 1) : 0;
         const int g = int(__builtin_fmaf(float(cpc * CPL), ginv, 0.5f * ginv));
         const uint32_t woff = uint32_t(cpc) * uint32_t(CPL * BITS * 4);
 #pragma unroll
