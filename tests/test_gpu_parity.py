@@ -269,6 +269,23 @@ def test_gptq_variants(bits, gs, act):
             check_y(run("gemm", x, L, bits, gs), y_ref, f"gemm b={bits} g={gs} act={act} M=1")
 
 
+@pytest.mark.parametrize("M,K", [(5, 4096), (300, 1024), (1030, 1024), (3, 33792)])
+def test_act_order_gemm_equals_pregathered(M, K):
+    # The act-order GEMM gathers x into packed column order first (rows
+    # staged in LDS while K <= 32768, one element per thread beyond); the
+    # product must equal the plain GEMM on x[:, perm] gathered by the host,
+    # bit for bit.
+    seed = (108, M, K)
+    N, bits, gs = 96, 4, 128
+    w = I.weights(seed, N, K, 0.02)
+    L = gpu_layer(w, bits, gs, I.act_order_gidx(seed, K, gs), sym=False)
+    x = dev(I.activations(seed, M, K))
+    xg = x[:, L["perm"].long()].contiguous()
+    a = wq.gemm(x, L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"])
+    b = wq.gemm(xg, L["packed"], L["scales"], L["zeros"], bits, gs)
+    assert np.array_equal(host(a).view(np.uint16), host(b).view(np.uint16))
+
+
 def test_dispatch_follows_batch_size():
     seed = (106,)
     K, N = 1024, 512
