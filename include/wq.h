@@ -249,16 +249,20 @@ wq_status wq_dequant(const uint32_t* packed, const uint16_t* scales, const uint8
 wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t K,
                        uint16_t* x_out, void* stream);
 
-/* Bytes of device workspace wq_gemm (and wq_linear when it dispatches to
- * wq_gemm) uses for these arguments on the current device; 0 when none.
- * Layout: with act-order (has_perm != 0) the gathered activations
- * x[:, perm], M*K fp16 values rounded up to 256 bytes; then, when the launch
- * has too few output tiles to fill the GPU, fp32 partial outputs of a K
- * split (splits*M*N floats; the split count is chosen on the host from the
- * shape and the number of compute units).  The act-order part is required;
- * the split part is optional: with less workspace wq_gemm does not split K
- * (same result up to fp32 summation order, slower).  wq_gemv never uses
- * workspace.  Returns 0 for non-positive sizes or unsupported bit widths. */
+/* Bytes of device workspace wq_gemv, wq_gemm and wq_linear use for these
+ * arguments on the current device (the largest of their needs); 0 when
+ * none.  wq_gemm layout: with act-order (has_perm != 0) the gathered
+ * activations x[:, perm], M*K fp16 values rounded up to 256 bytes; then,
+ * when the launch has too few output tiles to fill the GPU, fp32 partial
+ * outputs of a K split (splits*M*N floats; the split count is chosen on the
+ * host from the shape and the number of compute units).  wq_gemv at
+ * 2 <= M <= 16 without act-order, when M rows of K activations do not fit
+ * in LDS at once: fp32 partial outputs of its K slabs (slabs*M*N floats,
+ * sized here for the group size with the most groups).  The act-order part
+ * is required; the split parts are optional: with less workspace the
+ * kernels do not split K across blocks (same result up to fp32 summation
+ * order, slower).  Returns 0 for non-positive sizes or unsupported bit
+ * widths. */
 size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t has_perm);
 
 /* y fp16 [M][N] = x fp16 [M][K] . dequant(packed)^T with fp32 accumulation
@@ -274,7 +278,10 @@ size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t 
  *   products into fp32 and reduces the split-K partial sums across the
  *   wavefront.  2 <= M <= 16 without act-order: one pass over the weights
  *   with the products on fp16 matrix-core instructions (16 x 16 x 32), the
- *   activations staged in LDS (in K-slabs when M rows of K do not fit).
+ *   activations staged in LDS; when M rows of K do not fit, K is cut into
+ *   slabs, one group of blocks per slab with the workspace (then a second
+ *   kernel adds the slabs' fp32 partials in slab order), or each block
+ *   walking the slabs in turn without it.
  * wq_gemm: the prefill kernel for any M: dequantizes weight tiles to
  *   fp16 and feeds fp16 matrix-core (MFMA) instructions with fp32
  *   accumulators.
@@ -283,7 +290,7 @@ size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t 
  *
  * workspace: device memory of wq_workspace_size(M, N, K, bits, perm != NULL)
  * bytes (16-byte aligned), or NULL when that size is 0; WQ_ERR_ARG if
- * act-order needs it and it is missing or short.  Split-K partials are
+ * act-order needs it and it is missing or short, or if it is misaligned.  Split-K partials are
  * summed in a fixed order, so results are deterministic.  Calls that share
  * a workspace must be ordered on one stream.  y must not overlap any input
  * or the workspace. */
@@ -304,10 +311,11 @@ wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const uint16_t* s
 
 /* wq_linear for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc):
- * the same dispatch and kernels as wq_linear, with the GEMM's scratch (the
- * act-order activation gather, then split-K fp32 partials) in a static
- * device array of WQ_NOALLOC_SCRATCH_BYTES bytes inside the library instead
- * of a caller workspace.  Each GPU holds its own copy of the array from the
+ * the same dispatch and kernels as wq_linear, with their scratch (the
+ * GEMM's act-order activation gather, then split-K fp32 partials; the
+ * decode kernel's K-slab fp32 partials) in a static device array of
+ * WQ_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a caller
+ * workspace.  Each GPU holds its own copy of the array from the
  * first call on it until the process ends; the call looks up the current
  * device's copy (hipGetSymbolAddress) on its first use there and allocates
  * nothing.  The array keeps the last call's contents and nothing in it
@@ -317,7 +325,8 @@ wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const uint16_t* s
  * current device must be the stream's device.  Returns WQ_ERR_TOO_LARGE
  * when act-order needs a gather of more than WQ_NOALLOC_SCRATCH_BYTES
  * (M*K*2 bytes, rounded up to 256); with too little room for the split-K
- * partials the GEMM splits K fewer ways.  Otherwise as wq_linear. */
+ * partials the GEMM splits K fewer ways, and the decode kernel walks its
+ * K-slabs in each block.  Otherwise as wq_linear. */
 #define WQ_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
 wq_status wq_linear_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                             const uint8_t* zeros, const int32_t* perm, uint16_t* y,

@@ -60,6 +60,10 @@ def test_workspace_size():
     # few tiles along a long K: split partials only
     ws = wq.workspace_size(32, 8192, 28672, 4, False)
     assert ws > 0 and ws % (32 * 8192 * 4) == 0
+    # decode batch whose activations exceed LDS: fp32 partials of the K-slabs
+    # (or of the GEMM's split, whichever is larger), whole copies of y
+    ws = wq.workspace_size(16, 4096, 11008, 4, False)
+    assert ws > 0 and ws % (16 * 4096 * 4) == 0
     # invalid arguments
     assert wq.workspace_size(0, 4096, 4096, 4, False) == 0
     assert wq.workspace_size(256, 4096, 4096, 5, False) == 0

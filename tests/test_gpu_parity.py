@@ -202,12 +202,43 @@ def test_skinny_formats_and_slabs(M, bits, gs, sym, N, K):
     L = gpu_layer(w, bits, gs, sym=sym)
     x = I.activations(seed, M, K)
     check_y(run("gemv", x, L, bits, gs), O.linear_ref(x, ref["w_hat"]), f"gemv b={bits} g={gs} M={M} K={K}")
-    # the fused AWQ input division is bit-identical to dividing first
+    # the fused AWQ input division is bit-identical to dividing first (both
+    # without a workspace: wq_gemv_ex has none, so K-slabs are walked by
+    # each block in turn on both sides)
     _, s_h = O.awq_channel_scales(x, 0.5)
     xd, sd = dev(x), dev(s_h)
-    y_a = wq.gemv(wq.scale_act(xd, sd), L["packed"], L["scales"], L["zeros"], bits, gs)
+    no_ws = torch.empty((16,), dtype=torch.uint8, device="cuda")
+    y_a = wq.gemv(wq.scale_act(xd, sd), L["packed"], L["scales"], L["zeros"], bits, gs, workspace=no_ws)
     y_b = wq.gemv_ex(xd, L["packed"], L["scales"], L["zeros"], bits, gs, act_scale=sd)
     assert np.array_equal(host(y_a).view(np.uint16), host(y_b).view(np.uint16))
+
+
+@pytest.mark.parametrize("M,bits,gs,sym,N,K", [(16, 4, 128, False, 100, 11008), (7, 3, 32, True, 70, 28672),
+                                               (16, 2, 64, True, 4104, 8448), (9, 8, -1, True, 33, 16384)])
+def test_skinny_slab_split_matches_walk(M, bits, gs, sym, N, K):
+    # M rows of K too long for LDS: with the workspace each K-slab goes to
+    # its own group of blocks (fp32 partials, then summed in slab order);
+    # without it every block walks the slabs in turn.  Both must meet the
+    # tolerance and agree to rounding; the split form is deterministic.
+    seed = (110, M, bits, N, K)
+    w = I.weights(seed, N, K, 0.02)
+    ref = O.quantize_linear_layer(w, bits, gs, symmetric=sym)
+    L = gpu_layer(w, bits, gs, sym=sym)
+    x = I.activations(seed, M, K)
+    need = wq.workspace_size(M, N, K, bits, False)
+    assert need > 0 and need % (M * N * 4) == 0, "shape expected to split into slabs"
+    xd = dev(x)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    ys = wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, workspace=ws)
+    ys2 = wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, workspace=ws)
+    yw = wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs,
+                 workspace=torch.empty((16,), dtype=torch.uint8, device="cuda"))
+    y_ref = O.linear_ref(x, ref["w_hat"])
+    check_y(ys, y_ref, f"split M={M} N={N} K={K}")
+    check_y(yw, y_ref, f"walk M={M} N={N} K={K}")
+    assert np.array_equal(host(ys).view(np.uint16), host(ys2).view(np.uint16))
+    d = np.abs(host(ys).astype(np.float64) - host(yw).astype(np.float64))
+    assert d.max() <= 1e-2 * max(1.0, np.abs(y_ref).max()), d.max()
 
 
 @pytest.mark.parametrize("M", [1, 16, 17, 33, 100, 130, 300])

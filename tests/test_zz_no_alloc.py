@@ -77,6 +77,8 @@ def check(y, x, ref):
     ((256, 4096, 4096, 4, 128, True), (64, 1000, 1024, 4, 128, True)),
     ((32, 8192, 8192, 4, 128, False), (8, 520, 2048, 3, 32, False)),
     ((300, 1000, 4128, 8, 32, True), (3, 256, 512, 4, 128, True)),
+    # decode batches whose activations exceed LDS: K-slab partials
+    ((16, 4104, 11008, 4, 128, False), (7, 100, 16384, 2, 64, False)),
 ])
 def test_noalloc_matches_linear_on_two_calls(first, second):
     ws = torch.empty((wq.noalloc_scratch_bytes(),), dtype=torch.uint8, device="cuda")

@@ -369,8 +369,8 @@ def scale_act(x, s, out=None):
 
 
 def workspace_size(M: int, N: int, K: int, bits: int, has_perm: bool) -> int:
-    """Bytes of workspace wq_gemm uses for these arguments (act-order gather
-    and split-K partials); 0 when none."""
+    """Bytes of workspace wq_gemv, wq_gemm and wq_linear use for these
+    arguments (act-order gather, split-K partials); 0 when none."""
     return int(lib().wq_workspace_size(M, N, K, bits, int(bool(has_perm))))
 
 
@@ -381,10 +381,10 @@ def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, o
     N = packed.shape[0]
     y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
         _dev(out, torch.float16, "out", 2, shape=(M, N), device=x.device)
-    # wq_linear may send act-order layers to the GEMM below gemv_max_m(); the
-    # gather workspace is then allocated either way (unused by the GEMV)
-    uses_gemm = entry == "wq_gemm" or (entry == "wq_linear" and (M > gemv_max_m() or perm is not None))
-    need = workspace_size(M, N, K, bits, perm is not None) if uses_gemm else 0
+    # one query sizes the GEMM's act-order gather and split-K partials and the
+    # decode kernel's K split (M <= 16, no act-order); the act-order GEMV
+    # uses no workspace
+    need = 0 if (entry == "wq_gemv" and perm is not None) else workspace_size(M, N, K, bits, perm is not None)
     ws_bytes = 0
     if need:
         if workspace is None:

@@ -436,10 +436,17 @@ static size_t gather_bytes(int M, int K, int has_perm) {
     return (size_t(M) * size_t(K) * 2 + 255) & ~size_t(255);
 }
 
+namespace wqh {
+size_t skinny_workspace_bytes(int M, int N, int K);
+}
+
 extern "C" size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t has_perm) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return 0;
-    return gather_bytes(M, K, has_perm) + split_bytes(M, N, K, bits);
+    const size_t gemm = gather_bytes(M, K, has_perm) + split_bytes(M, N, K, bits);
+    // the decode kernel's K split (M <= 16, no act-order)
+    const size_t gemv = has_perm ? 0 : wqh::skinny_workspace_bytes(M, N, K);
+    return std::max(gemm, gemv);
 }
 
 extern "C" wq_status wq_gemm(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,

@@ -928,7 +928,7 @@ wq_status launch_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* s
 namespace wqh {
 wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       const int32_t* perm, uint16_t* y, int M, int N, int K, int bits, int gs, hipStream_t s,
-                      const uint16_t* act_scale, const uint16_t* bias);
+                      const uint16_t* act_scale, const uint16_t* bias, void* workspace, size_t ws_bytes);
 wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* y,
                             int M, int N, int K, int bits, int group_size, int* gs_out);
 }
@@ -936,17 +936,18 @@ wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uin
 extern "C" wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                              const int32_t* perm, uint16_t* y, int32_t M, int32_t N, int32_t K, int32_t bits,
                              int32_t group_size, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     int gs = 0;
     const wq_status st = wqh::check_linear_args(x, packed, scales, y, M, N, K, bits, group_size, &gs);
     if (st != WQ_OK) return st;
     if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;  // read 16 bytes at a time
+    if (workspace && !wqh::aligned16(workspace)) return WQ_ERR_ARG;
     if (M > 16) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M >= WQ_SKINNY_MIN_M) {
-        const wq_status st2 = wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, nullptr, nullptr);
+        const wq_status st2 =
+            wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, nullptr, nullptr, workspace,
+                             workspace ? workspace_bytes : 0);
         if (st2 != WQ_ERR_UNSUPPORTED) return st2;
     }
     switch (bits) {
@@ -991,7 +992,8 @@ extern "C" wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!sl && M >= WQ_SKINNY_MIN_M) {  // the kernel wq_gemv uses for this M
-        const wq_status st2 = wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, act_scale, bias);
+        const wq_status st2 =
+            wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, act_scale, bias, nullptr, 0);
         if (st2 != WQ_ERR_UNSUPPORTED || M > 4) return st2;
     }
     switch (bits) {

@@ -1,7 +1,8 @@
 // wq_linear_noalloc: the batch-size dispatch of wq_linear with its scratch
 // memory (the act-order activation gather and the split-K fp32 partials of
-// the matrix-core GEMM) in a static device array instead of a caller
-// workspace, for callers that cannot allocate device memory.
+// the matrix-core GEMM, the K-slab partials of the decode kernel) in a
+// static device array instead of a caller workspace, for callers that
+// cannot allocate device memory.
 //
 // The array `scratch` is a file-scope __device__ variable: each GPU the
 // library runs on holds its own copy, at its own address, from the first
@@ -52,15 +53,18 @@ bool linear_uses_gemv(int M, bool act_order);
 extern "C" wq_status wq_linear_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                                        const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
                                        int32_t K, int32_t bits, int32_t group_size, void* stream) {
-    if (wqh::linear_uses_gemv(M, perm != nullptr))  // the decode kernels use no scratch
+    const bool decode = wqh::linear_uses_gemv(M, perm != nullptr);
+    if (decode && perm)  // the act-order decode kernel uses no scratch
         return wq_linear(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, nullptr, 0, stream);
-    if (M > 0 && K > 0 && gather_need(M, K, perm) > kScratchBytes) return WQ_ERR_TOO_LARGE;
+    if (!decode && M > 0 && K > 0 && gather_need(M, K, perm) > kScratchBytes) return WQ_ERR_TOO_LARGE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return WQ_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return WQ_ERR_UNSUPPORTED;
     void* ws = device_scratch(dev);
     if (!ws) return WQ_ERR_HIP;
-    // the split-K part takes what the gather leaves; with less room the GEMM
-    // splits K fewer ways (same result up to fp32 summation order)
+    // the GEMM's split-K part takes what the gather leaves (with less room
+    // it splits K fewer ways); the decode kernel puts its K-slab partials
+    // there (with too little room each block walks the slabs); either way
+    // the same result up to fp32 summation order
     return wq_linear(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, ws, kScratchBytes, stream);
 }

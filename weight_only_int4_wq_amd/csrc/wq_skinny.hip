@@ -138,7 +138,12 @@ struct SlabGeo {
 // Otherwise every weight is dequantized, fp16((q - z) s), before the product.
 // SLABS: K is cut into several slabs (without it the slab switch is compiled
 // out, which keeps the streaming loop's scalar state small).
-template <int BITS, int D, bool HAS_Z, bool EX, bool ZSUB, bool SLABS>
+// SPLIT: K is cut into slabs across blocks instead: the grid is one group of
+// blocks per slab, a block stages its slab once for its tiles and writes the
+// fp32 sums of that slab to part[slab][M][N] (bias and rounding are left to
+// skinny_sum_kernel).  No block changes slab, so no wavefront waits at a
+// slab change for activations queued behind the weight loads in flight.
+template <int BITS, int D, bool HAS_Z, bool EX, bool ZSUB, bool SLABS, bool SPLIT>
 __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_t* __restrict__ x,
                                                                  const uint32_t* __restrict__ packed,
                                                                  const uint16_t* __restrict__ scales,
@@ -146,7 +151,9 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
                                                                  uint16_t* __restrict__ y, int M, int N, int K,
                                                                  GroupDiv gd, int tpb, SlabGeo geo,
                                                                  const uint16_t* __restrict__ act_scale,
-                                                                 const uint16_t* __restrict__ bias) {
+                                                                 const uint16_t* __restrict__ bias,
+                                                                 float* __restrict__ part) {
+    static_assert(!(SLABS && SPLIT), "one slab per block in the split form");
     constexpr int WPB = kSkinnyWaves;
     constexpr int NT = 64 * WPB;
     extern __shared__ u4 smem[];
@@ -158,6 +165,10 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     const int KS = geo.KS, GSL = geo.GSL;
     const int KSc = KS / 32;                   // chunks per slab
     const int nslab = SLABS ? (CN + KSc - 1) / KSc : 1;
+    // SPLIT: block group s0 (bps blocks) takes slab s0 of every tile
+    const int bps = SPLIT ? int(gridDim.x) / ((CN + KSc - 1) / KSc) : int(gridDim.x);
+    const int s0 = SPLIT ? int(blockIdx.x) / bps : 0;
+    const int bix = int(blockIdx.x) - s0 * bps;
 
     // LDS: x rows [M][KS * 2 + 16 bytes], partials [2][WPB][64 lanes][4],
     // outputs [tpb][M][16] (fp32), the block's scales u16 [tpb * 16][GSL]
@@ -170,7 +181,7 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     uint8_t* szr = reinterpret_cast<uint8_t*>(ssc + size_t(tpb) * 16 * GSL);
 
     const int n_tiles = (N + 15) / 16;
-    const int t0 = blockIdx.x * tpb;
+    const int t0 = bix * tpb;
     const int T = max(0, min(tpb, n_tiles - t0));
     const int RB = max(0, min(T * 16, N - t0 * 16));  // rows of this block
 
@@ -179,8 +190,8 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     // step)
     auto slab_steps = [&](int s) { return (min(KSc, CN - s * KSc) + 7) / 8; };
     auto my_of = [&](int s) { return max(1, (slab_steps(s) - wave + WPB - 1) / WPB); };
-    const int my_first = my_of(0);
-    const int items = T * ((nslab - 1) * my_first + my_of(nslab - 1));
+    const int my_first = my_of(s0);
+    const int items = SPLIT ? T * my_first : T * ((nslab - 1) * my_first + my_of(nslab - 1));
 
     // the slab's first group and its number of groups
     auto slab_g0 = [&](int s) { return chunk_group(s * KSc, gd); };
@@ -192,15 +203,16 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     // j = t, t + NT, ... of every row; the first batch is j = t, rows below
     // XU (fewer with the division, whose temporaries would spill)
     constexpr int XU = EX ? 8 : 16;
-    const int KB0 = min(KS, K) / 8;  // real blocks per row in slab 0
+    const int kb0 = s0 * KS;               // first channel of the first slab
+    const int KB0 = min(KS, K - kb0) / 8;  // real blocks per row in it
     u4 xv[XU], xs0 = {0u, 0u, 0u, 0u};
     {
         const int j = min(int(threadIdx.x), KB0 - 1);
 #pragma unroll
         for (int u = 0; u < XU; ++u)
-            if (u < M) xv[u] = *reinterpret_cast<const u4*>(x + size_t(u) * K + 8 * j);
+            if (u < M) xv[u] = *reinterpret_cast<const u4*>(x + size_t(u) * K + kb0 + 8 * j);
         if constexpr (EX) {
-            if (act_scale) xs0 = *reinterpret_cast<const u4*>(act_scale + 8 * j);
+            if (act_scale) xs0 = *reinterpret_cast<const u4*>(act_scale + kb0 + 8 * j);
         }
     }
     // scale entries of the block's rows and a slab's groups: entry e is row
@@ -213,11 +225,11 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     };
     constexpr int SU = 8;
     uint32_t sv[SU], zv[SU];
-    const int ng0 = slab_ng(0);
+    const int ng0 = slab_ng(s0);
     const float inv0 = 1.0f / float(ng0);
     const int sc_n0 = RB * ng0;
     {
-        const int g0 = slab_g0(0);
+        const int g0 = slab_g0(s0);
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
             const size_t gi = sc_index(min(int(threadIdx.x) + NT * u, max(sc_n0 - 1, 0)), ng0, inv0, g0);
@@ -231,8 +243,8 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     uint32_t wr[D][2][BITS];
     // (the lane's row pointer and the step's first chunk are kept up to
     // date incrementally: the per-item work is two adds)
-    int is = 0, it = 0, ij = 0, ii = 0, imy = my_first;
-    int icb = 8 * wave;  // global chunk of the step's first 32-code chunk
+    int is = s0, it = 0, ij = 0, ii = 0, imy = my_first;
+    int icb = s0 * KSc + 8 * wave;  // global chunk of the step's first 32-code chunk
     auto row_ptr = [&](int t) {
         const int n = min((t0 + min(t, max(T - 1, 0))) * 16 + li, N - 1);
         return reinterpret_cast<const char*>(packed) + size_t(n) * CN * BITS * 4;
@@ -317,13 +329,13 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
             for (int u = 0; u < XU; ++u)
                 if (u < M) put_x(u, j, xv[u], xs0);
         }
-        stage_rest(0, j, j < KB0 ? XU : 0);
+        stage_rest(s0, j, j < KB0 ? XU : 0);
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
             const int e = int(threadIdx.x) + NT * u;
             if (e < sc_n0) put_sc(e, sv[u], HAS_Z ? zv[u] : 0u);
         }
-        stage_scales(0, int(threadIdx.x) + NT * SU);
+        stage_scales(s0, int(threadIdx.x) + NT * SU);
     }
     __syncthreads();
 
@@ -332,8 +344,8 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     // of matrix instructions
     f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
     const char* xrow = lds + size_t(min(li, M - 1)) * xrs;
-    int cs = 0, ct = 0, cj = 0, cmy = my_first, te = 0;  // compute cursor, tile ends so far
-    int css8 = 8 * slab_steps(0), cg0 = slab_g0(0), cng = ng0;
+    int cs = s0, ct = 0, cj = 0, cmy = my_first, te = 0;  // compute cursor, tile ends so far
+    int css8 = 8 * slab_steps(s0), cg0 = slab_g0(s0), cng = ng0;
     int ccb = 8 * wave;                                   // the step's first chunk within the slab
     int srow = min(li, RB - 1) * cng;                     // this lane's row in ssc / szr
     auto tile_end = [&](f4 v) {
@@ -353,7 +365,7 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
 #pragma unroll
             for (int w = 0; w < WPB; ++w) sum += src[w * 256];
             float* dst = outb + (ct * M + m) * 16 + nn;
-            *dst = cs == 0 ? sum : *dst + sum;
+            *dst = (SPLIT || cs == 0) ? sum : *dst + sum;
         }
         ++te;
     };
@@ -469,11 +481,29 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
         const int m = r >> 4, n = (t0 + tord) * 16 + (r & 15);
         if (n < N) {
             float v = outb[o];
-            if constexpr (EX) {
-                if (bias) v += float(__builtin_bit_cast(_Float16, bias[n]));
+            if constexpr (SPLIT) {
+                part[(size_t(s0) * M + m) * N + n] = v;
+            } else {
+                if constexpr (EX) {
+                    if (bias) v += float(__builtin_bit_cast(_Float16, bias[n]));
+                }
+                y[size_t(m) * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
             }
-            y[size_t(m) * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
         }
+    }
+}
+
+// y[m][n] = fp16(sum over slabs s of part[s][m][n] (+ bias[n])), the slabs
+// added in order, as the block-serial form accumulates them.
+__global__ void __launch_bounds__(256) skinny_sum_kernel(const float* __restrict__ part, int nsl, int M, int N,
+                                                         const uint16_t* __restrict__ bias,
+                                                         uint16_t* __restrict__ y) {
+    const size_t MN = size_t(M) * N;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < MN; i += size_t(gridDim.x) * blockDim.x) {
+        float v = part[i];
+        for (int sl = 1; sl < nsl; ++sl) v += part[size_t(sl) * MN + i];
+        if (bias) v += float(__builtin_bit_cast(_Float16, bias[i % size_t(N)]));
+        y[i] = __builtin_bit_cast(uint16_t, (_Float16)v);
     }
 }
 
@@ -488,56 +518,127 @@ static size_t skinny_lds(int M, int KS, int tpb, int GSL) {
            size_t(tpb) * 16 * GSL * 3;
 }
 
-// Launch the skinny kernel; WQ_ERR_UNSUPPORTED when it does not apply
-// (act-order, M outside 1..16, K below 256).
-wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                      const int32_t* perm, uint16_t* y, int M, int N, int K, int bits, int gs, hipStream_t s,
-                      const uint16_t* act_scale, const uint16_t* bias) {
-    if (perm || M < 1 || M > 16 || K < 256) return WQ_ERR_UNSUPPORTED;
-    int dev = 0, cus = 256, lds_max = 64 * 1024;
+// Launch geometry of the skinny kernel.
+struct SkinnyPlan {
+    int blocks = 0, tpb = 0, nsl = 1;  // nsl: slabs of the split form (1: not split)
+    SlabGeo geo{0, 0};
+    size_t lds = 0;
+    size_t part_bytes = 0;  // fp32 partials of the split form
+};
+
+// Plan for cus compute units and lds_max bytes of LDS per block; the split
+// form is taken when K needs several slabs and ws_bytes holds its partials.
+// false when no geometry fits.
+static bool skinny_plan(int M, int N, int K, int gs, int cus, int lds_max, size_t ws_bytes, SkinnyPlan& p) {
+    const int n_tiles = (N + 15) / 16;
+    const int Kp = (K + 255) / 256 * 256;
+    const int G = (K + gs - 1) / gs;
+    // one slab: every block stages all of K once
+    p.blocks = std::min(n_tiles, cus);
+    p.tpb = (n_tiles + p.blocks - 1) / p.blocks;
+    if (skinny_lds(M, Kp, p.tpb, G) <= size_t(lds_max)) {
+        p.geo = SlabGeo{Kp, G};
+        p.lds = skinny_lds(M, Kp, p.tpb, G);
+        return true;
+    }
+    // K in slabs of KS channels (a multiple of 256); groups per slab at most
+    // KS / gs + 1 (+ 1 for a group cut by the slab's start)
+    auto slab_of = [&](int nslab) { return ((Kp / 256 + nslab - 1) / nslab) * 256; };
+    // split form: nsl groups of bps blocks, group s taking slab s of every
+    // tile, fewest slabs that fit
+    for (int nslab = 2; nslab <= Kp / 256; ++nslab) {
+        const int KS = slab_of(nslab);
+        const int nsl = (K + KS - 1) / KS;  // slabs this slab size gives
+        const int bps = std::max(1, cus / nsl);
+        const int tpb = (n_tiles + bps - 1) / bps;
+        const int GSL = std::min(G, KS / gs + 2);
+        if (skinny_lds(M, KS, tpb, GSL) > size_t(lds_max)) continue;
+        const size_t need = size_t(nsl) * size_t(M) * size_t(N) * 4;
+        if (need > ws_bytes) break;
+        p.blocks = bps * nsl;
+        p.tpb = tpb;
+        p.nsl = nsl;
+        p.geo = SlabGeo{KS, GSL};
+        p.lds = skinny_lds(M, KS, tpb, GSL);
+        p.part_bytes = need;
+        return true;
+    }
+    // without the workspace: each block walks the slabs in turn
+    for (int nslab = 2; nslab <= Kp / 256; ++nslab) {
+        const int KS = slab_of(nslab);
+        const int GSL = std::min(G, KS / gs + 2);
+        if (skinny_lds(M, KS, p.tpb, GSL) <= size_t(lds_max)) {
+            p.geo = SlabGeo{KS, GSL};
+            p.lds = skinny_lds(M, KS, p.tpb, GSL);
+            return true;
+        }
+    }
+    return false;
+}
+
+// Compute units and LDS bytes per block of the current device.
+static void skinny_device(int& cus, int& lds_max) {
+    int dev = 0;
+    cus = 256;
+    lds_max = 64 * 1024;
     if (hipGetDevice(&dev) == hipSuccess) {
         int v = 0;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
             lds_max = v;
     }
-    const int n_tiles = (N + 15) / 16;
-    const int blocks = std::min(n_tiles, cus);
-    const int tpb = (n_tiles + blocks - 1) / blocks;
-    // fewest slabs that fit: KS a multiple of 256, groups per slab at most
-    // KS / gs + 1 (+ 1 for a group cut by the slab's start)
-    const int Kp = (K + 255) / 256 * 256;
-    const int G = (K + gs - 1) / gs;
-    SlabGeo geo{0, 0};
-    for (int nslab = 1; nslab <= Kp / 256; ++nslab) {
-        const int KS = ((Kp / 256 + nslab - 1) / nslab) * 256;
-        const int GSL = nslab == 1 ? G : std::min(G, KS / gs + 2);
-        if (skinny_lds(M, KS, tpb, GSL) <= size_t(lds_max)) {
-            geo = SlabGeo{KS, GSL};
-            break;
-        }
-    }
-    if (geo.KS == 0) return WQ_ERR_UNSUPPORTED;
-    const size_t lds = skinny_lds(M, geo.KS, tpb, geo.GSL);
+}
+
+// Workspace bytes the skinny kernel's split form may use for M x N x K on
+// the current device, for any group size (group size 32 has the most scale
+// entries per slab, so it needs the most slabs); 0 when K fits in one slab.
+size_t skinny_workspace_bytes(int M, int N, int K) {
+    if (M < 1 || M > 16 || K < 256 || N < 1) return 0;
+    int cus = 0, lds_max = 0;
+    skinny_device(cus, lds_max);
+    SkinnyPlan p;
+    if (!skinny_plan(M, N, K, 32, cus, lds_max, ~size_t(0), p)) return 0;
+    return p.part_bytes;
+}
+
+// Launch the skinny kernel; WQ_ERR_UNSUPPORTED when it does not apply
+// (act-order, M outside 1..16, K below 256).  workspace (nullable,
+// ws_bytes): room for the split form's fp32 partials.
+wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                      const int32_t* perm, uint16_t* y, int M, int N, int K, int bits, int gs, hipStream_t s,
+                      const uint16_t* act_scale, const uint16_t* bias, void* workspace, size_t ws_bytes) {
+    if (perm || M < 1 || M > 16 || K < 256) return WQ_ERR_UNSUPPORTED;
+    int cus = 0, lds_max = 0;
+    skinny_device(cus, lds_max);
+    SkinnyPlan plan;
+    if (!skinny_plan(M, N, K, gs, cus, lds_max, workspace ? ws_bytes : 0, plan)) return WQ_ERR_UNSUPPORTED;
     const GroupDiv gd = group_magic(gs);
     const bool zsub = gs % 128 == 0;
-    const bool slabs = geo.KS < K;
+    const bool split = plan.nsl > 1;
+    const bool slabs = !split && plan.geo.KS < K;
+    float* part = split ? static_cast<float*>(workspace) : nullptr;
     constexpr int D = WQ_SKINNY_D;
     auto go = [&](auto kern) {
-        if (lds > 64 * 1024)
+        if (plan.lds > 64 * 1024)
             (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      int(lds));
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kSkinnyWaves), lds, s, x, packed, scales, zeros, y, M, N, K,
-                           gd, tpb, geo, act_scale, bias);
+                                      int(plan.lds));
+        hipLaunchKernelGGL(kern, dim3(plan.blocks), dim3(64 * kSkinnyWaves), plan.lds, s, x, packed, scales, zeros, y,
+                           M, N, K, gd, plan.tpb, plan.geo, act_scale, bias, part);
+        wq_status st = launch_status();
+        if (st != WQ_OK || !split) return st;
+        const size_t MN = size_t(M) * N;
+        const int sb = int(std::min<size_t>((MN + 255) / 256, size_t(cus) * 8));
+        hipLaunchKernelGGL(skinny_sum_kernel, dim3(sb), dim3(256), 0, s, part, plan.nsl, M, N, bias, y);
         return launch_status();
     };
     const bool ex = act_scale || bias;
-    // pick the instantiation: bits, zero-points, fused epilogue, ZSUB, slabs
+    // pick the instantiation: bits, zero-points, fused epilogue, ZSUB, slab form
     auto pick = [&](auto bits_c) -> wq_status {
         constexpr int B = decltype(bits_c)::value;
         auto by_slab = [&](auto z_c, auto ex_c, auto zs_c) -> wq_status {
             constexpr bool Z = decltype(z_c)::value, E = decltype(ex_c)::value, F = decltype(zs_c)::value;
-            return slabs ? go(skinny_kernel<B, D, Z, E, F, true>) : go(skinny_kernel<B, D, Z, E, F, false>);
+            if (split) return go(skinny_kernel<B, D, Z, E, F, false, true>);
+            return slabs ? go(skinny_kernel<B, D, Z, E, F, true, false>) : go(skinny_kernel<B, D, Z, E, F, false, false>);
         };
         auto by_zsub = [&](auto z_c, auto ex_c) -> wq_status {
             return zsub ? by_slab(z_c, ex_c, std::true_type{}) : by_slab(z_c, ex_c, std::false_type{});
