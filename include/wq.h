@@ -256,7 +256,7 @@ wq_status wq_scale_act(const uint16_t* x, const uint16_t* s, int32_t M, int32_t 
  * when the launch has too few output tiles to fill the GPU, fp32 partial
  * outputs of a K split (splits*M*N floats; the split count is chosen on the
  * host from the shape and the number of compute units).  wq_gemv at
- * 2 <= M <= 16 without act-order, when M rows of K activations do not fit
+ * 2 <= M <= 32 without act-order, when M rows of K activations do not fit
  * in LDS at once: fp32 partial outputs of its K slabs (slabs*M*N floats,
  * sized here for the group size with the most groups).  The act-order part
  * is required; the split parts are optional: with less workspace the
@@ -272,12 +272,14 @@ size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t 
  * ("AutoAWQ vs The Stack v2" and "AutoAWQ vs Unsloth", WQLinear_*
  * paragraphs).
  *
- * wq_gemv: the decode kernels for M <= 16 (returns WQ_ERR_UNSUPPORTED
- *   above).  M = 1 (and act-order layers): streams the packed words with
+ * wq_gemv: the decode kernels for M <= 16, and for 17 <= M <= 32 without
+ *   act-order and with K >= 256 (returns WQ_ERR_UNSUPPORTED otherwise).
+ *   M = 1 (and act-order layers): streams the packed words with
  *   128-bit loads, unpacks in registers, accumulates with fp16-pair dot
  *   products into fp32 and reduces the split-K partial sums across the
- *   wavefront.  2 <= M <= 16 without act-order: one pass over the weights
- *   with the products on fp16 matrix-core instructions (16 x 16 x 32), the
+ *   wavefront.  2 <= M <= 32 without act-order: one pass over the weights
+ *   with the products on fp16 matrix-core instructions (16 x 16 x 32; two
+ *   per weight fragment from 17 rows), the
  *   activations staged in LDS; when M rows of K do not fit, K is cut into
  *   slabs, one group of blocks per slab with the workspace (then a second
  *   kernel adds the slabs' fp32 partials in slab order), or each block
@@ -286,7 +288,8 @@ size_t wq_workspace_size(int32_t M, int32_t N, int32_t K, int32_t bits, int32_t 
  *   fp16 and feeds fp16 matrix-core (MFMA) instructions with fp32
  *   accumulators.
  * wq_linear: picks wq_gemv for M <= wq_gemv_max_m() (16; with act-order,
- *   M <= 4) and wq_gemm otherwise (the batch-size dispatch).
+ *   M <= 4), and for 17 <= M <= 24 without act-order when M * K <= 24 * 8192
+ *   and K >= 256, and wq_gemm otherwise (the batch-size dispatch).
  *
  * workspace: device memory of wq_workspace_size(M, N, K, bits, perm != NULL)
  * bytes (16-byte aligned), or NULL when that size is 0; WQ_ERR_ARG if
@@ -359,7 +362,8 @@ wq_status wq_gemv_silu_mul(const uint16_t* x, const uint32_t* packed, const uint
  * before its rounding.  silu = 0: y fp16 [M][N] = x' . dequant(Wq)^T + bias.
  * silu = 1: the stacked gate/up layout of wq_gemv_silu_mul (N even), y fp16
  * [M][N/2] = silu(g + bias[j]) * (u + bias[j + N/2]).  Other arguments as
- * wq_gemv.  silu = 0: 1 <= M <= 16 (act-order: M <= 4); silu = 1:
+ * wq_gemv.  silu = 0: 1 <= M <= 16 (act-order: M <= 4), and up to 32
+ * without act-order for K >= 256 (the matrix-core kernel); silu = 1:
  * 1 <= M <= 4 and fp16 x of K within the 64 KB staging budget (K <= 16384
  * at M = 1); else WQ_ERR_UNSUPPORTED. */
 wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
@@ -377,8 +381,9 @@ wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const uint16_t* 
  * pointers or a size that is not a multiple of 16; asynchronous. */
 wq_status wq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
-/* Largest M that wq_linear sends to wq_gemv (16; layers with act-order go
- * to wq_gemm from M = 5). */
+/* Largest M that wq_linear always sends to wq_gemv (16; layers with
+ * act-order go to wq_gemm from M = 5; 17 <= M <= 24 go to wq_gemv too when
+ * M * K <= 24 * 8192, K >= 256 and there is no act-order). */
 int32_t wq_gemv_max_m(void);
 
 #ifdef __cplusplus

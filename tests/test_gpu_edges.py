@@ -78,7 +78,7 @@ def int_activations(seed, M, K, lo=-4, hi=4):
     return g.integers(lo, hi + 1, size=(M, K)).astype(np.float16)
 
 
-GEMV_MS = (1, 2, 3, 4, 8, 16)
+GEMV_MS = (1, 2, 3, 4, 8, 16, 32)
 GEMM_MS = (1, 17, 64, 130)
 
 
@@ -86,7 +86,10 @@ def products(x_ms, L, bits, gs):
     """(kernel, M, y) for every kernel and row count that applies."""
     out = []
     for M, x in x_ms.items():
-        kernels = (["gemv"] if M <= 16 else []) + ["gemm", "linear"]
+        # the decode kernels take up to 16 rows, and up to 32 on the
+        # matrix-core kernel (no act-order, K of at least 256)
+        skinny = L["perm"] is None and x.shape[1] >= 256
+        kernels = (["gemv"] if M <= 16 or (M <= 32 and skinny) else []) + ["gemm", "linear"]
         for k in kernels:
             fn = {"gemv": wq.gemv, "gemm": wq.gemm, "linear": wq.linear}[k]
             out.append((k, M, fn(dev(x), L["packed"], L["scales"], L["zeros"], bits, gs, perm=L["perm"])))

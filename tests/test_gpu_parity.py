@@ -184,7 +184,8 @@ def test_gemv_ragged_shapes(M, N, K):
     check_y(run("gemv", x, L, 4, gs), O.linear_ref(x, ref["w_hat"]), f"gemv M={M} N={N} K={K}")
 
 
-# Batches of 2..16 rows run on the matrix-core decode kernel: every code
+# Batches of 2..32 rows run on the matrix-core decode kernel (from 17 rows
+# with a second 16-row activation fragment per weight fragment): every code
 # width and group form, K long enough that at M = 16 the activations are
 # staged in several K-slabs, and K below eight 256-channel steps (masked
 # steps on the idle wavefronts).
@@ -193,7 +194,7 @@ SKINNY_CASES = [(2, 32, True, 40, 8192), (3, 128, False, 70, 8448), (8, -1, True
                 (8, 128, False, 17, 1280)]
 
 
-@pytest.mark.parametrize("M", [2, 7, 16])
+@pytest.mark.parametrize("M", [2, 7, 16, 17, 32])
 @pytest.mark.parametrize("bits,gs,sym,N,K", SKINNY_CASES)
 def test_skinny_formats_and_slabs(M, bits, gs, sym, N, K):
     seed = (109, bits, gs % 997, N, K, M)
@@ -214,7 +215,8 @@ def test_skinny_formats_and_slabs(M, bits, gs, sym, N, K):
 
 
 @pytest.mark.parametrize("M,bits,gs,sym,N,K", [(16, 4, 128, False, 100, 11008), (7, 3, 32, True, 70, 28672),
-                                               (16, 2, 64, True, 4104, 8448), (9, 8, -1, True, 33, 16384)])
+                                               (16, 2, 64, True, 4104, 8448), (9, 8, -1, True, 33, 16384),
+                                               (32, 4, 128, False, 300, 8192), (23, 3, 32, True, 70, 4352)])
 def test_skinny_slab_split_matches_walk(M, bits, gs, sym, N, K):
     # M rows of K too long for LDS: with the workspace each K-slab goes to
     # its own group of blocks (fp32 partials, then summed in slab order);
@@ -323,11 +325,19 @@ def test_dispatch_follows_batch_size():
     w = I.weights(seed, N, K, 0.02)
     L = gpu_layer(w, 4, 128)
     mmax = wq.gemv_max_m()
-    for M, kernel in ((1, "gemv"), (mmax, "gemv"), (mmax + 1, "gemm"), (64, "gemm")):
+    # 17..24 rows stay on the decode kernel while M * K <= 24 * 8192
+    for M, kernel in ((1, "gemv"), (mmax, "gemv"), (mmax + 1, "gemv"), (24, "gemv"), (25, "gemm"), (64, "gemm")):
         x = I.activations(seed, M, K)
         a = host(run("linear", x, L, 4, 128))
         b = host(run(kernel, x, L, 4, 128))
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (M, kernel)
+    K2 = 16384
+    L2 = gpu_layer(I.weights(seed, 64, K2, 0.02), 4, 128)
+    for M, kernel in ((16, "gemv"), (17, "gemm")):
+        x = I.activations(seed, M, K2)
+        a = host(run("linear", x, L2, 4, 128))
+        b = host(run(kernel, x, L2, 4, 128))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (M, K2, kernel)
 
 
 def test_empty_problems():
@@ -394,7 +404,7 @@ def test_prefill_awq_gemm_sampled():
 @pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192), (8192, 10240)])
 def test_70b_layer_shapes_sampled(K, N):
     sampled_check((4, K, N), K, N, 0.015, (1, 8, 32, 512),
-                  lambda M: ("linear", "gemv", "gemm") if M <= 16 else ("linear", "gemm"))
+                  lambda M: ("linear", "gemv", "gemm") if M <= 32 else ("linear", "gemm"))
 
 
 # ------------------------------------------------------------ AWQ search ----

@@ -382,7 +382,7 @@ def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, o
     y = torch.empty((M, N), dtype=torch.float16, device=x.device) if out is None else \
         _dev(out, torch.float16, "out", 2, shape=(M, N), device=x.device)
     # one query sizes the GEMM's act-order gather and split-K partials and the
-    # decode kernel's K split (M <= 16, no act-order); the act-order GEMV
+    # decode kernel's K split (M <= 32, no act-order); the act-order GEMV
     # uses no workspace
     need = 0 if (entry == "wq_gemv" and perm is not None) else workspace_size(M, N, K, bits, perm is not None)
     ws_bytes = 0
@@ -400,7 +400,7 @@ def _matmul(entry: str, x, packed, scales, zeros, bits, group_size, perm=None, o
 
 
 def gemv(x, packed, scales, zeros, bits: int, group_size: int, perm=None, out=None, workspace=None):
-    """Decode kernel, 1 <= M <= 16."""
+    """Decode kernel, 1 <= M <= 16; up to 32 without act-order for K >= 256."""
     return _matmul("wq_gemv", x, packed, scales, zeros, bits, group_size, perm, out, workspace)
 
 

@@ -14,13 +14,28 @@ namespace {
 // ones; at M = 4 the gap is wider.  Act-order layers take the skinny kernel's
 // vector-ALU fallback, whose cost grows with M, so from M = 5 they go to the
 // GEMM, whose activation copy applies the gather.
-constexpr int kGemvMaxM = 16;
+#ifndef WQ_GEMV_MAX_M
+#define WQ_GEMV_MAX_M 16
+#endif
+constexpr int kGemvMaxM = WQ_GEMV_MAX_M;
 constexpr int kGemvMaxMActOrder = 4;
+// From 17 rows the skinny kernel feeds every decoded weight fragment to two
+// matrix instructions and reads twice the activation fragments from LDS,
+// and M rows of K activations need more K-slabs.  Measured against the
+// tiled GEMM (MI355X, 4-bit, group 128, the seven Llama decode and 70B
+// shapes): faster at 17 and 24 rows while M * K <= 24 * 8192 (1.02-1.32x),
+// slower past that (24 x 11008: 0.94x, 17 x 28672: 0.91x) and at 32 rows on
+// every shape (0.44-0.85x).
+constexpr int kSkinnyWideMaxM = 24;
+constexpr long long kSkinnyWideMaxMK = 24LL * 8192;
 }  // namespace
 
 namespace wqh {
 
-bool linear_uses_gemv(int M, bool act_order) { return M <= (act_order ? kGemvMaxMActOrder : kGemvMaxM); }
+bool linear_uses_gemv(int M, int K, bool act_order) {
+    if (M <= (act_order ? kGemvMaxMActOrder : kGemvMaxM)) return true;
+    return !act_order && M <= kSkinnyWideMaxM && K >= 256 && (long long)M * K <= kSkinnyWideMaxMK;
+}
 
 wq_status check_linear_args(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* y,
                             int M, int N, int K, int bits, int group_size, int* gs_out) {
@@ -59,7 +74,7 @@ extern "C" wq_status wq_linear(const uint16_t* x, const uint32_t* packed, const 
                                const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
                                int32_t K, int32_t bits, int32_t group_size, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    if (wqh::linear_uses_gemv(M, perm != nullptr))
+    if (wqh::linear_uses_gemv(M, K, perm != nullptr))
         return wq_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, workspace, workspace_bytes,
                        stream);
     return wq_gemm(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, workspace, workspace_bytes, stream);

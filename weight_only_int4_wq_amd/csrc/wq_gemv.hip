@@ -941,14 +941,15 @@ extern "C" wq_status wq_gemv(const uint16_t* x, const uint32_t* packed, const ui
     if (st != WQ_OK) return st;
     if (perm && !wqh::aligned16(perm)) return WQ_ERR_ARG;  // read 16 bytes at a time
     if (workspace && !wqh::aligned16(workspace)) return WQ_ERR_ARG;
-    if (M > 16) return WQ_ERR_UNSUPPORTED;
+    if (M > 32) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (M >= WQ_SKINNY_MIN_M) {
         const wq_status st2 =
             wqh::skinny_gemv(x, packed, scales, zeros, perm, y, M, N, K, bits, gs, s, nullptr, nullptr, workspace,
                              workspace ? workspace_bytes : 0);
-        if (st2 != WQ_ERR_UNSUPPORTED) return st2;
+        // the vector-ALU kernels below take at most 16 rows
+        if (st2 != WQ_ERR_UNSUPPORTED || M > 16) return st2;
     }
     switch (bits) {
         case 2: return launch_bits<2>(x, packed, scales, zeros, perm, y, M, N, K, gs, s);
@@ -988,7 +989,7 @@ extern "C" wq_status wq_gemv_ex(const uint16_t* x, const uint32_t* packed, const
     if (silu && N % 2) return WQ_ERR_ARG;
     if (act_scale && !wqh::aligned16(act_scale)) return WQ_ERR_ARG;
     const bool sl = silu != 0;
-    if (M > 16 || (sl && M > 4)) return WQ_ERR_UNSUPPORTED;
+    if (M > 32 || (sl && M > 4)) return WQ_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!sl && M >= WQ_SKINNY_MIN_M) {  // the kernel wq_gemv uses for this M

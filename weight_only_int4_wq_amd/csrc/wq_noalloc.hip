@@ -47,13 +47,13 @@ size_t gather_need(int32_t M, int32_t K, const int32_t* perm) {
 }  // namespace
 
 namespace wqh {
-bool linear_uses_gemv(int M, bool act_order);
+bool linear_uses_gemv(int M, int K, bool act_order);
 }
 
 extern "C" wq_status wq_linear_noalloc(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
                                        const uint8_t* zeros, const int32_t* perm, uint16_t* y, int32_t M, int32_t N,
                                        int32_t K, int32_t bits, int32_t group_size, void* stream) {
-    const bool decode = wqh::linear_uses_gemv(M, perm != nullptr);
+    const bool decode = wqh::linear_uses_gemv(M, K, perm != nullptr);
     if (decode && perm)  // the act-order decode kernel uses no scratch
         return wq_linear(x, packed, scales, zeros, perm, y, M, N, K, bits, group_size, nullptr, 0, stream);
     if (!decode && M > 0 && K > 0 && gather_need(M, K, perm) > kScratchBytes) return WQ_ERR_TOO_LARGE;

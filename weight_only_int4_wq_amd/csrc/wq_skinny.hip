@@ -1,4 +1,4 @@
-// Skinny matrix-core kernel for small batches (2 <= M <= 16):
+// Skinny matrix-core kernel for small batches (2 <= M <= 32):
 // y[M][N] = x[M][K] . dequant(Wq)^T with the weights streamed once from HBM.
 //
 // A batch of a few tokens is still bound by the weight stream (at M = 16 the
@@ -12,7 +12,9 @@
 // One v_mfma_f32_16x16x32_f16 multiplies a 16 x 32 activation fragment by a
 // 32 x 16 weight fragment.  Lane l supplies activation row l % 16 (rows at
 // or past M repeat the last real row; their outputs are discarded) and
-// weight row n0 + l % 16, both at k-block l / 16 of the 32.  A lane's 16-byte
+// weight row n0 + l % 16, both at k-block l / 16 of the 32.  With 17 to 32
+// rows (MF = 2) every decoded weight fragment feeds a second instruction for
+// activation rows 16..31.  A lane's 16-byte
 // load holds one 32-code chunk, i.e. four k-blocks: it feeds four
 // instructions, the k-blocks of four consecutive chunks spread over the four
 // lane groups.  One wavefront load instruction therefore reads 16 rows x 64
@@ -52,6 +54,8 @@ using namespace wq;
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 
 constexpr int kSkinnyWaves = 8;
+// Most activation rows the kernel takes (two 16-row fragments).
+constexpr int kSkinnyMaxM = 32;
 
 // weight loads in flight per lane, in steps of two 16-byte chunks
 #ifndef WQ_SKINNY_D
@@ -143,7 +147,8 @@ struct SlabGeo {
 // fp32 sums of that slab to part[slab][M][N] (bias and rounding are left to
 // skinny_sum_kernel).  No block changes slab, so no wavefront waits at a
 // slab change for activations queued behind the weight loads in flight.
-template <int BITS, int D, bool HAS_Z, bool EX, bool ZSUB, bool SLABS, bool SPLIT>
+// MF: 16-row activation fragments per weight fragment (M <= 16 * MF).
+template <int BITS, int D, bool HAS_Z, bool EX, bool ZSUB, bool SLABS, bool SPLIT, int MF>
 __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_t* __restrict__ x,
                                                                  const uint32_t* __restrict__ packed,
                                                                  const uint16_t* __restrict__ scales,
@@ -170,13 +175,13 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     const int s0 = SPLIT ? int(blockIdx.x) / bps : 0;
     const int bix = int(blockIdx.x) - s0 * bps;
 
-    // LDS: x rows [M][KS * 2 + 16 bytes], partials [2][WPB][64 lanes][4],
+    // LDS: x rows [M][KS * 2 + 16 bytes], partials [2][WPB][MF][64 lanes][4],
     // outputs [tpb][M][16] (fp32), the block's scales u16 [tpb * 16][GSL]
     // and zero-points u8 [tpb * 16][GSL] of the current slab
     const int xrs = KS * 2 + 16;
     char* lds = reinterpret_cast<char*>(smem);
     float* red = reinterpret_cast<float*>(lds + size_t(M) * xrs);
-    float* outb = red + 2 * WPB * 256;
+    float* outb = red + 2 * WPB * 256 * MF;
     uint16_t* ssc = reinterpret_cast<uint16_t*>(outb + size_t(tpb) * M * 16);
     uint8_t* szr = reinterpret_cast<uint8_t*>(ssc + size_t(tpb) * 16 * GSL);
 
@@ -342,28 +347,35 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     // ---- stream
     // two accumulators (one per chunk of a step) halve the dependent chain
     // of matrix instructions
-    f4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-    const char* xrow = lds + size_t(min(li, M - 1)) * xrs;
+    f4 acc[MF], acc2[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) acc[f] = acc2[f] = f4{0.f, 0.f, 0.f, 0.f};
+    const char* xrow[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) xrow[f] = lds + size_t(min(li + 16 * f, M - 1)) * xrs;
     int cs = s0, ct = 0, cj = 0, cmy = my_first, te = 0;  // compute cursor, tile ends so far
     int css8 = 8 * slab_steps(s0), cg0 = slab_g0(s0), cng = ng0;
     int ccb = 8 * wave;                                   // the step's first chunk within the slab
     int srow = min(li, RB - 1) * cng;                     // this lane's row in ssc / szr
-    auto tile_end = [&](f4 v) {
-        float* mine = red + ((te & 1) * WPB + wave) * 256 + lane * 4;
-        *reinterpret_cast<f4*>(mine) = v;
+    auto tile_end = [&](const f4 (&v)[MF]) {
+#pragma unroll
+        for (int f = 0; f < MF; ++f) {
+            float* mine = red + (((te & 1) * WPB + wave) * MF + f) * 256 + lane * 4;
+            *reinterpret_cast<f4*>(mine) = v[f];
+        }
         // workgroup barrier: its fences wait for LDS only (weight loads in
         // flight stay in flight), and the compiler keeps its own count of
         // those loads across it
         __syncthreads();
-        // output (m, n): lane 16 (m / 4) + n, element m % 4 of each partial;
-        // thread o always owns the same outputs, so the slabs add up without
-        // further synchronization
+        // output (m, n): fragment m / 16, lane 16 (m % 16 / 4) + n, element
+        // m % 4 of each partial; thread o always owns the same outputs, so the
+        // slabs add up without further synchronization
         for (int o = threadIdx.x; o < M * 16; o += NT) {
-            const int m = o >> 4, nn = o & 15;
-            const float* src = red + (te & 1) * WPB * 256 + (16 * (m >> 2) + nn) * 4 + (m & 3);
+            const int m = o >> 4, nn = o & 15, f = m >> 4, mm = m & 15;
+            const float* src = red + ((te & 1) * WPB * MF + f) * 256 + (16 * (mm >> 2) + nn) * 4 + (mm & 3);
             float sum = 0.f;
 #pragma unroll
-            for (int w = 0; w < WPB; ++w) sum += src[w * 256];
+            for (int w = 0; w < WPB; ++w) sum += src[w * 256 * MF];
             float* dst = outb + (ct * M + m) * 16 + nn;
             *dst = (SPLIT || cs == 0) ? sum : *dst + sum;
         }
@@ -387,9 +399,11 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
             const uint32_t zo = BITS == 4 ? (0x5400u + (z << 4)) * 0x10001u : ze;
             uint32_t h[16];
             decode_pairs<BITS>(wr[d][p], h);
-            f4& a = p == 0 ? acc : acc2;
+            f4 (&a)[MF] = p == 0 ? acc : acc2;
             if constexpr (ZSUB) {
-                f4 cp = {0.f, 0.f, 0.f, 0.f};
+                f4 cp[MF];
+#pragma unroll
+                for (int f = 0; f < MF; ++f) cp[f] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     u4 bv;
@@ -397,12 +411,17 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
                     bv.y = as_u32(as_h2(h[4 * q + 1]) - as_h2(zo));
                     bv.z = as_u32(as_h2(h[4 * q + 2]) - as_h2(ze));
                     bv.w = as_u32(as_h2(h[4 * q + 3]) - as_h2(zo));
-                    const h8v av = *reinterpret_cast<const h8v*>(xrow + 64 * cl + 16 * q);
-                    cp = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), cp, 0, 0, 0);
+#pragma unroll
+                    for (int f = 0; f < MF; ++f) {
+                        const h8v av = *reinterpret_cast<const h8v*>(xrow[f] + 64 * cl + 16 * q);
+                        cp[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), cp[f], 0, 0, 0);
+                    }
                 }
                 const float sf = float(__builtin_bit_cast(_Float16, uint16_t(sr_)));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf(sf, cp[r], a[r]);
+                for (int f = 0; f < MF; ++f)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[f][r] = __builtin_fmaf(sf, cp[f][r], a[f][r]);
             } else {
                 const uint32_t ss = scale_pair(uint16_t(sr_));
 #pragma unroll
@@ -412,9 +431,12 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
                     bv.y = as_u32((as_h2(h[4 * q + 1]) - as_h2(zo)) * as_h2(ss));
                     bv.z = as_u32((as_h2(h[4 * q + 2]) - as_h2(ze)) * as_h2(ss));
                     bv.w = as_u32((as_h2(h[4 * q + 3]) - as_h2(zo)) * as_h2(ss));
-                    // x fragment: row li, k = 32 cl + 8 q (the lane group's chunk)
-                    const h8v av = *reinterpret_cast<const h8v*>(xrow + 64 * cl + 16 * q);
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), a, 0, 0, 0);
+                    // x fragment: row li (+ 16 f), k = 32 cl + 8 q (the lane group's chunk)
+#pragma unroll
+                    for (int f = 0; f < MF; ++f) {
+                        const h8v av = *reinterpret_cast<const h8v*>(xrow[f] + 64 * cl + 16 * q);
+                        a[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8v, bv), a[f], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -425,9 +447,13 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_kernel(const uint16_
     auto advance = [&]() {
         ccb += 8 * WPB;
         if (++cj == cmy) {
-            tile_end(acc + acc2);
-            acc = f4{0.f, 0.f, 0.f, 0.f};
-            acc2 = f4{0.f, 0.f, 0.f, 0.f};
+            f4 v[MF];
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+                v[f] = acc[f] + acc2[f];
+                acc[f] = acc2[f] = f4{0.f, 0.f, 0.f, 0.f};
+            }
+            tile_end(v);
             cj = 0;
             ccb = 8 * wave;
             if (++ct == T) {
@@ -514,7 +540,8 @@ namespace wqh {
 // LDS bytes of the skinny kernel for M rows, slabs of KS channels, tpb
 // tiles per block and GSL scale entries per row.
 static size_t skinny_lds(int M, int KS, int tpb, int GSL) {
-    return size_t(M) * (size_t(KS) * 2 + 16) + 2 * kSkinnyWaves * 256 * 4 + size_t(tpb) * M * 16 * 4 +
+    const int MF = M > 16 ? 2 : 1;
+    return size_t(M) * (size_t(KS) * 2 + 16) + 2 * kSkinnyWaves * 256 * 4 * MF + size_t(tpb) * M * 16 * 4 +
            size_t(tpb) * 16 * GSL * 3;
 }
 
@@ -593,7 +620,7 @@ static void skinny_device(int& cus, int& lds_max) {
 // the current device, for any group size (group size 32 has the most scale
 // entries per slab, so it needs the most slabs); 0 when K fits in one slab.
 size_t skinny_workspace_bytes(int M, int N, int K) {
-    if (M < 1 || M > 16 || K < 256 || N < 1) return 0;
+    if (M < 1 || M > kSkinnyMaxM || K < 256 || N < 1) return 0;
     int cus = 0, lds_max = 0;
     skinny_device(cus, lds_max);
     SkinnyPlan p;
@@ -602,12 +629,12 @@ size_t skinny_workspace_bytes(int M, int N, int K) {
 }
 
 // Launch the skinny kernel; WQ_ERR_UNSUPPORTED when it does not apply
-// (act-order, M outside 1..16, K below 256).  workspace (nullable,
+// (act-order, M outside 1..32, K below 256).  workspace (nullable,
 // ws_bytes): room for the split form's fp32 partials.
 wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                       const int32_t* perm, uint16_t* y, int M, int N, int K, int bits, int gs, hipStream_t s,
                       const uint16_t* act_scale, const uint16_t* bias, void* workspace, size_t ws_bytes) {
-    if (perm || M < 1 || M > 16 || K < 256) return WQ_ERR_UNSUPPORTED;
+    if (perm || M < 1 || M > kSkinnyMaxM || K < 256) return WQ_ERR_UNSUPPORTED;
     int cus = 0, lds_max = 0;
     skinny_device(cus, lds_max);
     SkinnyPlan plan;
@@ -635,10 +662,16 @@ wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t*
     // pick the instantiation: bits, zero-points, fused epilogue, ZSUB, slab form
     auto pick = [&](auto bits_c) -> wq_status {
         constexpr int B = decltype(bits_c)::value;
-        auto by_slab = [&](auto z_c, auto ex_c, auto zs_c) -> wq_status {
+        auto by_mf = [&](auto z_c, auto ex_c, auto zs_c, auto mf_c) -> wq_status {
             constexpr bool Z = decltype(z_c)::value, E = decltype(ex_c)::value, F = decltype(zs_c)::value;
-            if (split) return go(skinny_kernel<B, D, Z, E, F, false, true>);
-            return slabs ? go(skinny_kernel<B, D, Z, E, F, true, false>) : go(skinny_kernel<B, D, Z, E, F, false, false>);
+            constexpr int MF = decltype(mf_c)::value;
+            if (split) return go(skinny_kernel<B, D, Z, E, F, false, true, MF>);
+            return slabs ? go(skinny_kernel<B, D, Z, E, F, true, false, MF>)
+                         : go(skinny_kernel<B, D, Z, E, F, false, false, MF>);
+        };
+        auto by_slab = [&](auto z_c, auto ex_c, auto zs_c) -> wq_status {
+            return M > 16 ? by_mf(z_c, ex_c, zs_c, std::integral_constant<int, 2>{})
+                          : by_mf(z_c, ex_c, zs_c, std::integral_constant<int, 1>{});
         };
         auto by_zsub = [&](auto z_c, auto ex_c) -> wq_status {
             return zsub ? by_slab(z_c, ex_c, std::true_type{}) : by_slab(z_c, ex_c, std::false_type{});
