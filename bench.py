@@ -82,7 +82,7 @@ GEMM_SOURCES = ("wq_gemm_large.hip", "wq_gemm_common.h", "wq_common.h")
 # before its sums (4 blocks per CU), the K = 11008 layer keeps two slots
 GEMV_KERNEL = ("gemv_stream_kernel<4,1,2,1,1,true,false,false,false,4,true> (qkv, o_proj, gate+up); "
                "gemv_stream_kernel<4,1,2,2,1,true,false,false,false,4,false> (down)")
-GEMM_KERNEL = "gemm_large_kernel<4,true,true,false>"
+GEMM_KERNEL = "gemm_large_kernel<4,true,true,false,128>"
 
 
 def src_sha(parts):

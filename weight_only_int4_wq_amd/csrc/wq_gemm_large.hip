@@ -3,16 +3,18 @@
 // kernel of "AutoAWQ vs The Stack v2" and "AutoAWQ vs Unsloth", WQLinear_*
 // paragraphs: weights dequantized on the fly, never stored as fp16).
 //
-// A 256-thread block owns a 128 x 256 output tile; its four wavefronts sit
-// side by side along N, each with a 128 x 64 tile = 4 x 2 instructions of
-// 32 x 32.  K advances in stages of 128 (one quantization group for the
-// usual group size), eight 16-deep k-steps per stage.
+// A 256-thread block owns a BM x 256 output tile (BM = 128, or 64 for a few
+// hundred rows, where 128-row tiles leave too few tiles and the K split's
+// fp32 partials dominate); its four wavefronts sit side by side along N,
+// each with a BM x 64 tile = BM/32 x 2 instructions of 32 x 32.  K advances
+// in stages of 128 (one quantization group for the usual group size), eight
+// 16-deep k-steps per stage.
 //
 // One 32x32x16 instruction does the work of two 16x16x32 ones, so a single
 // wavefront per SIMD has twice the issue slots per instruction for the LDS
 // reads, the weight decode and the address arithmetic around it.
 //
-//  - Activations: each stage's 128 x 128 fp16 tile is copied global -> LDS
+//  - Activations: each stage's BM x 128 fp16 tile is copied global -> LDS
 //    by global_load_lds_dwordx4 (16-byte units; unit u of row r stored at
 //    u ^ (r mod 16)), three stages in flight in three buffers.
 //  - Weights: in a 32x32x16 instruction lane l supplies 8 consecutive k of
@@ -27,6 +29,8 @@
 //    by then every LDS read of the stage has been issued, so the next
 //    stage's first fragments and the copies three stages ahead start while
 //    those instructions run.
+#include <type_traits>
+
 #include "wq_gemm_common.h"
 
 namespace {
@@ -64,7 +68,7 @@ __device__ __forceinline__ uint32_t zero_pair_nat(uint32_t z) {
         return zero_pair(z);
 }
 
-template <int BITS, bool HAS_Z, bool FAST, bool PART>
+template <int BITS, bool HAS_Z, bool FAST, bool PART, int BM>
 __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
@@ -73,7 +77,8 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
                                                          int m_tiles, int n_tiles, int tiles, int sps,
                                                          float* __restrict__ part) {
     constexpr int GM = 4;
-    constexpr int BM = 128, BN = 256, BK = 128, WN = 64;
+    static_assert(BM == 128 || BM == 64, "tile rows");
+    constexpr int BN = 256, BK = 128, WN = 64;
     constexpr int TM = BM / 32, TN = WN / 32;
     constexpr int ROW_BYTES = BK * 2;
     constexpr int A_INSTR = BM / 16;      // 1 KB copies per wavefront per stage
@@ -230,11 +235,12 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
 
     // Loads for stage st + 2 are spread over k-steps 0..6 of stage st, into
     // the register set and LDS buffer that stage st - 1 used (free since the
-    // barrier that ended it): activation copies (1 KB each) over all seven,
-    // weight column blocks at k-steps 1 and 4.
-    auto a_first = [](int t) { return t == 0 ? 0 : t + 1; };
+    // barrier that ended it): activation copies (1 KB each) over all seven
+    // (BM = 128) or one at each of k-steps 0..3 (BM = 64), weight column
+    // blocks at k-steps 1 and 4.
+    auto a_first = [](int t) { return A_INSTR == 8 ? (t == 0 ? 0 : t + 1) : min(t, A_INSTR); };
     auto b_step = [](int j) { return 1 + 3 * j; };
-    static_assert(A_INSTR == 8 && TN <= 2, "load schedule");
+    static_assert((A_INSTR == 8 || A_INSTR == 4) && TN <= 2, "load schedule");
 
     // Issue order within a k-step: each matrix instruction is followed by a
     // share of the LDS reads, loads and decode / dequant work of the next
@@ -257,15 +263,21 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
 
     // One stage.  On entry af[0] / bf[0] hold its k-step 0.  Its weights sit
     // in `cur`, its activations in Ab; the next stage's in `nxt` / An; the
-    // loads of stage st + 2 go to `fill` / Af.
-    auto stage = [&](int st, const BRegs& cur, const BRegs& nxt, BRegs& fill, const uint8_t* Ab,
+    // loads of stage st + 2 go to `fill` / Af.  Without ISSUE (the stages
+    // after the unrolled loop, where no stage st + 2 exists) nothing is
+    // loaded and the barrier waits for every load in flight: the count of
+    // loads a stage leaves in flight must be the one the barrier assumes, and
+    // loads into registers never read again would be dropped by the compiler.
+    auto stage = [&](auto issue_c, int st, const BRegs& cur, const BRegs& nxt, BRegs& fill, const uint8_t* Ab,
                      const uint8_t* An, uint8_t* Af) {
+        constexpr bool ISSUE = decltype(issue_c)::value;
         const int sf = min(st + 2, st_end - 1);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cb = t & 1;
             int n_vmem = 0;
             if (t < 7) {
+                if constexpr (ISSUE) {
                 const int i0 = a_first(t), i1 = a_first(t + 1);
                 issue_a(Af, sf * BK, i0, i1);
                 n_vmem = i1 - i0;
@@ -275,11 +287,12 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
                         issue_b(fill, sf, j);
                         n_vmem += 2 * (BITS == 8 ? 2 : 1) + NG * (HAS_Z ? 2 : 1);
                     }
+                }
                 load_a(Ab, t + 1, af[cb ^ 1]);
                 make_b(cur, q, t + 1, bf[cb ^ 1]);
             } else {
                 // stage st + 1 has landed; every read of Ab is done
-                copy_barrier<B_OPS + A_INSTR>();
+                copy_barrier<ISSUE ? B_OPS + A_INSTR : 0>();
                 make_q(nxt, qn);
                 load_a(An, 0, af[0]);
                 make_b(nxt, qn, 0, bf[0]);
@@ -295,8 +308,9 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
     };
 
     // Stage s uses register set s % 3 and buffer s % 3 (compile-time: the
-    // loop is unrolled by 3).  Past the last stage, copies and loads re-read
-    // the last stage into buffers and registers that are not used again.
+    // loop is unrolled by 3).  Inside the loop, loads past the last stage
+    // re-read the last stage into buffers and registers that are not used
+    // again.
     BRegs b0, b1, b2;
     const int st_next = min(st_begin + 1, st_end - 1);
     issue_b_all(b0, st_begin);
@@ -309,13 +323,15 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
     make_b(b0, q, 0, bf[0]);
 
     int st = st_begin;
+    const std::true_type loads;
+    const std::false_type no_loads;
     for (; st + 3 <= st_end; st += 3) {
-        stage(st, b0, b1, b2, As0, As1, As2);
-        stage(st + 1, b1, b2, b0, As1, As2, As0);
-        stage(st + 2, b2, b0, b1, As2, As0, As1);
+        stage(loads, st, b0, b1, b2, As0, As1, As2);
+        stage(loads, st + 1, b1, b2, b0, As1, As2, As0);
+        stage(loads, st + 2, b2, b0, b1, As2, As0, As1);
     }
-    if (st < st_end) stage(st, b0, b1, b2, As0, As1, As2);
-    if (st + 1 < st_end) stage(st + 1, b1, b2, b0, As1, As2, As0);
+    if (st < st_end) stage(no_loads, st, b0, b1, b2, As0, As1, As2);
+    if (st + 1 < st_end) stage(no_loads, st + 1, b1, b2, b0, As1, As2, As0);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -341,11 +357,11 @@ __global__ void __launch_bounds__(256) gemm_large_kernel(const uint16_t* __restr
         }
 }
 
-template <int BITS, bool HAS_Z>
+template <int BITS, bool HAS_Z, int BM>
 wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                    uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, float* out32,
                    hipStream_t s) {
-    constexpr int BM = 128, BN = 256;
+    constexpr int BN = 256;
     const int m_tiles = (M + BM - 1) / BM, n_tiles = (N + BN - 1) / BN;
     const int tiles = m_tiles * n_tiles;
     const GroupDiv gd = wqh::group_magic(gs);
@@ -357,28 +373,49 @@ wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* sc
     // PART (fp32 partials or the fp32 output) is a template flag so that the
     // plain fp16 epilogue carries no per-element branch
     if (fast && pp)
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true, true>), grid, dim3(256), 0, s, x, packed, scales,
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true, true, BM>), grid, dim3(256), 0, s, x, packed, scales,
                            zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else if (fast)
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true, false>), grid, dim3(256), 0, s, x, packed, scales,
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, true, false, BM>), grid, dim3(256), 0, s, x, packed, scales,
                            zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else if (pp)
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false, true>), grid, dim3(256), 0, s, x, packed, scales,
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false, true, BM>), grid, dim3(256), 0, s, x, packed, scales,
                            zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     else
-        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false, false>), grid, dim3(256), 0, s, x, packed, scales,
+        hipLaunchKernelGGL((gemm_large_kernel<BITS, HAS_Z, false, false, BM>), grid, dim3(256), 0, s, x, packed, scales,
                            zeros, y, M, N, K, gd, m_tiles, n_tiles, tiles, plan.sps, pp);
     const wq_status st = wqh::launch_status();
     if (st != WQ_OK || !split) return st;
     return wqh::splitk_reduce(part, plan.splits, M, N, y, s);
 }
 
+// Tile rows of the large kernel.  64-row tiles (two blocks per compute
+// unit) only where 128-row tiles are few and K is short: measured on MI355X
+// (4-bit, group 128) they gain 7-15 % on 4096 x 4096 at M = 96-256 and
+// 3-9 % on the 2/3/8-bit 4096 x 4096 layers at M = 256, but lose 16-25 % on
+// the wider Llama and 70B shapes and on K = 11008, where each block's
+// weight decode is spread over half the matrix instructions.
+#ifndef WQ_GEMM_L_BM64_MAX_M
+#define WQ_GEMM_L_BM64_MAX_M 256
+#endif
+inline int large_bm(int M, int N, int K) {
+    const int tiles128 = ((M + 127) / 128) * ((N + 255) / 256);
+    return (M <= WQ_GEMM_L_BM64_MAX_M && K <= 4096 && tiles128 <= 32) ? 64 : 128;
+}
+// Resident blocks per compute unit: one 128-row block (96 KB of LDS, 128
+// accumulator registers per lane), two 64-row blocks (48 KB, 64).
+inline int large_blocks_per_cu(int bm) { return bm == 64 ? 2 : 1; }
+
 template <int BITS>
 wq_status launch_large(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint8_t* zeros,
                        uint16_t* y, int M, int N, int K, int gs, wqh::SplitPlan plan, float* part, float* out32,
                        hipStream_t s) {
-    if (zeros) return launch_z<BITS, true>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
-    return launch_z<BITS, false>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+    if (large_bm(M, N, K) == 64) {
+        if (zeros) return launch_z<BITS, true, 64>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+        return launch_z<BITS, false, 64>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+    }
+    if (zeros) return launch_z<BITS, true, 128>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
+    return launch_z<BITS, false, 128>(x, packed, scales, zeros, y, M, N, K, gs, plan, part, out32, s);
 }
 
 }  // namespace
@@ -393,9 +430,10 @@ bool gemm_large_fits(int M, int N, int K, int bits) {
 }
 
 SplitPlan gemm_large_plan(int M, int N, int K, int bits, size_t ws_avail) {
-    constexpr int BM = 128, BN = 256;
+    constexpr int BN = 256;
+    const int BM = large_bm(M, N, K);
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    return plan_split(M, N, K, bits, BM, BN, tiles, gemm_slots(1), ws_avail);
+    return plan_split(M, N, K, bits, BM, BN, tiles, gemm_slots(large_blocks_per_cu(BM)), ws_avail);
 }
 
 wq_status gemm_large(int bits, const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
