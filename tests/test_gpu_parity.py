@@ -243,6 +243,52 @@ def test_skinny_slab_split_matches_walk(M, bits, gs, sym, N, K):
     assert d.max() <= 1e-2 * max(1.0, np.abs(y_ref).max()), d.max()
 
 
+def test_skinny_split_any_workspace_and_graph_replays():
+    # The split form writes every partial it later sums, so a workspace
+    # holding anything (zeros, all-ones bytes, random bytes) gives the same
+    # bits; a captured graph of the two launches (slabs, then their sum)
+    # gives them on every replay, with eager calls on the same workspace in
+    # between.
+    M, N, K, bits, gs = 16, 4104, 11008, 4, 128
+    seed = (111, M, N, K)
+    w = I.weights(seed, N, K, 0.02)
+    L = gpu_layer(w, bits, gs)
+    x = I.activations(seed, M, K)
+    xd = dev(x)
+    need = wq.workspace_size(M, N, K, bits, False)
+    assert need > 0
+    ref = O.quantize_linear_layer(w, bits, gs)
+    ws = torch.zeros((need,), dtype=torch.uint8, device="cuda")
+    y0_t = wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, workspace=ws)
+    check_y(y0_t, O.linear_ref(x, ref["w_hat"]), "split, zeroed workspace")
+    y0 = host(y0_t)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for fill in ("ones", "random"):
+        if fill == "ones":
+            ws.fill_(255)
+        else:
+            ws.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g).cuda())
+        y = host(wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, workspace=ws))
+        assert np.array_equal(y.view(np.uint16), y0.view(np.uint16)), fill
+    out = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, out=out, workspace=ws)
+    for r in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint16), y0.view(np.uint16)), f"replay {r}"
+        y = host(wq.gemv(xd, L["packed"], L["scales"], L["zeros"], bits, gs, workspace=ws))
+        assert np.array_equal(y.view(np.uint16), y0.view(np.uint16)), f"eager after replay {r}"
+
+
 @pytest.mark.parametrize("M", [1, 16, 17, 33, 100, 130, 300])
 @pytest.mark.parametrize("N,K", [(1000, 512), (4104, 256), (72, 4128)])
 def test_gemm_ragged_shapes(M, N, K):
