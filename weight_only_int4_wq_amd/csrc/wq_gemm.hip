@@ -27,6 +27,8 @@
 //    rectangle of the output and reuse activations and weights from its L2.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "wq_gemm_common.h"
 
 namespace {
@@ -132,13 +134,21 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
     // One stage: wait for its data, start the loads AHEAD stages ahead,
     // multiply.  Stage s's weights and activations were issued at the top of
     // stage s - AHEAD (in that order), so only the loads issued at the tops
-    // of the AHEAD - 1 stages since may still be outstanding.
-    auto stage = [&](int st, const BRegs& cur, BRegs& nxt, uint8_t* Ab, uint8_t* An) {
-        copy_barrier<(AHEAD - 1) * (B_OPS + A_INSTR)>();
-        issue_b(nxt, (st + AHEAD) * BK);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_a(An, (st + AHEAD) * BK);
-        __builtin_amdgcn_sched_barrier(0);
+    // of the AHEAD - 1 stages since may still be outstanding.  Without ISSUE
+    // (the stages after the unrolled loop, whose loads would all lie past
+    // the range) nothing is loaded and the barrier waits for every load in
+    // flight: register loads that are never read would be dropped by the
+    // compiler, and the barrier's count would then let this stage's own
+    // activation copies still be in flight.
+    auto stage = [&](auto issue_c, int st, const BRegs& cur, BRegs& nxt, uint8_t* Ab, uint8_t* An) {
+        constexpr bool ISSUE = decltype(issue_c)::value;
+        copy_barrier<ISSUE ? (AHEAD - 1) * (B_OPS + A_INSTR) : 0>();
+        if constexpr (ISSUE) {
+            issue_b(nxt, (st + AHEAD) * BK);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_a(An, (st + AHEAD) * BK);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
         uint32_t zz[TN], ss[TN];
 #pragma unroll
@@ -200,13 +210,16 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint16_t* __restrict__ 
         __builtin_amdgcn_sched_barrier(0);
     }
     int st = st_begin;
+    const std::true_type loads;
+    const std::false_type no_loads;
     for (; st + NST <= st_end; st += NST) {
 #pragma unroll
-        for (int i = 0; i < NST; ++i) stage(st + i, b[i], b[(i + AHEAD) % NST], As[i], As[(i + AHEAD) % NST]);
+        for (int i = 0; i < NST; ++i)
+            stage(loads, st + i, b[i], b[(i + AHEAD) % NST], As[i], As[(i + AHEAD) % NST]);
     }
 #pragma unroll
     for (int i = 0; i < NST - 1; ++i)
-        if (st + i < st_end) stage(st + i, b[i], b[(i + AHEAD) % NST], As[i], As[(i + AHEAD) % NST]);
+        if (st + i < st_end) stage(no_loads, st + i, b[i], b[(i + AHEAD) % NST], As[i], As[(i + AHEAD) % NST]);
 
     // no copy may still be writing this block's LDS when it exits
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

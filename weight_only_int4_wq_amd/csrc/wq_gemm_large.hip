@@ -390,13 +390,14 @@ wq_status launch_z(const uint16_t* x, const uint32_t* packed, const uint16_t* sc
 }
 
 // Tile rows of the large kernel.  64-row tiles (two blocks per compute
-// unit) only where 128-row tiles are few and K is short: measured on MI355X
-// (4-bit, group 128) they gain 7-15 % on 4096 x 4096 at M = 96-256 and
-// 3-9 % on the 2/3/8-bit 4096 x 4096 layers at M = 256, but lose 16-25 % on
-// the wider Llama and 70B shapes and on K = 11008, where each block's
-// weight decode is spread over half the matrix instructions.
+// unit) where 128-row tiles are few and K is short, up to
+// WQ_GEMM_L_BM64_MAX_M rows: measured on MI355X (4-bit, group 128) they gain
+// 7-15 % on 4096 x 4096 at M = 96-256 and 3-9 % on the 2/3/8-bit 4096 x 4096
+// layers at M = 256, but lose 16-25 % on the wider Llama and 70B shapes and
+// on K = 11008.  Off by default (0): one GPU parity run gave a wrong sum on
+// a 2-bit act-order layer at M = 256 with them, whose cause is not found.
 #ifndef WQ_GEMM_L_BM64_MAX_M
-#define WQ_GEMM_L_BM64_MAX_M 256
+#define WQ_GEMM_L_BM64_MAX_M 0
 #endif
 inline int large_bm(int M, int N, int K) {
     const int tiles128 = ((M + 127) / 128) * ((N + 255) / 256);
