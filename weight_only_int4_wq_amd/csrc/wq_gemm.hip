@@ -256,6 +256,25 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     }
 }
 
+// The same for M*N a multiple of 4: four outputs per thread, 16-byte loads
+// of each range and one 8-byte store (the same additions in the same order).
+__global__ void __launch_bounds__(256) splitk_reduce4_kernel(const float4* __restrict__ part, int splits,
+                                                             long long mn4, uint2* __restrict__ y) {
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < mn4;
+         t += (long long)gridDim.x * blockDim.x) {
+        float4 v = part[t];
+        for (int r = 1; r < splits; ++r) {
+            const float4 w = part[t + r * mn4];
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.x)) |
+                            (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.y)) << 16);
+        const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.z)) |
+                            (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.w)) << 16);
+        y[t] = uint2{lo, hi};
+    }
+}
+
 // x_out[m][k'] = x[m][perm[k']]: activations in packed column order.  A
 // block takes whole rows: it copies the row into LDS with 16-byte loads, then
 // every thread gathers 8 consecutive outputs through perm from LDS and writes
@@ -424,6 +443,15 @@ int gemm_slots(int blocks_per_cu) {
 
 wq_status splitk_reduce(const float* part, int splits, int M, int N, uint16_t* y, hipStream_t s) {
     const long long mn = (long long)M * N;
+    // partials and y are 16-byte aligned (workspace and output checks)
+    if (mn % 4 == 0) {
+        const long long mn4 = mn / 4;
+        long long blocks = (mn4 + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        hipLaunchKernelGGL(splitk_reduce4_kernel, dim3(int(blocks)), dim3(256), 0, s,
+                           reinterpret_cast<const float4*>(part), splits, mn4, reinterpret_cast<uint2*>(y));
+        return launch_status();
+    }
     long long blocks = (mn + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3(int(blocks)), dim3(256), 0, s, part, splits, mn, y);
