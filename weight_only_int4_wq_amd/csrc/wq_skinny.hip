@@ -533,6 +533,34 @@ __global__ void __launch_bounds__(256) skinny_sum_kernel(const float* __restrict
     }
 }
 
+// The same for N a multiple of 4: four outputs of one row per thread, 16-byte
+// loads of each slab's partials, one 8-byte store (same additions, same order).
+__global__ void __launch_bounds__(256) skinny_sum4_kernel(const float4* __restrict__ part, int nsl, int M, int N,
+                                                          const uint16_t* __restrict__ bias,
+                                                          uint2* __restrict__ y) {
+    const size_t MN4 = size_t(M) * N / 4;
+    const int N4 = N / 4;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < MN4; i += size_t(gridDim.x) * blockDim.x) {
+        float4 v = part[i];
+        for (int sl = 1; sl < nsl; ++sl) {
+            const float4 w = part[size_t(sl) * MN4 + i];
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+        }
+        if (bias) {
+            const int n = 4 * int(i % size_t(N4));
+            v.x += float(__builtin_bit_cast(_Float16, bias[n]));
+            v.y += float(__builtin_bit_cast(_Float16, bias[n + 1]));
+            v.z += float(__builtin_bit_cast(_Float16, bias[n + 2]));
+            v.w += float(__builtin_bit_cast(_Float16, bias[n + 3]));
+        }
+        const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.x)) |
+                            (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.y)) << 16);
+        const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.z)) |
+                            (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)v.w)) << 16);
+        y[i] = uint2{lo, hi};
+    }
+}
+
 }  // namespace
 
 namespace wqh {
@@ -654,6 +682,13 @@ wq_status skinny_gemv(const uint16_t* x, const uint32_t* packed, const uint16_t*
         wq_status st = launch_status();
         if (st != WQ_OK || !split) return st;
         const size_t MN = size_t(M) * N;
+        // the workspace and y are 16-byte aligned (checked by the entry points)
+        if (N % 4 == 0) {
+            const int sb = int(std::min<size_t>((MN / 4 + 255) / 256, size_t(cus) * 8));
+            hipLaunchKernelGGL(skinny_sum4_kernel, dim3(sb), dim3(256), 0, s, reinterpret_cast<const float4*>(part),
+                               plan.nsl, M, N, bias, reinterpret_cast<uint2*>(y));
+            return launch_status();
+        }
         const int sb = int(std::min<size_t>((MN + 255) / 256, size_t(cus) * 8));
         hipLaunchKernelGGL(skinny_sum_kernel, dim3(sb), dim3(256), 0, s, part, plan.nsl, M, N, bias, y);
         return launch_status();
